@@ -1,0 +1,189 @@
+"""CPU oracle for the 4-bit block-quantised matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The library path (``quantized_q4_block_amd``)
+never imports it and shares no code with it.
+
+The arithmetic lives in ``q4_oracle.c`` (plain C, double accumulation in
+ascending k, one output at a time); this module builds it with gcc, loads it
+with ctypes and converts numpy arrays.  See the C file's header for the
+definition computed and the passages it follows.
+
+Pinning (tests/test_oracle.py): exhaustive dequantisation of all 16 codes x
+all 65,536 fp16 scale patterns against numpy's fp16 decoding and torch's
+float32->bf16 rounding; a hand-written nibble-order fixture; closed forms on
+constant and alternating inputs; exact rational brute force on 8x64 tiles;
+agreement with a float64 library matmul of the dequantised weights; MoE
+reductions to the dense case.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4_oracle.c")
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the wrapper at another build of the oracle (the mutation
+# test compiles deliberately broken copies to show the pins catch them).
+_LIB_PATH = os.environ.get("Q4_ORACLE_LIB", _DEFAULT_LIB)
+_lib = None
+
+BLOCK = 32
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP over output rows)."""
+    if force or not os.path.exists(_DEFAULT_LIB):
+        compile_to(_SRC, _DEFAULT_LIB)
+    return _DEFAULT_LIB
+
+
+def compile_to(src: str, out: str) -> None:
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if _LIB_PATH == _DEFAULT_LIB and not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_fp16_value.restype = ctypes.c_double
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_bf16_round_bits.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_round_bits.restype = ctypes.c_uint16
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_dequant_f32.argtypes = [P, P, I64, I64, P]
+    lib.oracle_dequant_bf16.argtypes = [P, P, I64, I64, P]
+    lib.oracle_matmul.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P, P]
+    lib.oracle_matmul_sampled.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int,
+                                          P, P, I64, P, P]
+    lib.oracle_moe.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, P, P]
+    _lib = lib
+    return lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def fp16_value(bits: int) -> float:
+    return float(_load().oracle_fp16_value(int(bits)))
+
+
+def bf16_value(bits: int) -> float:
+    return float(_load().oracle_bf16_value(int(bits)))
+
+
+def bf16_round_bits(v: float) -> int:
+    return int(_load().oracle_bf16_round_bits(float(v)))
+
+
+def _check_w(w_q, w_s):
+    N, kh = w_q.shape[-2:]
+    K = 2 * kh
+    if K % BLOCK or w_s.shape[-1] != K // BLOCK or w_s.shape[-2] != N:
+        raise ValueError("inconsistent w_q / w_s shapes")
+    return N, K
+
+
+def dequant_f32(w_q: np.ndarray, w_s: np.ndarray) -> np.ndarray:
+    """float32 [N][K] dequantised weights (exact)."""
+    N, K = _check_w(w_q, w_s)
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    out = np.empty((N, K), dtype=np.float32)
+    _load().oracle_dequant_f32(_ptr(wq), _ptr(ws), N, K, _ptr(out))
+    return out
+
+
+def dequant_bf16_bits(w_q: np.ndarray, w_s: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns [N][K]: dequantised weights rounded nearest-even."""
+    N, K = _check_w(w_q, w_s)
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    out = np.empty((N, K), dtype=np.uint16)
+    _load().oracle_dequant_bf16(_ptr(wq), _ptr(ws), N, K, _ptr(out))
+    return out
+
+
+def matmul(x: np.ndarray, w_q: np.ndarray, w_s: np.ndarray,
+           bf16_weights: bool = False):
+    """(y, t): double [M][N] result and sum_k |x*w| per output."""
+    N, K = _check_w(w_q, w_s)
+    x = _c(x, np.uint16)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x has the wrong K")
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    y = np.empty((M, N), dtype=np.float64)
+    t = np.empty((M, N), dtype=np.float64)
+    _load().oracle_matmul(_ptr(x), _ptr(wq), _ptr(ws), M, N, K, int(bool(bf16_weights)),
+                          _ptr(y), _ptr(t))
+    return y, t
+
+
+def matmul_sampled(x: np.ndarray, w_q: np.ndarray, w_s: np.ndarray,
+                   ms: np.ndarray, ns: np.ndarray, bf16_weights: bool = False):
+    """(y, t) for the outputs (ms[i], ns[i]) only; double [count]."""
+    N, K = _check_w(w_q, w_s)
+    x = _c(x, np.uint16)
+    M = x.shape[0]
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    if ms.shape != ns.shape or ms.ndim != 1:
+        raise ValueError("ms and ns must be 1-D and equal length")
+    if ms.size and (ms.min() < 0 or ms.max() >= M or ns.min() < 0 or ns.max() >= N):
+        raise ValueError("sample index out of range")
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    y = np.empty(ms.size, dtype=np.float64)
+    t = np.empty(ms.size, dtype=np.float64)
+    _load().oracle_matmul_sampled(_ptr(x), _ptr(wq), _ptr(ws), M, N, K,
+                                  int(bool(bf16_weights)), _ptr(ms), _ptr(ns), ms.size,
+                                  _ptr(y), _ptr(t))
+    return y, t
+
+
+def moe(x: np.ndarray, w_q: np.ndarray, w_s: np.ndarray, ids: np.ndarray,
+        gates: np.ndarray):
+    """(y, t): double [T][N] expert-routed weighted sum and its |.| scale."""
+    E = w_q.shape[0]
+    N, K = _check_w(w_q, w_s)
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    ids = _c(ids, np.int32)
+    gates = _c(gates, np.float32)
+    topk = ids.shape[1]
+    if ids.shape != (T, topk) or gates.shape != (T, topk):
+        raise ValueError("ids / gates must be [T][topk]")
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    y = np.empty((T, N), dtype=np.float64)
+    t = np.empty((T, N), dtype=np.float64)
+    _load().oracle_moe(_ptr(x), _ptr(wq), _ptr(ws), _ptr(ids), _ptr(gates),
+                       T, topk, E, N, K, _ptr(y), _ptr(t))
+    return y, t

@@ -1,0 +1,227 @@
+/*
+ * q4_oracle.c -- plain, slow CPU oracle for the 4-bit block-quantised matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no source,
+ * header, table or helper with the HIP library; the two are built by
+ * different compilers from different files.
+ *
+ * What it computes (the plain definition; nothing is blocked, fused or
+ * reordered):
+ *
+ *   w[n,k] = (c[n,k] - 8) * s[n, k/32]
+ *   y[m,n] = sum_{k=0}^{K-1} x[m,k] * w[n,k]        (double, k ascending)
+ *   t[m,n] = sum_k |x[m,k] * w[n,k]|                 (the tolerance scale)
+ *
+ *   MoE:  y[t,n] = sum_j g[t,j] * (sum_k x[t,k] * w_{id[t,j]}[n,k])
+ *         t[t,n] = sum_j |g[t,j]| * (sum_k |x[t,k] * w_{id[t,j]}[n,k]|)
+ *
+ * Sources.  The specialised-runtime spec ("spec: specialized model runtimes")
+ * names quant/dequant and GEMM as T0 kernel-tier ops (section
+ * "Architecture"), a quantised GEMM as the first measured kernel (section
+ * "Feasibility gate"), groupwise-int weights as the first weight profile
+ * (section "Target package and artifact"), and asks for a clear, slow,
+ * independent reference for every tuned kernel (section "Kernel and
+ * portability contract", rule 1).  The layer-package spec ("Layer Package
+ * Repository Spec", the MoE fixture paragraph under "Policy Resolution")
+ * describes routed top-k expert matmuls followed by a weighted sum over the
+ * selected experts.  The pages fix no bit layout; the readings used here are:
+ *   - a code is 4 bits, value = code - 8 (symmetric, no zero point);
+ *   - one IEEE binary16 scale per 32 consecutive k of a row;
+ *   - codes of row n are packed two per byte, k = 2j in the LOW nibble of
+ *     byte j and k = 2j+1 in the HIGH nibble; rows are K/2 bytes apart;
+ *   - scales of row n are K/32 consecutive fp16 values;
+ *   - activations are bf16, row-major [M][K];
+ *   - the prefill (matrix-core) variant rounds each dequantised weight to
+ *     bf16, nearest-even, before the product (oracle option bf16_weights).
+ *
+ * Floating point: every fp16 / bf16 value is decoded from its IEEE fields
+ * into a double (exact); (c-8)*s is exact in double and in float; products
+ * x*w are exact in double; only the k-ordered sum rounds.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define Q4O_BLOCK 32
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double fp16_value(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* 0.f * 2^-14 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* 1.f * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits. */
+static double bf16_value(uint16_t b) {
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xFF;
+    int f = b & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* 0.f * 2^-126 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);     /* 1.f * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, and return the
+ * rounded value as a double.  Written from the definition: keep 8
+ * significant bits in the normal range, a fixed 2^-133 quantum in the
+ * subnormal range, and overflow to infinity past the largest finite value. */
+static double bf16_round(double v) {
+    if (isnan(v) || isinf(v) || v == 0.0)
+        return v;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);                       /* a = m * 2^e, m in [0.5, 1) */
+    double r;
+    if (e - 1 < -126)                   /* below the smallest normal */
+        r = ldexp(rint(ldexp(a, 133)), -133);
+    else
+        r = ldexp(rint(ldexp(a, 8 - e)), e - 8);
+    if (r >= ldexp(1.0, 128))           /* 2^128 is past the largest finite */
+        r = INFINITY;
+    return v < 0 ? -r : r;
+}
+
+static uint16_t bf16_bits_of(double v) {
+    /* v is a bf16 value (or inf/nan): it converts to float exactly. */
+    float f = (float)v;
+    uint32_t u;
+    if (isnan(v))
+        return (uint16_t)(signbit(v) ? 0xFFC0u : 0x7FC0u);
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+static int code_at(const uint8_t *row, int64_t k) {
+    uint8_t byte = row[k / 2];
+    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+static double weight_at(const uint8_t *wq_row, const uint16_t *ws_row, int64_t k,
+                        int bf16_weights) {
+    double w = (double)(code_at(wq_row, k) - 8) * fp16_value(ws_row[k / Q4O_BLOCK]);
+    return bf16_weights ? bf16_round(w) : w;
+}
+
+/* ---- exported ---------------------------------------------------------- */
+
+int oracle_block(void) { return Q4O_BLOCK; }
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+double oracle_fp16_value(uint16_t h) { return fp16_value(h); }
+double oracle_bf16_value(uint16_t b) { return bf16_value(b); }
+uint16_t oracle_bf16_round_bits(double v) { return bf16_bits_of(bf16_round(v)); }
+
+/* Dequantise to float32 [N][K]; (c-8)*s is exact in float. */
+void oracle_dequant_f32(const uint8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                        float *out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = (float)weight_at(wq + n * (K / 2), ws + n * (K / Q4O_BLOCK), k, 0);
+}
+
+/* Dequantise and round to bf16 (nearest-even); bf16 bit patterns [N][K]. */
+void oracle_dequant_bf16(const uint8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                         uint16_t *out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = bf16_bits_of(
+                weight_at(wq + n * (K / 2), ws + n * (K / Q4O_BLOCK), k, 1));
+}
+
+/* One output: sequential double dot product over k and its |.| companion. */
+static void dot_one(const uint16_t *x_row, const uint8_t *wq_row, const uint16_t *ws_row,
+                    int64_t K, int bf16_weights, double *y, double *t) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = bf16_value(x_row[k]) * weight_at(wq_row, ws_row, k, bf16_weights);
+        acc += p;
+        mag += fabs(p);
+    }
+    *y = acc;
+    *t = mag;
+}
+
+/* y, t: double [M][N]. */
+void oracle_matmul(const uint16_t *x, const uint8_t *wq, const uint16_t *ws,
+                   int64_t M, int64_t N, int64_t K, int bf16_weights,
+                   double *y, double *t) {
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m)
+            dot_one(x + m * K, wq + n * (K / 2), ws + n * (K / Q4O_BLOCK), K, bf16_weights,
+                    &y[m * N + n], &t[m * N + n]);
+}
+
+/* Only the listed outputs (ms[i], ns[i]); y, t: double [count]. */
+void oracle_matmul_sampled(const uint16_t *x, const uint8_t *wq, const uint16_t *ws,
+                           int64_t M, int64_t N, int64_t K, int bf16_weights,
+                           const int64_t *ms, const int64_t *ns, int64_t count,
+                           double *y, double *t) {
+    (void)M; (void)N;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i)
+        dot_one(x + ms[i] * K, wq + ns[i] * (K / 2), ws + ns[i] * (K / Q4O_BLOCK), K,
+                bf16_weights, &y[i], &t[i]);
+}
+
+/* Expert-routed rows.  x: bf16 [T][K]; wq: [E][N][K/2]; ws: [E][N][K/32];
+ * ids: int32 [T][topk]; gates: float [T][topk]; y, t: double [T][N].
+ * An id outside [0, E) selects no expert and contributes nothing. */
+void oracle_moe(const uint16_t *x, const uint8_t *wq, const uint16_t *ws,
+                const int32_t *ids, const float *gates,
+                int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
+                double *y, double *t) {
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t tok = 0; tok < T; ++tok) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < topk; ++j) {
+                int64_t e = ids[tok * topk + j];
+                if (e < 0 || e >= E) continue;
+                double d, dm;
+                dot_one(x + tok * K, wq + (e * N + n) * (K / 2),
+                        ws + (e * N + n) * (K / Q4O_BLOCK), K, 0, &d, &dm);
+                double g = (double)gates[tok * topk + j];
+                acc += g * d;
+                mag += fabs(g) * dm;
+            }
+            y[tok * N + n] = acc;
+            t[tok * N + n] = mag;
+        }
+    }
+}

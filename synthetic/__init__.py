@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for the Q4 block matmul, shared by the oracle tests,
+the GPU parity tests and the benchmark.
+
+This module draws random numbers and nothing else: it holds none of the
+method's arithmetic (no nibble unpacking, no dequantisation, no dot products).
+Every array is returned as raw bits in the storage layout the library's C ABI
+takes:
+
+* ``x``   -- bf16 activations, ``uint16[M][K]`` (bit patterns), drawn N(0, 1)
+             in float32 and rounded to bf16 (round-to-nearest-even).
+* ``w_q`` -- packed 4-bit codes, ``uint8[N][K/2]``.  Every byte is drawn
+             uniformly from 0..255, which makes both nibbles of every byte
+             independent and uniform over 0..15; which nibble maps to which
+             k is the library's convention, not this module's concern.
+* ``w_s`` -- one fp16 scale per 32-element block along K, ``uint16[N][K/32]``
+             (bit patterns), |N(0, 1)| * 0.02 rounded to fp16.
+
+Distributions follow the shapes and value laws of the workloads the specs'
+T0 quantized-GEMM tier is sized for (spec "specialized model runtimes",
+sections "Kernel and portability contract" and "Target package and
+artifact": groupwise-int weight quantisation first); the MoE routing table
+follows the expert-routed decode of the layer-package spec ("Policy
+Resolution" MoE fixture paragraph): each token picks ``topk`` distinct
+experts uniformly, with gates = softmax of N(0, 1) logits over the picked
+experts.
+
+Draw order inside one case: codes, scales, x, then (MoE) the router, token
+by token.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BLOCK = 32  # elements per quantisation block along K
+
+__all__ = [
+    "BLOCK", "DenseCase", "MoECase", "CONFIGS", "dense_case", "moe_case",
+    "f32_to_bf16_bits", "config_case",
+]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return the bits.
+
+    Used only to synthesise bf16 activations from float32 draws (finite
+    values only).
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+@dataclass
+class DenseCase:
+    x: np.ndarray    # uint16 [M][K]   bf16 bits
+    w_q: np.ndarray  # uint8  [N][K/2] packed codes
+    w_s: np.ndarray  # uint16 [N][K/32] fp16 bits
+
+    @property
+    def shape(self):
+        M, K = self.x.shape
+        return M, self.w_q.shape[0], K
+
+
+@dataclass
+class MoECase:
+    x: np.ndarray      # uint16 [T][K]
+    w_q: np.ndarray    # uint8  [E][N][K/2]
+    w_s: np.ndarray    # uint16 [E][N][K/32]
+    ids: np.ndarray    # int32  [T][topk]
+    gates: np.ndarray  # float32 [T][topk]
+
+
+def _weights(rng: np.random.Generator, lead: tuple, N: int, K: int, scale_std: float):
+    w_q = rng.integers(0, 256, size=lead + (N, K // 2), dtype=np.uint8)
+    s = np.abs(rng.standard_normal(lead + (N, K // BLOCK))) * scale_std
+    w_s = s.astype(np.float16).view(np.uint16)
+    return w_q, w_s
+
+
+def dense_case(seed: int, M: int, N: int, K: int, scale_std: float = 0.02) -> DenseCase:
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.default_rng(seed)
+    w_q, w_s = _weights(rng, (), N, K, scale_std)
+    x = f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return DenseCase(x=x, w_q=w_q, w_s=w_s)
+
+
+def moe_case(seed: int, T: int, topk: int, E: int, N: int, K: int,
+             scale_std: float = 0.02) -> MoECase:
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    if topk > E:
+        raise ValueError("topk distinct experts need topk <= E")
+    rng = np.random.default_rng(seed)
+    w_q, w_s = _weights(rng, (E,), N, K, scale_std)
+    x = f32_to_bf16_bits(rng.standard_normal((T, K), dtype=np.float32))
+    ids = np.empty((T, topk), dtype=np.int32)
+    gates = np.empty((T, topk), dtype=np.float32)
+    for t in range(T):
+        ids[t] = rng.choice(E, size=topk, replace=False)
+        logits = rng.standard_normal(topk)
+        e = np.exp(logits - logits.max())
+        gates[t] = (e / e.sum()).astype(np.float32)
+    return MoECase(x=x, w_q=w_q, w_s=w_s, ids=ids, gates=gates)
+
+
+# The five workloads: shapes, seeds and output dtype.
+CONFIGS = {
+    "tiny_gemv":      dict(kind="dense", M=1, K=256, N=512, seed=0, out="f32"),
+    "decode_gate_up": dict(kind="dense", M=1, K=5120, N=34816, seed=1, out="f32"),
+    "batched_down":   dict(kind="dense", M=4, K=17408, N=5120, seed=2, out="f32"),
+    "prefill":        dict(kind="dense", M=512, K=5120, N=34816, seed=3, out="bf16"),
+    "moe":            dict(kind="moe", T=8, topk=8, E=128, K=4096, N=1536, seed=4, out="f32"),
+}
+
+
+def config_case(name: str):
+    c = CONFIGS[name]
+    if c["kind"] == "dense":
+        return dense_case(c["seed"], c["M"], c["N"], c["K"])
+    return moe_case(c["seed"], c["T"], c["topk"], c["E"], c["N"], c["K"])

@@ -1,0 +1,50 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case compiles a copy of the oracle's C source with one deliberate
+mistake (on the CPU, into a temporary directory) and runs the pin suite
+(tests/test_oracle.py) against it in a subprocess; the suite must fail.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "q4_oracle.c")
+
+MUTANTS = {
+    "nibble_order_swapped": ("(byte & 0x0F) : (byte >> 4)", "(byte >> 4) : (byte & 0x0F)"),
+    "offset_7_not_8": ("code_at(wq_row, k) - 8", "code_at(wq_row, k) - 7"),
+    "scale_block_64": ("ws_row[k / Q4O_BLOCK]", "ws_row[k / 64]"),
+    "fp16_exponent_bias": ("e - 25);", "e - 24);"),
+    "fp16_subnormal_quantum": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    "bf16_exponent_bias": ("e - 134);", "e - 133);"),
+    "output_transposed": ("&y[m * N + n], &t[m * N + n]", "&y[n * M + m], &t[n * M + m]"),
+    "sum_sign": ("acc += p;", "acc -= p;"),
+    "abs_dropped": ("mag += fabs(p);", "mag += p;"),
+    "bf16_round_truncates": ("r = ldexp(rint(ldexp(a, 8 - e)), e - 8);",
+                             "r = ldexp(floor(ldexp(a, 8 - e)), e - 8);"),
+    "moe_gate_dropped": ("acc += g * d;", "acc += d;"),
+    "moe_abs_gate_dropped": ("mag += fabs(g) * dm;", "mag += dm;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    oracle.compile_to(str(mpath), lib)
+    env = dict(os.environ, Q4_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
