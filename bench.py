@@ -1,0 +1,267 @@
+"""Benchmark: weight-only Q4 block matmul on one MI355X.
+
+Headline workload: decode_gate_up -- the fused gate+up projection at decode,
+M = 1, K = 5120, N = 34816 (int4 codes, 32-element blocks, fp16 scales,
+bf16 activations, fp32 output).  A step is one q4_matmul call over one
+activation row, i.e. the whole decode hot path (activation staging, weight
+and scale streaming, unpack + dequant, contraction, reduction, store).  The
+weights rotate over byte-identical copies totalling more than 1 GB so that
+neither the L2 caches nor the 256 MB Infinity Cache can serve them: every
+step streams its 100.27 MB of codes and scales from HBM.
+
+Printed: one JSON line with value = weight+scale GB/s (whole job), the
+roofline of the dominant kernel (the decode GEMV) from HIP events over the
+timed region, the CPU oracle's rate on the host, and the other workloads
+(batched decode M = 4, prefill M = 512, MoE) measured the same way as
+extra context.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "weight GB/s (% HBM peak) at decode M=1/4; TFLOP/s (% MFMA peak) at M=512"
+ROTATE_BYTES = 1 << 30         # rotate weights over at least this much HBM
+
+
+def weight_bytes(N, K):
+    return N * K // 2 + N * (K // 32) * 2
+
+
+def csrc_digest():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_q4_block_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_tag, digest):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("csrc_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Dense:
+    """Device copies of one dense workload, weights rotated over copies."""
+
+    def __init__(self, torch, q4, name, copies=None):
+        import synthetic
+        c = synthetic.CONFIGS[name]
+        self.name, self.M, self.N, self.K = name, c["M"], c["N"], c["K"]
+        d = synthetic.dense_case(c["seed"], self.M, self.N, self.K)
+        dev = "cuda:0"
+        wb = weight_bytes(self.N, self.K)
+        n = copies or max(2, -(-ROTATE_BYTES // wb) + 1)
+        self.copies = n
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev)
+        wq = torch.from_numpy(d.w_q).to(dev)
+        ws = torch.from_numpy(d.w_s.view(np.int16)).to(dev)
+        self.wq = [wq] + [wq.clone() for _ in range(n - 1)]
+        self.ws = [ws] + [ws.clone() for _ in range(n - 1)]
+        self.bf16 = c["out"] == "bf16"
+        self.y = torch.empty((self.M, self.N), device=dev,
+                             dtype=torch.bfloat16 if self.bf16 else torch.float32)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_matmul
+        self.args = [(P(self.x.data_ptr()), P(self.wq[i].data_ptr()), P(self.ws[i].data_ptr()),
+                      P(self.y.data_ptr()), q4.Q4_BF16 if self.bf16 else q4.Q4_F32,
+                      self.M, self.N, self.K) for i in range(n)]
+        self.wbytes = wb
+        self.flops = 2 * self.M * self.N * self.K
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_matmul failed with status {st}")
+
+
+class MoE:
+    def __init__(self, torch, q4, copies=None):
+        import synthetic
+        c = synthetic.CONFIGS["moe"]
+        self.T, self.topk, self.E, self.N, self.K = c["T"], c["topk"], c["E"], c["N"], c["K"]
+        m = synthetic.moe_case(c["seed"], self.T, self.topk, self.E, self.N, self.K)
+        dev = "cuda:0"
+        per_expert = weight_bytes(self.N, self.K)
+        n = copies or max(2, -(-ROTATE_BYTES // (per_expert * self.E)) + 1)
+        self.copies = n
+        self.x = torch.from_numpy(m.x.view(np.int16)).to(dev)
+        wq = torch.from_numpy(m.w_q).to(dev)
+        ws = torch.from_numpy(m.w_s.view(np.int16)).to(dev)
+        self.wq = [wq] + [wq.clone() for _ in range(n - 1)]
+        self.ws = [ws] + [ws.clone() for _ in range(n - 1)]
+        self.ids = torch.from_numpy(m.ids).to(dev)
+        self.g = torch.from_numpy(m.gates).to(dev)
+        self.y = torch.empty((self.T, self.N), device=dev, dtype=torch.float32)
+        need = q4.q4_moe_workspace_bytes(self.T, self.topk, self.E, self.N)
+        self.wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_moe_matmul
+        self.args = [(P(self.x.data_ptr()), P(self.wq[i].data_ptr()), P(self.ws[i].data_ptr()),
+                      P(self.ids.data_ptr()), P(self.g.data_ptr()), P(self.y.data_ptr()),
+                      self.T, self.topk, self.E, self.N, self.K, P(self.wsp.data_ptr()), need)
+                     for i in range(n)]
+        touched = len(np.unique(m.ids))
+        self.touched = touched
+        self.wbytes = touched * per_expert          # every touched expert read once
+        self.flops = 2 * self.T * self.topk * self.N * self.K
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_moe_matmul failed with status {st}")
+
+
+def time_steps(torch, work, steps, warmup):
+    """Host-timed steps (synchronised on both sides) and HIP-event time over
+    the same region on the launch stream."""
+    stream = torch.cuda.current_stream()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    for i in range(warmup):
+        work.step(i, h)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        work.step(warmup + i, h)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(min_seconds=10.0, max_reps=20):
+    """The CPU oracle on decode_gate_up, repeated until >= min_seconds."""
+    import oracle
+    import synthetic
+    c = synthetic.CONFIGS["decode_gate_up"]
+    d = synthetic.dense_case(c["seed"], c["M"], c["N"], c["K"])
+    oracle.matmul(d.x[:, :], d.w_q[:64], d.w_s[:64])      # load + warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.matmul(d.x, d.w_q, d.w_s)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    gbs = reps * weight_bytes(c["N"], c["K"]) / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"full decode_gate_up (M=1, K=5120, N=34816) x {reps} reps, "
+                      f"{el:.1f} s, double accumulation"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the decode and prefill paths would shard the weight rows; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_q4_block_amd as q4
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    digest = csrc_digest()
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    progress("decode_gate_up: generating inputs")
+    head = Dense(torch, q4, "decode_gate_up")
+    progress(f"decode_gate_up: timing {args.steps} steps over {head.copies} weight copies")
+    ms_step, ev_ms = time_steps(torch, head, args.steps, args.warmup)
+    copies = head.copies
+    value = head.wbytes / (ms_step * 1e-3) / 1e9
+    achieved = head.wbytes / (ev_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile("gemv_decode_gate_up", digest),
+            "kernel": "q4::gemv_kernel<1,8>", "avg_launch_us": round(ev_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": head.wbytes}
+    del head
+    torch.cuda.empty_cache()
+
+    others = {}
+    if not args.headline_only:
+        steps = max(50, args.steps // 10)
+        for name in ("batched_down", "prefill"):
+            progress(f"{name}: generating inputs")
+            w = Dense(torch, q4, name)
+            progress(f"{name}: timing")
+            _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+            if name == "prefill":
+                tf = w.flops / (ev * 1e-3) / 1e12
+                others[name] = {"M": w.M, "N": w.N, "K": w.K, "avg_launch_us": round(ev * 1e3, 2),
+                                "TFLOP/s": round(tf, 2), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+            else:
+                gbs = w.wbytes / (ev * 1e-3) / 1e9
+                others[name] = {"M": w.M, "N": w.N, "K": w.K, "avg_launch_us": round(ev * 1e3, 2),
+                                "weight_GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            del w
+            torch.cuda.empty_cache()
+        progress("moe: generating inputs")
+        w = MoE(torch, q4)
+        progress("moe: timing")
+        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+        gbs = w.wbytes / (ev * 1e-3) / 1e9
+        others["moe"] = {"T": w.T, "topk": w.topk, "E": w.E, "N": w.N, "K": w.K,
+                         "touched_experts": w.touched, "avg_call_us": round(ev * 1e3, 2),
+                         "touched_weight_GB/s": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del w
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        progress("cpu baseline: timing the oracle")
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode_gate_up: y[1][34816] = x[1][5120] . dequant(W)^T, "
+                               "int4 codes (value = code - 8), 32-element blocks, fp16 scales, "
+                               "bf16 x, fp32 y, seed 1",
+                   "M": 1, "K": 5120, "N": 34816, "parallelism": "single GPU",
+                   "rotating_weight_copies": copies, "csrc_digest": digest},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * q4.h -- C ABI of libq4: weight-only 4-bit block-quantised matmul on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   y[m][n] = sum_k x[m][k] * w[n][k],   w[n][k] = (c[n][k] - 8) * s[n][k / 32]
+ *
+ * Where the operation comes from.  The spec "spec: specialized model
+ * runtimes" puts quant/dequant and GEMM in its T0 kernel tier (section
+ * "Architecture"), names a quantised GEMM as the first measured kernel
+ * (section "Feasibility gate") and groupwise-int as the first weight profile
+ * (section "Target package and artifact"); it wants runtimes loaded
+ * in-process behind a C ABI whose version is pinned and whose failures
+ * return a clean value the caller handles (sections "Architecture" and
+ * "Prototype ABI scope").  The expert-routed call follows the routed top-k
+ * expert matmul plus weighted sum of the "Layer Package Repository Spec"
+ * (MoE fixture paragraph under "Policy Resolution").  The pages fix no bit
+ * layout; the layout below is this library's.
+ *
+ * Data layout (all tensors contiguous, row-major, in DEVICE memory):
+ *   x    bf16  [M][K]      activations (bit patterns, uint16 storage)
+ *   w_q  uint8 [N][K/2]    codes: element k = 2j is the LOW nibble of byte
+ *                          j of its row, k = 2j+1 the HIGH nibble; a code c
+ *                          stands for the integer c - 8 (-8..7)
+ *   w_s  fp16  [N][K/32]   one IEEE binary16 scale per 32 consecutive k
+ *   y    fp32 or bf16 [M][N]
+ * K must be a positive multiple of 32.
+ *
+ * Numerics.  Products and sums are fp32.  Matrix-vector path (M <= 8):
+ * every weight (c-8)*s enters exactly (no rounding before the product).
+ * Matrix-core path (M > 8): every weight is rounded to bf16 (nearest-even)
+ * and the bf16 matrix cores accumulate in fp32.  bf16 outputs are rounded
+ * nearest-even from the fp32 result.  Results are bit-identical from run to
+ * run (no floating-point atomics).
+ *
+ * Conventions of every call:
+ *   - All checks run on the host before anything is enqueued; on any error
+ *     nothing is launched and no output is written.
+ *   - Check order: dtype, shape, zero-size no-op, NULL, alignment, device,
+ *     launch.  M == 0 or N == 0 (T == 0 for MoE) returns Q4_OK and touches
+ *     nothing (pointers may then be NULL).
+ *   - Alignment: every tensor pointer must be 16-byte aligned (the kernels
+ *     use 128-bit loads and stores).
+ *   - Device: the current HIP device must be a gfx950 GPU, else
+ *     Q4_ERR_DEVICE.
+ *   - The call returns once the work is enqueued on `stream` (a hipStream_t;
+ *     NULL is the default stream).  The caller owns and frees every buffer,
+ *     synchronises the stream, and keeps the buffers alive until the work
+ *     completes.  The library allocates no device memory.
+ *   - Calls are thread-safe; calls on one stream execute in order.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define Q4_API __attribute__((visibility("default")))
+#else
+#define Q4_API
+#endif
+
+#define Q4_ABI_VERSION 1
+
+/* Status codes. */
+#define Q4_OK            0
+#define Q4_ERR_NULL      1  /* a required pointer is NULL */
+#define Q4_ERR_SHAPE     2  /* negative size, K <= 0, K % 32 != 0, or size overflow */
+#define Q4_ERR_ALIGN     3  /* a tensor pointer is not 16-byte aligned */
+#define Q4_ERR_DTYPE     4  /* unknown output dtype */
+#define Q4_ERR_WORKSPACE 5  /* MoE workspace NULL/misaligned or too small */
+#define Q4_ERR_DEVICE    6  /* no current HIP device, or it is not gfx950 */
+#define Q4_ERR_LAUNCH    7  /* the HIP runtime reported an error at enqueue */
+
+/* Output dtypes. */
+#define Q4_F32  0
+#define Q4_BF16 1
+
+/* Paths chosen by q4_matmul. */
+#define Q4_PATH_GEMV 0      /* M <= 8: fused dequant + matrix-vector, exact weights */
+#define Q4_PATH_MFMA 1      /* M > 8: dequant to bf16 in LDS + bf16 matrix cores */
+
+typedef void *q4_stream_t;  /* a hipStream_t */
+
+/* ABI version of the loaded library (== Q4_ABI_VERSION it was built with).
+ * A caller built against another version must refuse to use it. */
+Q4_API int32_t q4_abi_version(void);
+
+/* Static, NUL-terminated description of a status code; never NULL
+ * (unknown codes map to "unknown status"). */
+Q4_API const char *q4_status_str(int32_t status);
+
+/* Path q4_matmul takes for M rows (Q4_PATH_GEMV or Q4_PATH_MFMA); -1 if
+ * M < 0.  Host-only: enqueues nothing. */
+Q4_API int32_t q4_matmul_path(int64_t M);
+
+/* y = x * dequant(W)^T.
+ *   x       bf16  [M][K]    device
+ *   w_q     uint8 [N][K/2]  device
+ *   w_s     fp16  [N][K/32] device
+ *   y       [M][N] device, fp32 (y_dtype = Q4_F32) or bf16 (Q4_BF16);
+ *           fully overwritten
+ *   M, N, K sizes (K a positive multiple of 32)
+ *   stream  hipStream_t or NULL
+ * Returns Q4_OK or an error code (see the conventions above). */
+Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
+                         void *y, int32_t y_dtype,
+                         int64_t M, int64_t N, int64_t K, q4_stream_t stream);
+
+/* Dequantise W to fp32 ((c-8)*s, exact) or bf16 (that value rounded
+ * nearest-even): w_out [N][K] device, out_dtype Q4_F32 or Q4_BF16.  Same
+ * conventions as q4_matmul (N == 0 is a no-op). */
+Q4_API int32_t q4_dequantize(const void *w_q, const void *w_s, void *w_out,
+                             int32_t out_dtype, int64_t N, int64_t K,
+                             q4_stream_t stream);
+
+/* Device workspace (bytes) q4_moe_matmul needs for these sizes; 0 if a size
+ * is negative or the size overflows. */
+Q4_API size_t q4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t N);
+
+/* Expert-routed rows:
+ *   y[t][n] = sum_{j < topk} g[t][j] * sum_k x[t][k] * w_{id[t][j]}[n][k]
+ *   x         bf16  [T][K]          device
+ *   w_q       uint8 [E][N][K/2]     device (E experts, each laid out as above)
+ *   w_s       fp16  [E][N][K/32]    device
+ *   topk_ids  int32 [T][topk]       device; an id outside [0, E) selects no
+ *                                   expert and contributes nothing; repeated
+ *                                   ids of one token are summed
+ *   topk_w    fp32  [T][topk]       device gate weights g
+ *   y         fp32  [T][N]          device, fully overwritten
+ *   workspace device scratch of at least q4_moe_workspace_bytes(T, topk, E, N)
+ *             bytes, 16-byte aligned, owned by the caller; its contents on
+ *             entry do not matter and it must not be shared by calls that
+ *             may run concurrently
+ * Every expert's weights are read once per call, whatever the number of
+ * tokens routed to it; the per-(token, slot) products are summed in slot
+ * order, so results are bit-identical from run to run.  Returns Q4_OK or an
+ * error code (Q4_ERR_WORKSPACE for a missing or short workspace). */
+Q4_API int32_t q4_moe_matmul(const void *x, const void *w_q, const void *w_s,
+                             const int32_t *topk_ids, const float *topk_w,
+                             float *y,
+                             int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
+                             void *workspace, size_t workspace_bytes,
+                             q4_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

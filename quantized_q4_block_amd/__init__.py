@@ -1,0 +1,221 @@
+"""Python binding of libq4 -- weight-only 4-bit block-quantised matmul on
+MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libq4.so`` (built in-tree from ``csrc/`` by ``_build.py``).
+PyTorch supplies device memory and streams.  The functions carry the names
+of the C ABI in ``include/q4.h``:
+
+    q4_abi_version()                        -> int
+    q4_status_str(status)                   -> str
+    q4_matmul_path(M)                       -> Q4_PATH_GEMV | Q4_PATH_MFMA
+    q4_matmul(x, w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> y
+    q4_dequantize(w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> w
+    q4_moe_workspace_bytes(T, topk, E, N)   -> int
+    q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None,
+                  stream=None) -> y
+
+Tensor conventions (all CUDA/HIP device tensors, contiguous):
+    x    torch.bfloat16 [M][K]       (or int16/uint16 holding bf16 bits)
+    w_q  torch.uint8    [N][K/2]     (MoE: [E][N][K/2])
+    w_s  torch.float16  [N][K/32]    (or int16/uint16 holding fp16 bits)
+A non-zero status from the library raises ``Q4Error``.  If ``libq4.so`` is
+missing the import fails: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4.so")
+
+Q4_ABI_VERSION = 1
+Q4_OK = 0
+Q4_ERR_NULL = 1
+Q4_ERR_SHAPE = 2
+Q4_ERR_ALIGN = 3
+Q4_ERR_DTYPE = 4
+Q4_ERR_WORKSPACE = 5
+Q4_ERR_DEVICE = 6
+Q4_ERR_LAUNCH = 7
+Q4_F32 = 0
+Q4_BF16 = 1
+Q4_PATH_GEMV = 0
+Q4_PATH_MFMA = 1
+
+__all__ = [
+    "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
+    "q4_dequantize", "q4_moe_workspace_bytes", "q4_moe_matmul",
+]
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {q4_status_str(status)} (status {status})")
+
+
+def _open():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python quantized_q4_block_amd/_build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.q4_abi_version.argtypes = []
+    L.q4_abi_version.restype = I32
+    L.q4_status_str.argtypes = [I32]
+    L.q4_status_str.restype = ctypes.c_char_p
+    L.q4_matmul_path.argtypes = [I64]
+    L.q4_matmul_path.restype = I32
+    L.q4_matmul.argtypes = [P, P, P, P, I32, I64, I64, I64, P]
+    L.q4_matmul.restype = I32
+    L.q4_dequantize.argtypes = [P, P, P, I32, I64, I64, P]
+    L.q4_dequantize.restype = I32
+    L.q4_moe_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    L.q4_moe_workspace_bytes.restype = ctypes.c_size_t
+    L.q4_moe_matmul.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t, P]
+    L.q4_moe_matmul.restype = I32
+    if L.q4_abi_version() != Q4_ABI_VERSION:
+        raise ImportError(f"libq4 ABI version {L.q4_abi_version()} != {Q4_ABI_VERSION}")
+    return L
+
+
+lib = _open()
+
+
+def q4_abi_version() -> int:
+    return int(lib.q4_abi_version())
+
+
+def q4_status_str(status: int) -> str:
+    return lib.q4_status_str(int(status)).decode()
+
+
+def q4_matmul_path(M: int) -> int:
+    return int(lib.q4_matmul_path(int(M)))
+
+
+# ---------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check_dev(t, name, dtypes, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out_code(dtype):
+    torch = _torch()
+    if dtype == torch.float32:
+        return Q4_F32
+    if dtype == torch.bfloat16:
+        return Q4_BF16
+    raise TypeError(f"unsupported output dtype {dtype}")
+
+
+def q4_matmul(x, w_q, w_s, out=None, out_dtype=None, stream=None):
+    """y[M][N] = x[M][K] . dequant(W)[N][K]^T (fp32 or bf16 output)."""
+    torch = _torch()
+    _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _check_dev(w_q, "w_q", (torch.uint8,), 2)
+    _check_dev(w_s, "w_s", (torch.float16, torch.int16, torch.uint16), 2)
+    M, K = x.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] * 2 != K or tuple(w_s.shape) != (N, K // 32):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_q {tuple(w_q.shape)}, "
+                         f"w_s {tuple(w_s.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    else:
+        _check_dev(out, "out", (torch.float32, torch.bfloat16), 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    st = lib.q4_matmul(_ptr(x), _ptr(w_q), _ptr(w_s), _ptr(out), _out_code(out.dtype),
+                       M, N, K, _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_matmul")
+    return out
+
+
+def q4_dequantize(w_q, w_s, out=None, out_dtype=None, stream=None):
+    """W[N][K] = (code - 8) * scale, fp32 (exact) or bf16 (nearest-even)."""
+    torch = _torch()
+    _check_dev(w_q, "w_q", (torch.uint8,), 2)
+    _check_dev(w_s, "w_s", (torch.float16, torch.int16, torch.uint16), 2)
+    N, KH = w_q.shape
+    K = 2 * KH
+    if tuple(w_s.shape) != (N, K // 32):
+        raise ValueError("w_s has the wrong shape")
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype or torch.float32, device=w_q.device)
+    else:
+        _check_dev(out, "out", (torch.float32, torch.bfloat16), 2)
+        if tuple(out.shape) != (N, K):
+            raise ValueError("out has the wrong shape")
+    st = lib.q4_dequantize(_ptr(w_q), _ptr(w_s), _ptr(out), _out_code(out.dtype), N, K,
+                           _stream_handle(stream, w_q.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_dequantize")
+    return out
+
+
+def q4_moe_workspace_bytes(T: int, topk: int, E: int, N: int) -> int:
+    return int(lib.q4_moe_workspace_bytes(int(T), int(topk), int(E), int(N)))
+
+
+def q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None, stream=None):
+    """y[T][N] = sum_j topk_w[t][j] * x[t] . dequant(W[topk_ids[t][j]])^T (fp32)."""
+    torch = _torch()
+    _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _check_dev(w_q, "w_q", (torch.uint8,), 3)
+    _check_dev(w_s, "w_s", (torch.float16, torch.int16, torch.uint16), 3)
+    _check_dev(topk_ids, "topk_ids", (torch.int32,), 2)
+    _check_dev(topk_w, "topk_w", (torch.float32,), 2)
+    T, K = x.shape
+    E, N = w_q.shape[0], w_q.shape[1]
+    topk = topk_ids.shape[1]
+    if w_q.shape[2] * 2 != K or tuple(w_s.shape) != (E, N, K // 32):
+        raise ValueError("weight shapes do not match x")
+    if tuple(topk_ids.shape) != (T, topk) or tuple(topk_w.shape) != (T, topk):
+        raise ValueError("topk_ids / topk_w must be [T][topk]")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    else:
+        _check_dev(out, "out", (torch.float32,), 2)
+        if tuple(out.shape) != (T, N):
+            raise ValueError("out has the wrong shape")
+    need = q4_moe_workspace_bytes(T, topk, E, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.q4_moe_matmul(_ptr(x), _ptr(w_q), _ptr(w_s), _ptr(topk_ids), _ptr(topk_w),
+                           _ptr(out), T, topk, E, N, K, _ptr(workspace),
+                           workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_moe_matmul")
+    return out

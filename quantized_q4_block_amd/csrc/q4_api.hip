@@ -1,0 +1,162 @@
+// q4_api.hip -- the C ABI (include/q4.h): argument checks, device check,
+// path dispatch, launches.
+//
+// The conventions follow the spec "spec: specialized model runtimes": a
+// runtime is an in-process library behind a C ABI whose version is pinned
+// (section "Prototype ABI scope"), failures come back as a clean value the
+// caller already handles (same section), and a runtime is only used on the
+// exact GPU architecture it was built for (section "Runtime selection",
+// condition 3).  Every check here runs on the host before anything is
+// enqueued, so an error never leaves partial work or a written output.
+#include <atomic>
+
+#include "../../include/q4.h"
+#include "q4_launch.h"
+
+namespace {
+
+constexpr int64_t kGemvMaxRows = 8;   // M <= 8 takes the matrix-vector path
+constexpr int kMaxDevices = 64;
+
+// 0 = unknown, 1 = gfx950, 2 = other.
+std::atomic<int> g_arch[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b without signed overflow, both >= 0; false on overflow past 2^62.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > (int64_t(1) << 62) / a) return false;
+  *out = a * b;
+  return true;
+}
+
+int32_t check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return Q4_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int known = g_arch[dev].load(std::memory_order_relaxed);
+    if (known == 1) return Q4_OK;
+    if (known == 2) return Q4_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return Q4_ERR_DEVICE;
+  }
+  const char* a = prop.gcnArchName;
+  const bool ok = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
+                  a[5] == '0' && (a[6] == '\0' || a[6] == ':');
+  if (dev < kMaxDevices) g_arch[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? Q4_OK : Q4_ERR_DEVICE;
+}
+
+int32_t check_weights(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K % 32 != 0) return Q4_ERR_SHAPE;
+  int64_t nk;
+  if (!mul_ok(N, K, &nk)) return Q4_ERR_SHAPE;
+  return Q4_OK;
+}
+
+int32_t launched(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+Q4_API int32_t q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+Q4_API const char* q4_status_str(int32_t status) {
+  switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "null pointer argument";
+    case Q4_ERR_SHAPE: return "invalid shape (negative size, K not a positive multiple of 32, or overflow)";
+    case Q4_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case Q4_ERR_DTYPE: return "unknown output dtype";
+    case Q4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case Q4_ERR_DEVICE: return "no current HIP device or it is not gfx950";
+    case Q4_ERR_LAUNCH: return "HIP runtime error at enqueue";
+    default: return "unknown status";
+  }
+}
+
+Q4_API int32_t q4_matmul_path(int64_t M) {
+  if (M < 0) return -1;
+  return M <= kGemvMaxRows ? Q4_PATH_GEMV : Q4_PATH_MFMA;
+}
+
+Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* y,
+                         int32_t y_dtype, int64_t M, int64_t N, int64_t K,
+                         q4_stream_t stream) {
+  if (y_dtype != Q4_F32 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+  if (M < 0) return Q4_ERR_SHAPE;
+  if (int32_t s = check_weights(N, K)) return s;
+  int64_t mk, mn;
+  if (!mul_ok(M, K, &mk) || !mul_ok(M, N, &mn)) return Q4_ERR_SHAPE;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!x || !w_q || !w_s || !y) return Q4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return Q4_ERR_ALIGN;
+  if (int32_t s = check_device()) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = y_dtype == Q4_BF16;
+  const auto* xp = static_cast<const uint16_t*>(x);
+  const auto* wp = static_cast<const uint8_t*>(w_q);
+  const auto* sp = static_cast<const uint16_t*>(w_s);
+  if (q4_matmul_path(M) == Q4_PATH_GEMV)
+    return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, st));
+  return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, st));
+}
+
+Q4_API int32_t q4_dequantize(const void* w_q, const void* w_s, void* w_out, int32_t out_dtype,
+                             int64_t N, int64_t K, q4_stream_t stream) {
+  if (out_dtype != Q4_F32 && out_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+  if (int32_t s = check_weights(N, K)) return s;
+  if (N == 0) return Q4_OK;
+  if (!w_q || !w_s || !w_out) return Q4_ERR_NULL;
+  if (!aligned16(w_q) || !aligned16(w_s) || !aligned16(w_out)) return Q4_ERR_ALIGN;
+  if (int32_t s = check_device()) return s;
+  return launched(q4::launch_dequant(static_cast<const uint8_t*>(w_q),
+                                     static_cast<const uint16_t*>(w_s), w_out,
+                                     out_dtype == Q4_BF16, N, K,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+Q4_API size_t q4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t N) {
+  int64_t P, PN;
+  if (T < 0 || topk < 0 || E < 0 || N < 0) return 0;
+  if (!mul_ok(T, topk, &P) || !mul_ok(P, N, &PN) || PN > (int64_t(1) << 40)) return 0;
+  if (E > (int64_t(1) << 40)) return 0;
+  return q4::moe_workspace_layout(T, topk, E, N).total;
+}
+
+Q4_API int32_t q4_moe_matmul(const void* x, const void* w_q, const void* w_s,
+                             const int32_t* topk_ids, const float* topk_w, float* y, int64_t T,
+                             int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
+                             size_t workspace_bytes, q4_stream_t stream) {
+  if (T < 0 || topk < 0 || E < 0) return Q4_ERR_SHAPE;
+  if (int32_t s = check_weights(N, K)) return s;
+  int64_t P, tk, en, enk;
+  if (!mul_ok(T, topk, &P) || !mul_ok(T, K, &tk) || !mul_ok(E, N, &en) || !mul_ok(en, K, &enk))
+    return Q4_ERR_SHAPE;
+  // the gathered kernel puts one workgroup row per touched expert (<= 65535)
+  if ((P < E ? P : E) > 65535) return Q4_ERR_SHAPE;
+  if (T == 0 || N == 0) return Q4_OK;
+  if (!y || !x || (topk > 0 && (!topk_ids || !topk_w))) return Q4_ERR_NULL;
+  if (E > 0 && topk > 0 && (!w_q || !w_s)) return Q4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_w && !aligned16(topk_w)) || (w_q && !aligned16(w_q)) || (w_s && !aligned16(w_s)))
+    return Q4_ERR_ALIGN;
+  const size_t need = q4_moe_workspace_bytes(T, topk, E, N);
+  if (need == 0 || !workspace || !aligned16(workspace) || workspace_bytes < need)
+    return Q4_ERR_WORKSPACE;
+  if (int32_t s = check_device()) return s;
+  return launched(q4::launch_moe(static_cast<const uint16_t*>(x),
+                                 static_cast<const uint8_t*>(w_q),
+                                 static_cast<const uint16_t*>(w_s), topk_ids, topk_w, y, T, topk,
+                                 E, N, K, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// q4_device.h -- device helpers shared by the gfx950 kernels of libq4.
+//
+// Weight format (the library's layout of the groupwise-int weights that the
+// spec "spec: specialized model runtimes" plans for its T0 quantised GEMM,
+// section "Target package and artifact"): codes c in 0..15 stand for c - 8,
+// two per byte (even k in the low nibble), one fp16 scale per 32 k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+constexpr int kBlock = 32;          // elements per scale block
+constexpr int kWave = 64;           // gfx950 wavefront width
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
+// Four exact fp16 pairs (c - 8) from one dword holding 8 codes.
+//
+// The dword's bytes b0..b3 hold elements e0..e7 (b_i low nibble = e_{2i},
+// high nibble = e_{2i+1}).  Masking one nibble per 16-bit half and OR-ing an
+// fp16 exponent makes each half an fp16 whose value is a constant plus the
+// code: with exponent 2^10 the low nibble (bits 0..3) is worth 1..8, with
+// exponent 2^6 the next nibble (bits 4..7) is worth 1..8 too.  One packed
+// fp16 subtract of (constant + 8) then leaves exactly c - 8 in each half.
+// Result pairs: p[0] = (e0, e4), p[1] = (e1, e5), p[2] = (e2, e6),
+// p[3] = (e3, e7) as (low half, high half).
+__device__ __forceinline__ void codes_to_half_pairs(uint32_t d, half2v p[4]) {
+  const half2v b_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
+  const half2v b_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
+  const uint32_t d8 = d >> 8;
+  p[0] = __builtin_bit_cast(half2v, (d & 0x000F000Fu) | 0x64006400u) - b_lo;
+  p[1] = __builtin_bit_cast(half2v, (d & 0x00F000F0u) | 0x54005400u) - b_hi;
+  p[2] = __builtin_bit_cast(half2v, (d8 & 0x000F000Fu) | 0x64006400u) - b_lo;
+  p[3] = __builtin_bit_cast(half2v, (d8 & 0x00F000F0u) | 0x54005400u) - b_hi;
+}
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+__device__ __forceinline__ float fp16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
+// Sum over the 64 lanes of a wavefront; every lane gets the total.  The
+// butterfly order is fixed, so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace q4

@@ -1,0 +1,192 @@
+// q4_gemm.hip -- prefill path (M > 8): dequant to bf16 in LDS + bf16 MFMA.
+//
+// At prefill shapes every weight is used by hundreds of activation rows, so
+// the quantised GEMM of the T0 kernel tier ("spec: specialized model
+// runtimes", sections "Architecture", "Feasibility gate" and "Phase 3"'s
+// tensor-core GEMM rung) is a dense contraction and belongs on the matrix
+// cores.  The pages' own design targets another vendor's block-scaled MMA;
+// here the codes are expanded once per workgroup tile into bf16 in LDS and
+// the gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16) does the products with
+// fp32 accumulation.
+//
+// Tile: 128 (activation rows) x 128 (weight rows) per workgroup of 4
+// wavefronts (2 x 2, each 64 x 64 = 2 x 2 MFMA 32x32 tiles), K step 64.
+// Each thread stages 32 activations (4 x 128-bit loads) and one 32-element
+// weight block (one 128-bit code load + one scale) per K step; the weights
+// are dequantised -- (c - 8) exact in fp16, times the scale exact in fp32,
+// rounded to bf16 nearest-even -- straight into LDS.  The next K step's
+// global loads are issued before the current step's MFMAs.  LDS rows are
+// padded by 8 bf16 so the 128-bit fragment reads of 8 consecutive rows fall
+// in distinct banks.  Workgroups are numbered so that the workgroups sharing
+// one weight tile land on the same XCD (same L2).
+#include "q4_device.h"
+#include "q4_launch.h"
+
+namespace q4 {
+
+namespace {
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDK = BK + 8;          // padded LDS row, in bf16
+constexpr int kThreads = 256;
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restrict__ x,
+                                                        const uint8_t* __restrict__ wq,
+                                                        const uint16_t* __restrict__ ws,
+                                                        void* __restrict__ y, int y_bf16,
+                                                        int64_t M, int64_t N, int64_t K,
+                                                        int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+
+  // XCD-aware tile order: consecutive workgroup ids go to different XCDs
+  // (round robin over 8), so give each XCD a contiguous range of tiles in
+  // which the activation-row tiles of one weight tile are adjacent.
+  const int total = tiles_m * tiles_n;
+  int c = blockIdx.x;
+  if (total % 8 == 0) c = (c % 8) * (total / 8) + c / 8;
+  const int tile_n = c / tiles_m;
+  const int tile_m = c % tiles_m;
+  const int64_t m0 = (int64_t)tile_m * BM;
+  const int64_t n0 = (int64_t)tile_n * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Staging assignment: thread -> (row, 32-wide half of the K step).
+  const int srow = tid >> 1;
+  const int shalf = tid & 1;
+  const int64_t bpr = K / kBlock;
+  const int64_t am = m0 + srow;
+  const int64_t bn = n0 + srow;
+  const bool a_ok = am < M;
+  const bool b_ok = bn < N;
+  const uint16_t* a_src = x + (a_ok ? am : 0) * K;
+  const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
+  const uint16_t* s_src = ws + (b_ok ? bn : 0) * bpr;
+
+  uint4 a_reg[4];
+  uint4 b_codes;
+  float b_scale;
+
+  auto load_step = [&](int64_t k0) {
+    const int64_t blk = k0 / kBlock + shalf;
+    const bool in_k = blk < bpr;
+    if (a_ok && in_k) {
+      const uint4* p = reinterpret_cast<const uint4*>(a_src + blk * kBlock);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a_reg[q] = p[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a_reg[q] = make_uint4(0, 0, 0, 0);
+    }
+    if (b_ok && in_k) {
+      b_codes = *reinterpret_cast<const uint4*>(b_src + blk * 16);
+      b_scale = fp16_to_f32(s_src[blk]);
+    } else {
+      b_codes = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);  // code 8 = 0
+      b_scale = 0.0f;
+    }
+  };
+
+  auto store_step = [&]() {
+    uint4* ad = reinterpret_cast<uint4*>(As + srow * LDK + shalf * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ad[q] = a_reg[q];
+    const uint32_t dw[4] = {b_codes.x, b_codes.y, b_codes.z, b_codes.w};
+    uint4* bd = reinterpret_cast<uint4*>(Bs + srow * LDK + shalf * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2v p[4];
+      codes_to_half_pairs(dw[i], p);
+      // elements 8i..8i+7 are p0.lo p1.lo p2.lo p3.lo p0.hi p1.hi p2.hi p3.hi
+      uint4 o;
+      o.x = pack_bf16x2((float)p[0][0] * b_scale, (float)p[1][0] * b_scale);
+      o.y = pack_bf16x2((float)p[2][0] * b_scale, (float)p[3][0] * b_scale);
+      o.z = pack_bf16x2((float)p[0][1] * b_scale, (float)p[1][1] * b_scale);
+      o.w = pack_bf16x2((float)p[2][1] * b_scale, (float)p[3][1] * b_scale);
+      bd[i] = o;
+    }
+  };
+
+  f32x16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int64_t nk = (K + BK - 1) / BK;
+  load_step(0);
+  store_step();
+  __syncthreads();
+
+  const int frow = lane & 31;          // fragment row within a 32-row MFMA tile
+  const int fk = (lane >> 5) * 8;      // fragment k offset within a 16-wide MFMA step
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_step((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8v a_frag[2], b_frag[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(As + (wm * 64 + i * 32 + frow) * LDK + kk + fk);
+        a_frag[i] = __builtin_bit_cast(bf16x8v, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + j * 32 + frow) * LDK + kk + fk);
+        b_frag[j] = __builtin_bit_cast(bf16x8v, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag[i], b_frag[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      store_step();
+      __syncthreads();
+    }
+  }
+
+  // D layout of a 32x32 MFMA tile: lane l holds column l % 32, rows
+  // 8 * (v / 4) + 4 * (l / 32) + (v % 4) for v = 0..15.
+  const int col = lane & 31;
+  const int rbase = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 32 + col;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v / 4) + rbase + (v % 4);
+        if (m < M) {
+          if (y_bf16)
+            static_cast<uint16_t*>(y)[m * N + n] = to_bf16(acc[i][j][v]);
+          else
+            static_cast<float*>(y)[m * N + n] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t tm = (M + BM - 1) / BM;
+  const int64_t tn = (N + BN - 1) / BN;
+  if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  gemm_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+      x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,32 @@
+// q4_launch.h -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4 {
+
+hipError_t launch_dequant(const uint8_t* wq, const uint16_t* ws, void* out, bool bf16,
+                          int64_t N, int64_t K, hipStream_t stream);
+
+// M <= 8 rows: fused dequant + matrix-vector product, exact weights.
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// M > 8 rows: dequant to bf16 in LDS + bf16 MFMA.
+hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Expert-routed rows; workspace laid out by moe_workspace_layout.
+struct MoeLayout {
+  size_t counts, fill, offsets, order, active, num_active, partial, total;
+};
+MoeLayout moe_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t N);
+
+hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
+                      const int32_t* ids, const float* gates, float* y, int64_t T,
+                      int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
+                      hipStream_t stream);
+
+}  // namespace q4

@@ -1,0 +1,230 @@
+// q4_moe.hip -- expert-routed rows: y[t] = sum_j g[t][j] * (x[t] . W_{id[t][j]}).
+//
+// The routed expert matmul plus weighted sum that the "Layer Package
+// Repository Spec" measures on its MoE decode fixture (paragraph on MoE
+// expert execution under "Policy Resolution": routed gate/up/down expert
+// matmuls are nearly all of a routed FFN layer's time, the matrix-vector
+// kernel wins at one token, and a separate weighted-sum op closes the layer).
+//
+// Three kernels, all on the caller's stream, no host round trip:
+//  1. prep (one workgroup): count the (token, slot) pairs per expert,
+//     exclusive-scan the counts, list the experts that got any pair, and
+//     bucket the pair indices by expert.  Everything it reads back is
+//     rebuilt from scratch on every call (the workspace needs no clearing).
+//  2. gathered matrix-vector product: one workgroup per (touched expert,
+//     64 weight rows); it reads that expert's rows once and applies them to
+//     all tokens routed to it (up to 8 at a time, more in chunks of 8),
+//     writing one fp32 partial row per (token, slot) pair.  A token's
+//     partial does not depend on which other tokens share the expert.
+//  3. weighted sum: y[t][n] = sum over slots j in order of g[t][j] * partial.
+// Results are bit-identical from run to run: atomics only assign bucket
+// slots (integers), never sum floating point.
+#include "q4_device.h"
+#include "q4_gemv.h"
+#include "q4_launch.h"
+
+namespace q4 {
+
+namespace {
+constexpr int kPrepThreads = 256;
+constexpr int kRowsPerWg = 64;     // weight rows per workgroup (16 per wavefront)
+constexpr int kRowsPerWave = 16;
+constexpr int kMaxTok = 8;         // tokens per gathered pass
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+}  // namespace
+
+MoeLayout moe_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t N) {
+  const size_t P = (size_t)T * (size_t)topk;
+  const size_t A = (size_t)(P < (size_t)E ? P : (size_t)E);
+  MoeLayout L;
+  size_t o = 0;
+  L.counts = o;     o = align_up(o + 4 * (size_t)E);
+  L.fill = o;       o = align_up(o + 4 * (size_t)E);
+  L.offsets = o;    o = align_up(o + 4 * (size_t)E);
+  L.order = o;      o = align_up(o + 4 * P);
+  L.active = o;     o = align_up(o + 4 * A);
+  L.num_active = o; o = align_up(o + 4);
+  L.partial = o;    o = align_up(o + 4 * P * (size_t)N);
+  L.total = o;
+  return L;
+}
+
+__global__ __launch_bounds__(kPrepThreads) void moe_prep_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int64_t E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ fill, int32_t* __restrict__ offsets, int32_t* __restrict__ order,
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
+  __shared__ int32_t s_cnt[kPrepThreads];
+  __shared__ int32_t s_act[kPrepThreads];
+  __shared__ int32_t s_base[2];
+  const int tid = threadIdx.x;
+
+  for (int64_t e = tid; e < E; e += kPrepThreads) {
+    counts[e] = 0;
+    fill[e] = 0;
+  }
+  __threadfence();
+  __syncthreads();
+  for (int64_t p = tid; p < P; p += kPrepThreads) {
+    const int32_t e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+  }
+  __threadfence();
+  __syncthreads();
+
+  if (tid == 0) { s_base[0] = 0; s_base[1] = 0; }
+  __syncthreads();
+  for (int64_t base = 0; base < E; base += kPrepThreads) {
+    const int64_t e = base + tid;
+    const int32_t c = e < E ? counts[e] : 0;
+    const int32_t a = c > 0 ? 1 : 0;
+    s_cnt[tid] = c;
+    s_act[tid] = a;
+    __syncthreads();
+    for (int off = 1; off < kPrepThreads; off <<= 1) {   // inclusive scan
+      const int32_t vc = tid >= off ? s_cnt[tid - off] : 0;
+      const int32_t va = tid >= off ? s_act[tid - off] : 0;
+      __syncthreads();
+      s_cnt[tid] += vc;
+      s_act[tid] += va;
+      __syncthreads();
+    }
+    if (e < E) {
+      offsets[e] = s_base[0] + s_cnt[tid] - c;
+      if (a) active[s_base[1] + s_act[tid] - 1] = (int32_t)e;
+    }
+    __syncthreads();
+    if (tid == kPrepThreads - 1) {
+      s_base[0] += s_cnt[tid];
+      s_base[1] += s_act[tid];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *num_active = s_base[1];
+  __threadfence();
+  __syncthreads();
+
+  for (int64_t p = tid; p < P; p += kPrepThreads) {
+    const int32_t e = ids[p];
+    if (e >= 0 && e < E) {
+      const int32_t slot = atomicAdd(&fill[e], 1);
+      order[offsets[e] + slot] = (int32_t)p;
+    }
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void moe_rows(const uint16_t* __restrict__ x,
+                                         const uint8_t* __restrict__ wq_e,
+                                         const uint16_t* __restrict__ ws_e,
+                                         const int32_t* pairs, int64_t topk,
+                                         float* __restrict__ partial, int64_t row0,
+                                         int64_t row_end, int64_t N, int64_t K) {
+  constexpr int R = GemvRows<M>::R;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* xrow[M];
+  int32_t pr[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    pr[m] = pairs[m];
+    xrow[m] = x + (int64_t)(pr[m] / topk) * K;
+  }
+  for (int64_t n0 = row0; n0 < row_end; n0 += R) {
+    float out[R][M];
+    gemv_tile<M, R>(xrow, wq_e, ws_e, n0, N - 1, K, out);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (lane == r * M + m && n0 + r < row_end) partial[(int64_t)pr[m] * N + n0 + r] = out[r][m];
+  }
+}
+
+__global__ __launch_bounds__(256) void moe_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ ws, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
+    float* __restrict__ partial, int64_t topk, int64_t N, int64_t K) {
+  const int slot = blockIdx.y;
+  if (slot >= *num_active) return;
+  const int32_t e = active[slot];
+  const int32_t start = offsets[e];
+  const int32_t cnt = counts[e];
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWg + wave * kRowsPerWave;
+  if (row0 >= N) return;
+  const int64_t row_end = row0 + kRowsPerWave < N ? row0 + kRowsPerWave : N;
+  const uint8_t* wq_e = wq + (int64_t)e * N * (K / 2);
+  const uint16_t* ws_e = ws + (int64_t)e * N * (K / kBlock);
+
+  for (int32_t c0 = 0; c0 < cnt; c0 += kMaxTok) {
+    const int32_t* pairs = order + start + c0;
+    const int32_t mc = cnt - c0 < kMaxTok ? cnt - c0 : kMaxTok;
+    switch (mc) {
+      case 1: moe_rows<1>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      case 2: moe_rows<2>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      case 3: moe_rows<3>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      case 4: moe_rows<4>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      case 5: moe_rows<5>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      case 6: moe_rows<6>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      case 7: moe_rows<7>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+      default: moe_rows<8>(x, wq_e, ws_e, pairs, topk, partial, row0, row_end, N, K); break;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ gates,
+                                                          const float* __restrict__ partial,
+                                                          float* __restrict__ y, int64_t T,
+                                                          int64_t topk, int64_t E, int64_t N) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T * N; i += stride) {
+    const int64_t t = i / N, n = i - t * N;
+    float acc = 0.0f;
+    for (int64_t j = 0; j < topk; ++j) {
+      const int64_t p = t * topk + j;
+      const int32_t e = ids[p];
+      if (e >= 0 && e < E) acc = __builtin_fmaf(gates[p], partial[p * N + n], acc);
+    }
+    y[i] = acc;
+  }
+}
+
+hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
+                      const int32_t* ids, const float* gates, float* y, int64_t T,
+                      int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
+                      hipStream_t stream) {
+  const MoeLayout L = moe_workspace_layout(T, topk, E, N);
+  char* wsp = static_cast<char*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(wsp + L.counts);
+  int32_t* fill = reinterpret_cast<int32_t*>(wsp + L.fill);
+  int32_t* offsets = reinterpret_cast<int32_t*>(wsp + L.offsets);
+  int32_t* order = reinterpret_cast<int32_t*>(wsp + L.order);
+  int32_t* active = reinterpret_cast<int32_t*>(wsp + L.active);
+  int32_t* num_active = reinterpret_cast<int32_t*>(wsp + L.num_active);
+  float* partial = reinterpret_cast<float*>(wsp + L.partial);
+  const int64_t P = T * topk;
+  const int64_t max_active = P < E ? P : E;
+
+  moe_prep_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(ids, P, E, counts, fill, offsets,
+                                                              order, active, num_active);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (max_active > 0) {
+    const int64_t row_blocks = (N + kRowsPerWg - 1) / kRowsPerWg;
+    if (row_blocks > 0x7FFFFFFF || max_active > 65535) return hipErrorInvalidValue;
+    moe_gemv_kernel<<<dim3((unsigned)row_blocks, (unsigned)max_active), dim3(256), 0, stream>>>(
+        x, wq, ws, counts, offsets, order, active, num_active, partial, topk, N, K);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  int64_t grid = (T * N + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  moe_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(ids, gates, partial, y, T,
+                                                                     topk, E, N);
+  return hipGetLastError();
+}
+
+}  // namespace q4

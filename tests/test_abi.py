@@ -1,0 +1,211 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU.
+
+None of these tests needs a GPU.  Calls with valid arguments and fake
+device pointers are made only where no GPU is present (they must then stop
+at the device check); on a machine with a GPU those cases are skipped so a
+fake pointer is never launched on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+def _lib():
+    q4 = pytest.importorskip("quantized_q4_block_amd")
+    return q4, q4.lib
+
+
+def _header():
+    return open(HEADER).read()
+
+
+def _declared_symbols():
+    return re.findall(r"^Q4_API\s+[^(]*?\b(q4_\w+)\s*\(", _header(), flags=re.M)
+
+
+def _defines():
+    return {k: int(v) for k, v in re.findall(r"^#define\s+(Q4_\w+)\s+(-?\d+)", _header(), flags=re.M)}
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_header_declares_the_abi():
+    syms = _declared_symbols()
+    assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
+                         "q4_dequantize", "q4_moe_workspace_bytes", "q4_moe_matmul"}
+
+
+def test_every_declared_symbol_is_exported():
+    q4, L = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", q4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for s in _declared_symbols():
+        assert s in exported, s
+        getattr(L, s)
+    # nothing but the ABI leaks out of the library
+    assert {s for s in exported if s.startswith("q4")} == set(_declared_symbols())
+
+
+def test_constants_match_header():
+    q4, L = _lib()
+    d = _defines()
+    for name in ("Q4_ABI_VERSION", "Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN",
+                 "Q4_ERR_DTYPE", "Q4_ERR_WORKSPACE", "Q4_ERR_DEVICE", "Q4_ERR_LAUNCH",
+                 "Q4_F32", "Q4_BF16", "Q4_PATH_GEMV", "Q4_PATH_MFMA"):
+        assert getattr(q4, name) == d[name], name
+    assert L.q4_abi_version() == d["Q4_ABI_VERSION"]
+
+
+def test_status_strings():
+    q4, L = _lib()
+    seen = set()
+    for code in range(0, 8):
+        s = q4.q4_status_str(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 8
+    assert q4.q4_status_str(99) == "unknown status"
+    assert q4.q4_status_str(-1) == "unknown status"
+
+
+def test_path_dispatch():
+    q4, _ = _lib()
+    for M in range(0, 9):
+        assert q4.q4_matmul_path(M) == q4.Q4_PATH_GEMV
+    for M in (9, 16, 127, 128, 512, 1 << 20):
+        assert q4.q4_matmul_path(M) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path(-1) == -1
+
+
+A = 1 << 20          # a 16-byte aligned fake address
+MIS = A + 8          # misaligned
+
+
+def _mm(L, x=A, wq=A, ws=A, y=A, dt=0, M=1, N=32, K=64):
+    P = ctypes.c_void_p
+    return L.q4_matmul(P(x), P(wq), P(ws), P(y), dt, M, N, K, None)
+
+
+def test_matmul_argument_errors():
+    q4, L = _lib()
+    assert _mm(L, dt=2) == q4.Q4_ERR_DTYPE
+    assert _mm(L, dt=-1) == q4.Q4_ERR_DTYPE
+    assert _mm(L, K=0) == q4.Q4_ERR_SHAPE
+    assert _mm(L, K=48) == q4.Q4_ERR_SHAPE
+    assert _mm(L, K=-32) == q4.Q4_ERR_SHAPE
+    assert _mm(L, N=-1) == q4.Q4_ERR_SHAPE
+    assert _mm(L, M=-1) == q4.Q4_ERR_SHAPE
+    assert _mm(L, M=1 << 40, N=1 << 40) == q4.Q4_ERR_SHAPE
+    assert _mm(L, N=1 << 40, K=1 << 40) == q4.Q4_ERR_SHAPE
+    # dtype is checked before shape
+    assert _mm(L, dt=7, K=3) == q4.Q4_ERR_DTYPE
+    # zero-size calls are no-ops, even with NULL pointers
+    assert _mm(L, x=0, wq=0, ws=0, y=0, M=0) == q4.Q4_OK
+    assert _mm(L, x=0, wq=0, ws=0, y=0, N=0) == q4.Q4_OK
+    # NULL, then alignment
+    for kw in ("x", "wq", "ws", "y"):
+        assert _mm(L, **{kw: 0}) == q4.Q4_ERR_NULL, kw
+        assert _mm(L, **{kw: MIS}) == q4.Q4_ERR_ALIGN, kw
+    # shape errors win over NULL
+    assert _mm(L, x=0, K=33) == q4.Q4_ERR_SHAPE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="would launch on fake pointers")
+def test_matmul_without_gpu_is_device_error():
+    q4, L = _lib()
+    assert _mm(L) == q4.Q4_ERR_DEVICE
+    assert _mm(L, M=64, dt=1) == q4.Q4_ERR_DEVICE
+
+
+def test_dequantize_argument_errors():
+    q4, L = _lib()
+    P = ctypes.c_void_p
+
+    def dq(wq=A, ws=A, out=A, dt=0, N=4, K=64):
+        return L.q4_dequantize(P(wq), P(ws), P(out), dt, N, K, None)
+
+    assert dq(dt=3) == q4.Q4_ERR_DTYPE
+    assert dq(K=31) == q4.Q4_ERR_SHAPE
+    assert dq(N=-2) == q4.Q4_ERR_SHAPE
+    assert dq(wq=0, ws=0, out=0, N=0) == q4.Q4_OK
+    assert dq(wq=0) == q4.Q4_ERR_NULL
+    assert dq(out=0) == q4.Q4_ERR_NULL
+    assert dq(ws=MIS) == q4.Q4_ERR_ALIGN
+    if not _gpu_present():
+        assert dq() == q4.Q4_ERR_DEVICE
+
+
+def test_moe_workspace_bytes():
+    q4, _ = _lib()
+    assert q4.q4_moe_workspace_bytes(-1, 8, 128, 1536) == 0
+    assert q4.q4_moe_workspace_bytes(8, -1, 128, 1536) == 0
+    assert q4.q4_moe_workspace_bytes(1 << 40, 1 << 20, 4, 4) == 0
+    b = q4.q4_moe_workspace_bytes(8, 8, 128, 1536)
+    # at least the per-(token, slot) fp32 partial rows
+    assert b >= 8 * 8 * 1536 * 4
+    assert b % 256 == 0
+    assert q4.q4_moe_workspace_bytes(16, 8, 128, 1536) > b
+    assert q4.q4_moe_workspace_bytes(8, 8, 256, 1536) > b
+
+
+def test_moe_argument_errors():
+    q4, L = _lib()
+    P = ctypes.c_void_p
+    T, topk, E, N, K = 8, 8, 128, 1536, 4096
+    need = q4.q4_moe_workspace_bytes(T, topk, E, N)
+
+    def moe(x=A, wq=A, ws=A, ids=A, g=A, y=A, T=T, topk=topk, E=E, N=N, K=K, w=A, wb=need):
+        return L.q4_moe_matmul(P(x), P(wq), P(ws), P(ids), P(g), P(y), T, topk, E, N, K, P(w),
+                               wb, None)
+
+    assert moe(K=100) == q4.Q4_ERR_SHAPE
+    assert moe(T=-1) == q4.Q4_ERR_SHAPE
+    assert moe(E=-1) == q4.Q4_ERR_SHAPE
+    assert moe(topk=-1) == q4.Q4_ERR_SHAPE
+    assert moe(T=70000, topk=1, E=70000) == q4.Q4_ERR_SHAPE
+    assert moe(x=0, wq=0, ws=0, ids=0, g=0, y=0, w=0, T=0) == q4.Q4_OK
+    for kw in ("x", "wq", "ws", "ids", "g", "y"):
+        assert moe(**{kw: 0}) == q4.Q4_ERR_NULL, kw
+        assert moe(**{kw: MIS}) == q4.Q4_ERR_ALIGN, kw
+    assert moe(w=0) == q4.Q4_ERR_WORKSPACE
+    assert moe(w=MIS) == q4.Q4_ERR_WORKSPACE
+    assert moe(wb=need - 1) == q4.Q4_ERR_WORKSPACE
+    if not _gpu_present():
+        assert moe() == q4.Q4_ERR_DEVICE
+
+
+def test_binding_rejects_host_tensors():
+    q4, _ = _lib()
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    wq = torch.zeros((4, 32), dtype=torch.uint8)
+    ws = torch.zeros((4, 2), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        q4.q4_matmul(x, wq, ws)
+    with pytest.raises(ValueError):
+        q4.q4_dequantize(wq, ws)
+
+
+def test_library_has_no_host_fallback():
+    """The package is only the binding: no compute in Python, no oracle."""
+    pkg = os.path.join(ROOT, "quantized_q4_block_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert "import oracle" not in src and "from oracle" not in src, name
