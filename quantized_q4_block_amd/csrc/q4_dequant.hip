@@ -18,6 +18,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       void* __restrict__ out,
                                                       int64_t n_blocks) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const CodeUnpacker unpack;
   for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < n_blocks;
        blk += stride) {
     const uint4 codes = *reinterpret_cast<const uint4*>(wq + blk * 16);
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2v p[4];
-      codes_to_half_pairs(dw[i], p);
+      unpack(dw[i], p);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[8 * i + j] = (float)p[j][0] * s;      // elements 8i + j

@@ -20,25 +20,41 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 
-// Four exact fp16 pairs (c - 8) from one dword holding 8 codes.
+// A value the compiler must treat as unknown, kept in a VGPR.  Used for the
+// unpack masks: gfx9 VOP3 encodings take no literal and read at most one
+// SGPR, so v_and_or_b32(codes, mask, magic) needs the mask in a VGPR (the
+// magic then rides in an SGPR); with both as constants the compiler falls
+// back to separate AND and OR instructions.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Unpacks codes into exact fp16 (c - 8) pairs.
 //
-// The dword's bytes b0..b3 hold elements e0..e7 (b_i low nibble = e_{2i},
+// A dword's bytes b0..b3 hold elements e0..e7 (b_i low nibble = e_{2i},
 // high nibble = e_{2i+1}).  Masking one nibble per 16-bit half and OR-ing an
 // fp16 exponent makes each half an fp16 whose value is a constant plus the
 // code: with exponent 2^10 the low nibble (bits 0..3) is worth 1..8, with
 // exponent 2^6 the next nibble (bits 4..7) is worth 1..8 too.  One packed
 // fp16 subtract of (constant + 8) then leaves exactly c - 8 in each half.
 // Result pairs: p[0] = (e0, e4), p[1] = (e1, e5), p[2] = (e2, e6),
-// p[3] = (e3, e7) as (low half, high half).
-__device__ __forceinline__ void codes_to_half_pairs(uint32_t d, half2v p[4]) {
-  const half2v b_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
-  const half2v b_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
-  const uint32_t d8 = d >> 8;
-  p[0] = __builtin_bit_cast(half2v, (d & 0x000F000Fu) | 0x64006400u) - b_lo;
-  p[1] = __builtin_bit_cast(half2v, (d & 0x00F000F0u) | 0x54005400u) - b_hi;
-  p[2] = __builtin_bit_cast(half2v, (d8 & 0x000F000Fu) | 0x64006400u) - b_lo;
-  p[3] = __builtin_bit_cast(half2v, (d8 & 0x00F000F0u) | 0x54005400u) - b_hi;
-}
+// p[3] = (e3, e7) as (low half, high half).  Cost per dword: one shift, four
+// v_and_or_b32, four v_pk_add_f16.
+struct CodeUnpacker {
+  uint32_t m_lo, m_hi;
+  __device__ __forceinline__ CodeUnpacker()
+      : m_lo(opaque_vgpr(0x000F000Fu)), m_hi(opaque_vgpr(0x00F000F0u)) {}
+  __device__ __forceinline__ void operator()(uint32_t d, half2v p[4]) const {
+    const half2v b_lo = {(_Float16)1032.0f, (_Float16)1032.0f};  // 1024 + 8
+    const half2v b_hi = {(_Float16)72.0f, (_Float16)72.0f};      // 64 + 8
+    const uint32_t d8 = d >> 8;
+    p[0] = __builtin_bit_cast(half2v, (d & m_lo) | 0x64006400u) - b_lo;
+    p[1] = __builtin_bit_cast(half2v, (d & m_hi) | 0x54005400u) - b_hi;
+    p[2] = __builtin_bit_cast(half2v, (d8 & m_lo) | 0x64006400u) - b_lo;
+    p[3] = __builtin_bit_cast(half2v, (d8 & m_hi) | 0x54005400u) - b_hi;
+  }
+};
 
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
@@ -51,6 +67,11 @@ __device__ __forceinline__ float fp16_to_f32(uint16_t h) {
 // fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Two fp32 -> packed fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  half2v v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ uint16_t to_bf16(float v) {

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
   const uint16_t* s_src = ws + (b_ok ? bn : 0) * bpr;
 
+  const CodeUnpacker unpack;
   uint4 a_reg[4];
   uint4 b_codes;
   float b_scale;
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2v p[4];
-      codes_to_half_pairs(dw[i], p);
+      unpack(dw[i], p);
       // elements 8i..8i+7 are p0.lo p1.lo p2.lo p3.lo p0.hi p1.hi p2.hi p3.hi
       uint4 o;
       o.x = pack_bf16x2((float)p[0][0] * b_scale, (float)p[1][0] * b_scale);

@@ -1,100 +1,448 @@
-// q4_gemv.h -- the wavefront matrix-vector tile shared by the dense decode
+// q4_gemv.h -- wavefront matrix-vector kernels shared by the dense decode
 // kernel and the expert-routed kernel.
+//
+// A task is R consecutive weight rows n0 .. n0+R-1 against M activation rows.
+// Lane l owns the 32-element blocks l, l+64, l+128, ... of every row of the
+// task ("stages"), so each row read is one coalesced run of 128-bit loads
+// (one block = 16 code bytes).  When K/32 is not a multiple of 64 and the
+// leftover r <= 32 blocks would leave half the lanes idle, the two
+// half-waves split the task's rows for that last stage instead: lanes 0..31
+// take the leftover blocks of the first R/2 rows, lanes 32..63 those of the
+// last R/2 rows, so every lane does the same work.
+//
+// Arithmetic per block and row: 4 dwords of codes -> 16 exact fp16 (c - 8)
+// pairs (one shift, four v_and_or_b32, four v_pk_add_f16 per dword), one
+// v_fma_mix_f32 per element and activation row (fp16 weight x fp32
+// activation, fp32 accumulate: every product exact), then one fma with the
+// block's fp16 scale into the row total.  The 64 lane totals are summed with
+// DPP row operations in a fixed order.  Lanes or slots outside the leftover
+// blocks add exactly nothing (their contribution is selected away, so even a
+// non-finite activation cannot leak in).
 #pragma once
 
 #include "q4_device.h"
 
 namespace q4 {
 
-// Rows per wavefront task for M activation rows: enough rows that one
-// activation load feeds several weight rows, few enough that R * M
-// accumulators (and R * M <= 64 storing lanes) fit.
-template <int M> struct GemvRows { static constexpr int R = M == 1 ? 8 : (M <= 4 ? 4 : 2); };
+// Rows per wavefront task for M activation rows.
+#ifndef Q4_GEMV_R_SMALL
+#define Q4_GEMV_R_SMALL 4
+#endif
+#ifndef Q4_GEMV_R_LARGE
+#define Q4_GEMV_R_LARGE 2
+#endif
+template <int M> struct GemvRows {
+  static constexpr int R = M <= 2 ? Q4_GEMV_R_SMALL : Q4_GEMV_R_LARGE;
+};
 
-// Dot products of M activation rows with R consecutive weight rows
-// n0 .. n0+R-1 of one weight matrix.  Rows past n_last are read as row
-// n_last (in bounds) and their results must be discarded by the caller.
-// Returns the totals in every lane.  Must be called by all 64 lanes of the
-// wavefront with the same arguments.
-//
-// Per lane and block: one 128-bit code load and one fp16 scale per row, one
-// 128-bit activation load per 8 elements per activation row (shared by the
-// R rows), then for each dword of codes 9 integer/fp16 ops and 8 fp32 fused
-// multiply-adds per activation row.
+// One DPP move of a float: lanes in ROW_MASK rows read the lane CTRL picks;
+// other rows read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float a) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront with DPP row ops; the total lands in
+// lanes 48..63.  Fixed order, so the result is deterministic.
+__device__ __forceinline__ float dpp_wave_sum(float v) {
+  v += dpp_f<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]: pairs
+  v += dpp_f<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: quads
+  v += dpp_f<0x141, 0xF>(v);  // row_half_mirror: 8 lanes
+  v += dpp_f<0x140, 0xF>(v);  // row_mirror: 16 lanes (a row)
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Wave-uniform total of a per-lane value.
+__device__ __forceinline__ float wave_total(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dpp_wave_sum(v)), 63));
+}
+
+// Stage geometry of a row of K elements (see the file comment).
+struct StagePlan {
+  int64_t bpr, full, S;  // blocks per row, full stages, stages
+  int rem;               // leftover blocks per row
+  bool split;            // leftover stage split between the half-waves
+  int sub;               // this lane's leftover block (within the last stage)
+  bool tail_ok;          // this lane has a leftover block
+  int half;              // 0: lanes 0..31, 1: lanes 32..63 (split only)
+  int64_t tail_b;        // block index this lane reads in the leftover stage
+  __device__ __forceinline__ StagePlan(int64_t K, int lane) {
+    bpr = K / kBlock;
+    full = bpr / kWave;
+    rem = (int)(bpr % kWave);
+    split = rem > 0 && rem <= kWave / 2;
+    S = full + (rem > 0 ? 1 : 0);
+    sub = split ? (lane & 31) : lane;
+    tail_ok = sub < rem;
+    half = split ? (lane >> 5) : 0;
+    tail_b = full * kWave + (tail_ok ? sub : 0);
+  }
+  __device__ __forceinline__ int64_t block(int64_t st, int lane) const {
+    return st < full ? st * kWave + lane : tail_b;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Block arithmetic.
+
+// acc[r][m] += s[r] * sum over one block of x[m] * (c[r] - 8), activations
+// given as bf16 (8 per uint4, converted here).
+template <int M, int RR>
+__device__ __forceinline__ void block_rows_bf16(const CodeUnpacker& unpack, const uint4 (&c)[RR],
+                                                const _Float16 (&s)[RR], const uint4 (&xd)[M][4],
+                                                float (&acc)[RR][M]) {
+  float part[RR][M];
+#pragma unroll
+  for (int r = 0; r < RR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[r][m] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {       // dword i: elements 8i .. 8i+7
+    float xv[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4 d = xd[m][i];
+      xv[m][0] = bf16_lo(d.x); xv[m][1] = bf16_hi(d.x);
+      xv[m][2] = bf16_lo(d.y); xv[m][3] = bf16_hi(d.y);
+      xv[m][4] = bf16_lo(d.z); xv[m][5] = bf16_hi(d.z);
+      xv[m][6] = bf16_lo(d.w); xv[m][7] = bf16_hi(d.w);
+    }
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+      const uint32_t d = i == 0 ? c[r].x : i == 1 ? c[r].y : i == 2 ? c[r].z : c[r].w;
+      half2v p[4];
+      unpack(d, p);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = part[r][m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a = __builtin_fmaf((float)p[j][0], xv[m][j], a);      // element 8i + j
+          a = __builtin_fmaf((float)p[j][1], xv[m][j + 4], a);  // element 8i + j + 4
+        }
+        part[r][m] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf((float)s[r], part[r][m], acc[r][m]);
+}
+
+// The same with fp32 activations xv[m][k], k = 0..31 within the block.
+template <int M, int RR>
+__device__ __forceinline__ void block_rows_f32(const CodeUnpacker& unpack, const uint4 (&c)[RR],
+                                               const _Float16 (&s)[RR], const float (&xv)[M][32],
+                                               float (&acc)[RR][M]) {
+#pragma unroll
+  for (int r = 0; r < RR; ++r) {
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t d = i == 0 ? c[r].x : i == 1 ? c[r].y : i == 2 ? c[r].z : c[r].w;
+      half2v p[4];
+      unpack(d, p);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          part[m] = __builtin_fmaf((float)p[j][0], xv[m][8 * i + j], part[m]);
+          part[m] = __builtin_fmaf((float)p[j][1], xv[m][8 * i + j + 4], part[m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf((float)s[r], part[m], acc[r][m]);
+  }
+}
+
+// Leftover-stage epilogue (not split): contributions t, computed from raw
+// loads, are added only by lanes that own a leftover block.
 template <int M, int R>
-__device__ __forceinline__ void gemv_tile(const uint16_t* const (&xrow)[M],
+__device__ __forceinline__ void add_tail(const StagePlan& sp, const float (&t)[R][M],
+                                         float (&acc)[R][M]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] += sp.tail_ok ? t[r][m] : 0.0f;
+}
+
+// Split leftover stage: slot j of half h is row h*H + j, so row r takes
+// slot r % H of the half that owns it, and only from lanes with a block.
+template <int M, int R>
+__device__ __forceinline__ void add_tail_split(const StagePlan& sp, const float (&t)[R / 2][M],
+                                               float (&acc)[R][M]) {
+  constexpr int H = R / 2;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const bool owns = r < H ? sp.half == 0 : sp.half == 1;
+      acc[r][m] += (sp.tail_ok && owns) ? t[r % H][m] : 0.0f;
+    }
+}
+
+// Row (relative to the task) that slot r of this lane reads in the
+// leftover stage.  Split: slots 0..H-1 hold this half's rows; the other
+// slots repeat a valid row and are never used.
+template <int R>
+__device__ __forceinline__ int64_t tail_row(const StagePlan& sp, int r) {
+  constexpr int H = R / 2;
+  return sp.split ? sp.half * H + (r % H) : r;
+}
+
+// ---------------------------------------------------------------------------
+// Activations in LDS as fp32 (exact from bf16), laid out [m][stage][chunk q]
+// [lane] in 16-byte units, chunk q = elements 4q .. 4q+3 of the block, so
+// that in a stage consecutive lanes read consecutive 16 bytes (no bank
+// conflicts).  Positions past K hold 0.
+__host__ __device__ __forceinline__ int64_t x_stages(int64_t K) {
+  return (K / kBlock + kWave - 1) / kWave;
+}
+__host__ __device__ __forceinline__ int64_t xlds_bytes(int64_t M, int64_t K) {
+  return M * x_stages(K) * 8 * kWave * 16;
+}
+
+// Copies the M activation rows into that layout (whole workgroup of
+// THREADS threads, S stages per row).
+template <int M, int S, int THREADS>
+__device__ __forceinline__ void stage_x_f32(const uint16_t* __restrict__ x, int64_t K,
+                                            float4* __restrict__ xs) {
+  constexpr int row_chunks = S * 8 * kWave;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int c0 = 0; c0 < row_chunks; c0 += THREADS) {
+      const int c = c0 + (int)threadIdx.x;
+      if (row_chunks % THREADS != 0 && c >= row_chunks) break;
+      const int st = c >> 9, q = (c >> 6) & 7, l = c & 63;
+      const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 4;
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (k < K) {
+        const uint2 d = *reinterpret_cast<const uint2*>(x + m * K + k);
+        v = make_float4(bf16_lo(d.x), bf16_hi(d.x), bf16_lo(d.y), bf16_hi(d.y));
+      }
+      xs[m * row_chunks + c] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One task of R rows with the activations in LDS and every code and scale
+// load issued up front, for rows of FULL whole stages plus a leftover stage
+// of kind TAIL (none, split between the half-waves, or one block per lane).
+//
+// Split in two so a kernel can issue the loads before it stages the
+// activations: the LDS staging and its barrier then overlap the loads'
+// HBM latency.  Rows past the last one are read as the last row (in
+// bounds); the caller discards their results.
+enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2 };
+
+template <int R, int FULL, int TAIL>
+struct UpfrontLoads {
+  static constexpr int TR = TAIL == kSplitTail ? R / 2 : (TAIL == kWideTail ? R : 0);
+  uint4 c[FULL > 0 ? FULL : 1][R];
+  _Float16 s[FULL > 0 ? FULL : 1][R];
+  uint4 ct[TR > 0 ? TR : 1];
+  _Float16 st[TR > 0 ? TR : 1];
+};
+
+// room = rows that exist past n0 (>= 0); rem = leftover blocks per row.
+template <int R, int FULL, int TAIL>
+__device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL>& b,
+                                             const uint8_t* __restrict__ wq,
+                                             const uint16_t* __restrict__ ws, int64_t n0,
+                                             int room, int64_t K, int rem, int lane) {
+  const uint32_t row_bytes = (uint32_t)(K / 2);
+  const uint32_t row_sc = (uint32_t)(K / kBlock);
+  const uint8_t* cbase = wq + n0 * (int64_t)row_bytes;   // wave-uniform
+  const uint16_t* sbase = ws + n0 * (int64_t)row_sc;
+  auto load = [&](int row, uint32_t blk, uint4& c, _Float16& s) {
+    row = row < room ? row : room;
+    c = *reinterpret_cast<const uint4*>(cbase + (uint32_t)row * row_bytes + blk * 16);
+    s = __builtin_bit_cast(_Float16, sbase[(uint32_t)row * row_sc + blk]);
+  };
+#pragma unroll
+  for (int st = 0; st < FULL; ++st)
+#pragma unroll
+    for (int r = 0; r < R; ++r) load(r, (uint32_t)(st * kWave + lane), b.c[st][r], b.s[st][r]);
+  if constexpr (TAIL == kSplitTail) {
+    constexpr int H = R / 2;
+    const int sub = lane & 31, half = lane >> 5;
+    const uint32_t blk = (uint32_t)(FULL * kWave + (sub < rem ? sub : 0));
+#pragma unroll
+    for (int j = 0; j < H; ++j) load(half * H + j, blk, b.ct[j], b.st[j]);
+  } else if constexpr (TAIL == kWideTail) {
+    const uint32_t blk = (uint32_t)(FULL * kWave + (lane < rem ? lane : 0));
+#pragma unroll
+    for (int r = 0; r < R; ++r) load(r, blk, b.ct[r], b.st[r]);
+  }
+}
+
+// Totals (wave-uniform) of the task loaded into b; xs is the LDS activation
+// table (fp32 layout above).
+template <int M, int R, int FULL, int TAIL>
+__device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL>& b,
+                                                const float4* xs, int rem, int lane,
+                                                float (&out)[R][M]) {
+  constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
+  const CodeUnpacker unpack;
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  auto read_x = [&](int st, int l, float (&xv)[M][32]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = xs[((m * S + st) * 8 + q) * kWave + l];
+        xv[m][4 * q + 0] = v.x;
+        xv[m][4 * q + 1] = v.y;
+        xv[m][4 * q + 2] = v.z;
+        xv[m][4 * q + 3] = v.w;
+      }
+  };
+#pragma unroll
+  for (int st = 0; st < FULL; ++st) {
+    float xv[M][32];
+    read_x(st, lane, xv);
+    block_rows_f32<M, R>(unpack, b.c[st], b.s[st], xv, acc);
+  }
+  if constexpr (TAIL == kSplitTail) {
+    constexpr int H = R / 2;
+    const int sub = lane & 31, half = lane >> 5;
+    float xv[M][32];
+    read_x(FULL, sub, xv);
+    float t[H][M];
+#pragma unroll
+    for (int j = 0; j < H; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m) t[j][m] = 0.0f;
+    block_rows_f32<M, H>(unpack, b.ct, b.st, xv, t);
+    // slot j of half h is row h*H + j; only lanes with a leftover block add
+    const bool ok = sub < rem;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const bool owns = r < H ? half == 0 : half == 1;
+        acc[r][m] += (ok && owns) ? t[r % H][m] : 0.0f;
+      }
+  } else if constexpr (TAIL == kWideTail) {
+    // A lane past the leftover blocks reads zero activations (LDS holds 0
+    // past K) and gets scale 0, so it adds exactly zero whatever its
+    // (clamped, real) codes and scale are.
+    float xv[M][32];
+    read_x(FULL, lane, xv);
+    const bool ok = lane < rem;
+    _Float16 sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (_Float16)0.0f;
+    block_rows_f32<M, R>(unpack, b.ct, sc, xv, acc);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) out[r][m] = wave_total(acc[r][m]);
+}
+
+// ---------------------------------------------------------------------------
+// One task of R rows with activations read from global memory (bf16),
+// loads one stage ahead.  Used by the expert-routed kernel, whose tokens are
+// gathered rows of x, and by the decode kernel when the activations do not
+// fit in LDS.  Rows past n_last are read as row n_last (in bounds); the
+// caller discards their results.  Totals are returned wave-uniform.
+template <int M, int R>
+__device__ __forceinline__ void gemv_task(const uint16_t* const (&xrow)[M],
                                           const uint8_t* __restrict__ wq,
                                           const uint16_t* __restrict__ ws, int64_t n0,
                                           int64_t n_last, int64_t K, float (&out)[R][M]) {
+  static_assert(R % 2 == 0, "rows per task must be even");
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t bpr = K / kBlock;   // blocks per row
+  const StagePlan sp(K, lane);
   const int64_t row_bytes = K / 2;
-  const uint8_t* wrow[R];
-  const uint16_t* srow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t n = (n0 + r < n_last) ? n0 + r : n_last;
-    wrow[r] = wq + n * row_bytes;
-    srow[r] = ws + n * bpr;
-  }
+  const CodeUnpacker unpack;
+
   float acc[R][M];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-  for (int64_t b = lane; b < bpr; b += kWave) {
-    uint4 codes[R];
-    float s[R];
+  struct Buf {
+    uint4 c[R];
+    _Float16 s[R];
+  };
+  auto load = [&](int64_t st, Buf& b) {
+    const int64_t blk = sp.block(st, lane);
+    const bool last = st >= sp.full;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      codes[r] = *reinterpret_cast<const uint4*>(wrow[r] + b * 16);
-      s[r] = fp16_to_f32(srow[r][b]);
+      const int64_t row = last ? tail_row<R>(sp, r) : r;
+      const int64_t n = n0 + row < n_last ? n0 + row : n_last;
+      b.c[r] = *reinterpret_cast<const uint4*>(wq + n * row_bytes + blk * 16);
+      b.s[r] = __builtin_bit_cast(_Float16, ws[n * sp.bpr + blk]);
     }
-    float part[R][M];
+  };
+  auto compute = [&](int64_t st, const Buf& b) {
+    uint4 xd[M][4];
+    const int64_t blk = sp.block(st, lane);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int m = 0; m < M; ++m) {
+      const uint4* p = reinterpret_cast<const uint4*>(xrow[m] + blk * kBlock);
 #pragma unroll
-      for (int m = 0; m < M; ++m) part[r][m] = 0.0f;
+      for (int q = 0; q < 4; ++q) xd[m][q] = p[q];
+    }
+    if (st < sp.full) {
+      block_rows_bf16<M, R>(unpack, b.c, b.s, xd, acc);
+    } else if (sp.split) {
+      constexpr int H = R / 2;
+      uint4 c[H];
+      _Float16 sc[H];
+      float t[H][M];
+#pragma unroll
+      for (int r = 0; r < H; ++r) {
+        c[r] = b.c[r];
+        sc[r] = b.s[r];
+#pragma unroll
+        for (int m = 0; m < M; ++m) t[r][m] = 0.0f;
+      }
+      block_rows_bf16<M, H>(unpack, c, sc, xd, t);
+      add_tail_split<M, R>(sp, t, acc);
+    } else {
+      float t[R][M];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) t[r][m] = 0.0f;
+      block_rows_bf16<M, R>(unpack, b.c, b.s, xd, t);
+      add_tail<M, R>(sp, t, acc);
+    }
+  };
 
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {       // dword i: elements 8i .. 8i+7
-      float xv[M][8];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint4 xd = *reinterpret_cast<const uint4*>(xrow[m] + b * kBlock + 8 * i);
-        xv[m][0] = bf16_lo(xd.x); xv[m][1] = bf16_hi(xd.x);
-        xv[m][2] = bf16_lo(xd.y); xv[m][3] = bf16_hi(xd.y);
-        xv[m][4] = bf16_lo(xd.z); xv[m][5] = bf16_hi(xd.z);
-        xv[m][6] = bf16_lo(xd.w); xv[m][7] = bf16_hi(xd.w);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t d = i == 0 ? codes[r].x : i == 1 ? codes[r].y : i == 2 ? codes[r].z : codes[r].w;
-        half2v p[4];
-        codes_to_half_pairs(d, p);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          float a = part[r][m];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a = __builtin_fmaf((float)p[j][0], xv[m][j], a);      // element 8i + j
-            a = __builtin_fmaf((float)p[j][1], xv[m][j + 4], a);  // element 8i + j + 4
-          }
-          part[r][m] = a;
-        }
-      }
+  Buf A, B;
+  if (sp.S > 0) load(0, A);
+  for (int64_t st = 0; st < sp.S; st += 2) {
+    if (st + 1 < sp.S) load(st + 1, B);
+    compute(st, A);
+    if (st + 1 < sp.S) {
+      if (st + 2 < sp.S) load(st + 2, A);
+      compute(st + 1, B);
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(s[r], part[r][m], acc[r][m]);
   }
-
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < M; ++m) out[r][m] = wave_sum(acc[r][m]);
+    for (int m = 0; m < M; ++m) out[r][m] = wave_total(acc[r][m]);
 }
 
 }  // namespace q4

@@ -9,65 +9,147 @@
 // matrix-vector kernel beat the matrix-matrix one about 5x for one token,
 // and taking several rows per thread group mattered more than other knobs.
 //
-// Mapping.  A wavefront owns R consecutive weight rows at a time (grid-stride
-// over row groups); lane l owns the 32-element blocks l, l+64, l+128, ... of
-// every row, so each row read is one coalesced run of 128-bit loads (one
-// block = 16 code bytes = one load per lane).  The activation block a lane
-// needs is loaded once per block index and reused for all R rows.
-//
-// Arithmetic.  Codes become exact fp16 (c - 8) pairs in registers (two
-// bitwise ops and one packed fp16 subtract per 4 codes); v_fma_mix_f32
-// multiplies each fp16 weight with the fp32 activation and accumulates in
-// fp32, so every product x * (c - 8) is exact.  Each 32-element block is
-// summed on its own, then scaled by its fp16 scale into the row total; the
-// 64 lane totals are combined by a fixed butterfly.  A row of zero weights
-// (all codes 8) gives exactly zero.
+// Two kernels (see q4_gemv.h for the per-wavefront work):
+//  * gemv_lds_kernel (M <= 4, rows of at most 4 x 64 blocks, activations
+//    within 64 KB as fp32) -- one task of 2 rows per wavefront, 8
+//    wavefronts per workgroup, compiled per row geometry.  Each wavefront
+//    first issues every code and scale load of its task, then the
+//    workgroup converts the activations to fp32 in LDS (one conversion per
+//    workgroup instead of one per task), so the staging and its barrier run
+//    while the weights are in flight.
+//  * gemv_glb_kernel -- one task per wavefront, activations read as bf16
+//    from global memory (L1/L2 hits); for longer rows.
+// Every product x * (c - 8) is exact and each 32-element block is summed on
+// its own before its scale is applied, so a row of zero weights (all codes
+// 8) gives exactly zero.
 #include "q4_device.h"
 #include "q4_gemv.h"
 #include "q4_launch.h"
 
 namespace q4 {
 
+constexpr int64_t kLdsLimit = 64 * 1024;
+
 template <int M, int R>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ x,
-                                                   const uint8_t* __restrict__ wq,
-                                                   const uint16_t* __restrict__ ws,
-                                                   void* __restrict__ y, int y_bf16,
-                                                   int64_t N, int64_t K) {
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void store_rows(void* __restrict__ y, int y_bf16, int64_t N,
+                                           int64_t n0, const float (&out)[R][M]) {
+  if ((threadIdx.x & 63) != 0) return;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (n0 + r >= N) break;
+      if (y_bf16)
+        static_cast<uint16_t*>(y)[m * N + n0 + r] = to_bf16(out[r][m]);
+      else
+        static_cast<float*>(y)[m * N + n0 + r] = out[r][m];
+    }
+}
+
+// Rows per task and wavefronts per workgroup of the LDS kernel.
+constexpr int kLdsRows = 2;
+constexpr int kLdsWaves = 8;
+constexpr int kLdsMaxStages = 4;   // K <= 8192
+
+// Rows of FULL whole stages plus a leftover stage of kind TAIL (so the row
+// geometry, and with it the register budget, is fixed at compile time).
+template <int M, int FULL, int TAIL>
+__global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint8_t* __restrict__ wq,
+                                                                  const uint16_t* __restrict__ ws,
+                                                                  void* __restrict__ y,
+                                                                  int y_bf16, int64_t N,
+                                                                  int64_t K, int rem) {
+  constexpr int R = kLdsRows;
+  constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
+  __shared__ float4 xs[M * S * 8 * kWave];
   const int lane = threadIdx.x & 63;
-  const int64_t groups = (N + R - 1) / R;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = ((int64_t)blockIdx.x * kLdsWaves + wave) * R;
+  const bool live = n0 < N;
+  const int64_t nl = live ? n0 : N - 1;
+  const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
+  // weight loads first: the staging below runs while they are in flight
+  UpfrontLoads<R, FULL, TAIL> b;
+  upfront_load<R, FULL, TAIL>(b, wq, ws, nl, room, K, rem, lane);
+  stage_x_f32<M, S, kLdsWaves * 64>(x, K, xs);
+  __syncthreads();
+  if (!live) return;
+  float out[R][M];
+  upfront_compute<M, R, FULL, TAIL>(b, xs, rem, lane, out);
+  store_rows<M, R>(y, y_bf16, N, n0, out);
+}
+
+template <int M, int FULL, int TAIL>
+static hipError_t launch_lds(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                             int yb, int64_t N, int64_t K, int rem, hipStream_t stream) {
+  constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
+  if constexpr ((int64_t)M * S * 8 * kWave * 16 > kLdsLimit) {
+    return hipErrorInvalidValue;   // never chosen (the caller checks the size)
+  } else {
+    const int64_t tasks = (N + kLdsRows - 1) / kLdsRows;
+    const int64_t grid = (tasks + kLdsWaves - 1) / kLdsWaves;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemv_lds_kernel<M, FULL, TAIL><<<dim3((unsigned)grid), dim3(kLdsWaves * 64), 0, stream>>>(
+        x, wq, ws, y, yb, N, K, rem);
+    return hipGetLastError();
+  }
+}
+
+// One task of R rows per wavefront, starting at row `row0`; activations
+// read from global memory.
+template <int M, int R>
+__global__ __launch_bounds__(256) void gemv_glb_kernel(const uint16_t* __restrict__ x,
+                                                       const uint8_t* __restrict__ wq,
+                                                       const uint16_t* __restrict__ ws,
+                                                       void* __restrict__ y, int y_bf16,
+                                                       int64_t N, int64_t K, int64_t row0) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = row0 + ((int64_t)blockIdx.x * 4 + wave) * R;
+  if (n0 >= N) return;
   const uint16_t* xrow[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) xrow[m] = x + m * K;
-
-  for (int64_t g = (int64_t)blockIdx.x * 4 + wave; g < groups; g += (int64_t)gridDim.x * 4) {
-    const int64_t n0 = g * R;
-    float out[R][M];
-    gemv_tile<M, R>(xrow, wq, ws, n0, N - 1, K, out);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        if (lane == r * M + m && n0 + r < N) {
-          if (y_bf16)
-            static_cast<uint16_t*>(y)[m * N + n0 + r] = to_bf16(out[r][m]);
-          else
-            static_cast<float*>(y)[m * N + n0 + r] = out[r][m];
-        }
-      }
-    }
-  }
+  float out[R][M];
+  gemv_task<M, R>(xrow, wq, ws, n0, N - 1, K, out);
+  store_rows<M, R>(y, y_bf16, N, n0, out);
 }
 
 template <int M, int R>
 static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                            bool y_bf16, int64_t N, int64_t K, hipStream_t stream) {
-  const int64_t groups = (N + R - 1) / R;
-  int64_t grid = (groups + 3) / 4;
-  if (grid > (1 << 20)) grid = 1 << 20;
-  gemv_kernel<M, R><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0,
-                                                                   N, K);
+  if constexpr (M <= 4) {
+    const int64_t bpr = K / kBlock;
+    const int64_t full = bpr / kWave;
+    const int rem = (int)(bpr % kWave);
+    const int tail = rem == 0 ? kNoTail : (rem <= kWave / 2 ? kSplitTail : kWideTail);
+    const int64_t S = full + (tail != kNoTail ? 1 : 0);
+    if (S <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) {
+      const int yb = y_bf16 ? 1 : 0;
+      switch (full * 3 + tail) {
+        case 0 * 3 + kSplitTail: return launch_lds<M, 0, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 0 * 3 + kWideTail: return launch_lds<M, 0, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 1 * 3 + kNoTail: return launch_lds<M, 1, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 1 * 3 + kSplitTail: return launch_lds<M, 1, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 1 * 3 + kWideTail: return launch_lds<M, 1, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 2 * 3 + kNoTail: return launch_lds<M, 2, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 2 * 3 + kSplitTail: return launch_lds<M, 2, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 2 * 3 + kWideTail: return launch_lds<M, 2, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 3 * 3 + kNoTail: return launch_lds<M, 3, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 3 * 3 + kSplitTail: return launch_lds<M, 3, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 3 * 3 + kWideTail: return launch_lds<M, 3, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        case 4 * 3 + kNoTail: return launch_lds<M, 4, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
+        default: break;   // not reachable: S <= 4
+      }
+    }
+  }
+  {
+    const int64_t tasks = (N + R - 1) / R;
+    const int64_t grid = (tasks + 3) / 4;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemv_glb_kernel<M, R><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, N, K, 0);
+  }
   return hipGetLastError();
 }
 

@@ -126,17 +126,19 @@ __device__ __forceinline__ void moe_rows(const uint16_t* __restrict__ x,
   int32_t pr[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    pr[m] = pairs[m];
+    pr[m] = __builtin_amdgcn_readfirstlane(pairs[m]);
     xrow[m] = x + (int64_t)(pr[m] / topk) * K;
   }
   for (int64_t n0 = row0; n0 < row_end; n0 += R) {
     float out[R][M];
-    gemv_tile<M, R>(xrow, wq_e, ws_e, n0, N - 1, K, out);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
+    gemv_task<M, R>(xrow, wq_e, ws_e, n0, N - 1, K, out);
+    if (lane == 0) {
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        if (lane == r * M + m && n0 + r < row_end) partial[(int64_t)pr[m] * N + n0 + r] = out[r][m];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (n0 + r < row_end) partial[(int64_t)pr[m] * N + n0 + r] = out[r][m];
+    }
   }
 }
 
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
   const int32_t e = active[slot];
   const int32_t start = offsets[e];
   const int32_t cnt = counts[e];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWg + wave * kRowsPerWave;
   if (row0 >= N) return;
   const int64_t row_end = row0 + kRowsPerWave < N ? row0 + kRowsPerWave : N;

@@ -181,6 +181,29 @@ def test_sparse_codes_exact_per_weight(M):
     assert_parity(y, y_ref, t, RTOL, what="sparse codes")
 
 
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("kind", ["wide", "subnormal", "huge", "tiny"])
+def test_gemv_activation_ranges(M, kind):
+    """Activation rows the decode kernel cannot scale into exact fp16 (range
+    beyond 2^28, a bf16 subnormal) or that sit at the ends of bf16's range:
+    results must still be exact-weight parity."""
+    N, K = 200, 5120
+    d = synthetic.dense_case(5300 + M, M, N, K)
+    x = d.x.copy()
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    if kind == "wide":
+        x[:, 7] = 0x5F00            # ~9.2e18 next to O(1) values
+    elif kind == "subnormal":
+        x[:, 100] = 0x0003          # bf16 subnormal
+    elif kind == "huge":
+        x = synthetic.f32_to_bf16_bits(xf * np.float32(2.0 ** 100))
+    else:
+        x = synthetic.f32_to_bf16_bits(xf * np.float32(2.0 ** -100))
+    y = matmul(x, d.w_q, d.w_s)
+    y_ref, t = oracle.matmul(x, d.w_q, d.w_s)
+    assert_parity(y, y_ref, t, RTOL, what=f"range {kind} M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 16])
 def test_closed_form_constant(M):
     K, N = 512, 70
