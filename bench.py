@@ -40,10 +40,15 @@ def weight_bytes(N, K):
     return N * K // 2 + N * (K // 32) * 2
 
 
-def csrc_digest():
+# Sources the decode GEMV kernel is built from: a counter summary taken on
+# other sources no longer describes the kernel.
+GEMV_SOURCES = ("q4_api.hip", "q4_device.h", "q4_gemv.h", "q4_gemv.hip", "q4_launch.h")
+
+
+def csrc_digest(names=GEMV_SOURCES):
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantized_q4_block_amd", "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in sorted(names):
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -133,6 +138,73 @@ class MoE:
             raise RuntimeError(f"q4_moe_matmul failed with status {st}")
 
 
+def calibration_copy(torch, mib, reps=3):
+    """A plain elementwise copy of known size (y = -x over `mib` MiB of fp32:
+    `mib` MiB read, `mib` MiB written per launch), run so that a counter pass
+    can scale the HBM byte counters against a kernel whose traffic is known."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def _counter_means(run_dir, counter):
+    """Mean per-dispatch value of `counter` by kernel name, from the
+    counter_collection.csv files a rocprofv3 --pmc run wrote under run_dir."""
+    import csv
+    sums, counts = {}, {}
+    for dirpath, _, files in os.walk(run_dir):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(dirpath, fn), newline="") as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    k = row["Kernel_Name"]
+                    sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+                    counts[k] = counts.get(k, 0) + 1
+    return {k: (sums[k] / counts[k], counts[k]) for k in sums}
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_mib, kernel_tag, kernel_match, algorithmic, out):
+    """HBM bytes per launch of the kernel whose name contains kernel_match:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
+    the calibration copy's known bytes to what the same counter read for it."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(table, sub):
+        hits = [(k, v) for k, v in table.items() if sub in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {sub!r}, found {[k for k, _ in hits]}")
+        return hits[0]
+
+    copy_bytes = copy_mib * (1 << 20)
+    (ck, (cf, _)), (_, (cw, _)) = pick(fetch, "neg"), pick(write, "neg")
+    (gk, (gf, nf)), (_, (gw, nw)) = pick(fetch, kernel_match), pick(write, kernel_match)
+    f_read = copy_bytes / (cf * 1024.0)
+    f_write = copy_bytes / (cw * 1024.0)
+    traffic = gf * 1024.0 * f_read + gw * 1024.0 * f_write
+    rec = {"kernel": gk, "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+           "FETCH_SIZE_KiB": gf, "WRITE_SIZE_KiB": gw,
+           "calibration": {"kernel": ck, "bytes_each_way": copy_bytes,
+                           "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                           "read_factor": f_read, "write_factor": f_write},
+           "hbm_bytes_per_launch": round(traffic),
+           "algorithmic_bytes_per_launch": algorithmic,
+           "traffic_over_algorithmic": traffic / algorithmic,
+           "csrc_digest": csrc_digest()}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def time_steps(torch, work, steps, warmup):
     """Host-timed steps (synchronised on both sides) and HIP-event time over
     the same region on the launch stream."""
@@ -153,7 +225,7 @@ def time_steps(torch, work, steps, warmup):
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(min_seconds=10.0, max_reps=20):
+def cpu_baseline(min_seconds=12.0, max_reps=100000):
     """The CPU oracle on decode_gate_up, repeated until >= min_seconds."""
     import oracle
     import synthetic
@@ -181,7 +253,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain copy kernel of this many MiB (for counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script with --calibrate-copy-mib 256 into the decode kernel's "
+                         "HBM traffic record under profiles/ (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], 256,
+                      "gemv_decode_gate_up", "gemv_lds_kernel", weight_bytes(34816, 5120),
+                      os.path.join(ROOT, "profiles", "gemv_decode_gate_up_pmc.json"))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the decode and prefill paths would shard the weight rows; see DESIGN.md)",
@@ -197,6 +280,9 @@ def main():
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    if args.calibrate_copy_mib:
+        progress(f"calibration copy: {args.calibrate_copy_mib} MiB")
+        calibration_copy(torch, args.calibrate_copy_mib)
     progress("decode_gate_up: generating inputs")
     head = Dense(torch, q4, "decode_gate_up")
     progress(f"decode_gate_up: timing {args.steps} steps over {head.copies} weight copies")
@@ -207,7 +293,9 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile("gemv_decode_gate_up", digest),
-            "kernel": "q4::gemv_kernel<1,8>", "avg_launch_us": round(ev_ms * 1e3, 3),
+            # K = 5120 is 160 blocks a row: two full 64-lane stages and a
+            # leftover stage of 32 blocks split between the half-waves
+            "kernel": "q4::gemv_lds_kernel<1, 2, 1>", "avg_launch_us": round(ev_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": head.wbytes}
     del head
     torch.cuda.empty_cache()
