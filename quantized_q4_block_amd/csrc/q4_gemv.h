@@ -20,6 +20,8 @@
 // non-finite activation cannot leak in).
 #pragma once
 
+#include <type_traits>
+
 #include "q4_device.h"
 
 namespace q4 {
@@ -284,6 +286,44 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL>& b,
 #pragma unroll
     for (int r = 0; r < R; ++r) load(r, blk, b.ct[r], b.st[r]);
   }
+}
+
+// Rows per task and wavefronts per workgroup of the kernels built on the
+// up-front loads; rows of at most kLdsMaxStages stages (K <= 8192).
+constexpr int kLdsRows = 2;
+constexpr int kLdsWaves = 8;
+constexpr int kLdsMaxStages = 4;
+
+// Calls f(FULL, TAIL) -- both std::integral_constant -- with the row
+// geometry of K when it has at most kLdsMaxStages stages; otherwise returns
+// hipErrorInvalidValue without calling f.
+template <class F>
+hipError_t dispatch_row_geometry(int64_t K, F&& f) {
+  using std::integral_constant;
+  const int64_t bpr = K / kBlock;
+  const int64_t full = bpr / kWave;
+  const int rem = (int)(bpr % kWave);
+  const int tail = rem == 0 ? kNoTail : (rem <= kWave / 2 ? kSplitTail : kWideTail);
+  switch (full * 3 + tail) {
+    case 0 * 3 + kSplitTail: return f(integral_constant<int, 0>{}, integral_constant<int, kSplitTail>{});
+    case 0 * 3 + kWideTail: return f(integral_constant<int, 0>{}, integral_constant<int, kWideTail>{});
+    case 1 * 3 + kNoTail: return f(integral_constant<int, 1>{}, integral_constant<int, kNoTail>{});
+    case 1 * 3 + kSplitTail: return f(integral_constant<int, 1>{}, integral_constant<int, kSplitTail>{});
+    case 1 * 3 + kWideTail: return f(integral_constant<int, 1>{}, integral_constant<int, kWideTail>{});
+    case 2 * 3 + kNoTail: return f(integral_constant<int, 2>{}, integral_constant<int, kNoTail>{});
+    case 2 * 3 + kSplitTail: return f(integral_constant<int, 2>{}, integral_constant<int, kSplitTail>{});
+    case 2 * 3 + kWideTail: return f(integral_constant<int, 2>{}, integral_constant<int, kWideTail>{});
+    case 3 * 3 + kNoTail: return f(integral_constant<int, 3>{}, integral_constant<int, kNoTail>{});
+    case 3 * 3 + kSplitTail: return f(integral_constant<int, 3>{}, integral_constant<int, kSplitTail>{});
+    case 3 * 3 + kWideTail: return f(integral_constant<int, 3>{}, integral_constant<int, kWideTail>{});
+    case 4 * 3 + kNoTail: return f(integral_constant<int, 4>{}, integral_constant<int, kNoTail>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Leftover blocks per row (0 .. 63).
+__host__ __device__ __forceinline__ int row_leftover(int64_t K) {
+  return (int)((K / kBlock) % kWave);
 }
 
 // Totals (wave-uniform) of the task loaded into b; xs is the LDS activation

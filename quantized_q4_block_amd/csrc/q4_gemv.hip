@@ -46,11 +46,6 @@ __device__ __forceinline__ void store_rows(void* __restrict__ y, int y_bf16, int
     }
 }
 
-// Rows per task and wavefronts per workgroup of the LDS kernel.
-constexpr int kLdsRows = 2;
-constexpr int kLdsWaves = 8;
-constexpr int kLdsMaxStages = 4;   // K <= 8192
-
 // Rows of FULL whole stages plus a leftover stage of kind TAIL (so the row
 // geometry, and with it the register budget, is fixed at compile time).
 template <int M, int FULL, int TAIL>
@@ -119,28 +114,13 @@ template <int M, int R>
 static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                            bool y_bf16, int64_t N, int64_t K, hipStream_t stream) {
   if constexpr (M <= 4) {
-    const int64_t bpr = K / kBlock;
-    const int64_t full = bpr / kWave;
-    const int rem = (int)(bpr % kWave);
-    const int tail = rem == 0 ? kNoTail : (rem <= kWave / 2 ? kSplitTail : kWideTail);
-    const int64_t S = full + (tail != kNoTail ? 1 : 0);
-    if (S <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) {
+    if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) {
       const int yb = y_bf16 ? 1 : 0;
-      switch (full * 3 + tail) {
-        case 0 * 3 + kSplitTail: return launch_lds<M, 0, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 0 * 3 + kWideTail: return launch_lds<M, 0, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 1 * 3 + kNoTail: return launch_lds<M, 1, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 1 * 3 + kSplitTail: return launch_lds<M, 1, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 1 * 3 + kWideTail: return launch_lds<M, 1, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 2 * 3 + kNoTail: return launch_lds<M, 2, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 2 * 3 + kSplitTail: return launch_lds<M, 2, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 2 * 3 + kWideTail: return launch_lds<M, 2, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 3 * 3 + kNoTail: return launch_lds<M, 3, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 3 * 3 + kSplitTail: return launch_lds<M, 3, kSplitTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 3 * 3 + kWideTail: return launch_lds<M, 3, kWideTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        case 4 * 3 + kNoTail: return launch_lds<M, 4, kNoTail>(x, wq, ws, y, yb, N, K, rem, stream);
-        default: break;   // not reachable: S <= 4
-      }
+      const int rem = row_leftover(K);
+      return dispatch_row_geometry(K, [&](auto full, auto tail) {
+        return launch_lds<M, decltype(full)::value, decltype(tail)::value>(x, wq, ws, y, yb, N, K,
+                                                                          rem, stream);
+      });
     }
   }
   {

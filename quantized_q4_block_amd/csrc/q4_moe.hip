@@ -9,13 +9,17 @@
 // Three kernels, all on the caller's stream, no host round trip:
 //  1. prep (one workgroup): count the (token, slot) pairs per expert,
 //     exclusive-scan the counts, list the experts that got any pair, and
-//     bucket the pair indices by expert.  Everything it reads back is
-//     rebuilt from scratch on every call (the workspace needs no clearing).
+//     bucket the pair indices by expert (counting in LDS when the experts
+//     fit, else in the workspace).  Everything it writes is rebuilt from
+//     scratch on every call (the workspace needs no clearing).
 //  2. gathered matrix-vector product: one workgroup per (touched expert,
-//     64 weight rows); it reads that expert's rows once and applies them to
-//     all tokens routed to it (up to 8 at a time, more in chunks of 8),
-//     writing one fp32 partial row per (token, slot) pair.  A token's
-//     partial does not depend on which other tokens share the expert.
+//     16 weight rows).  Each wavefront issues every code and scale load of
+//     its 2 rows once, then runs the expert's tokens one after another
+//     against those registers (each token's activations staged as fp32 in
+//     LDS), writing one fp32 partial row per (token, slot) pair.  Rows
+//     longer than the LDS path allows take a chunked kernel that reads the
+//     activations from global memory instead.  A token's partial does not
+//     depend on which other tokens share the expert.
 //  3. weighted sum: y[t][n] = sum over slots j in order of g[t][j] * partial.
 // Results are bit-identical from run to run: atomics only assign bucket
 // slots (integers), never sum floating point.
@@ -30,6 +34,7 @@ constexpr int kPrepThreads = 256;
 constexpr int kRowsPerWg = 64;     // weight rows per workgroup (16 per wavefront)
 constexpr int kRowsPerWave = 16;
 constexpr int kMaxTok = 8;         // tokens per gathered pass
+constexpr int kPrepLdsExperts = 4096;   // experts counted in LDS by the prep kernel
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 }  // namespace
@@ -50,6 +55,63 @@ MoeLayout moe_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t N) {
   return L;
 }
 
+// Prep with the per-expert counters in LDS (E <= kPrepLdsExperts).  Each
+// thread scans a contiguous run of experts, so the active list comes out in
+// ascending expert order.
+__global__ __launch_bounds__(kPrepThreads) void moe_prep_lds_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int64_t E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ order, int32_t* __restrict__ active,
+    int32_t* __restrict__ num_active) {
+  __shared__ int32_t s_cnt[kPrepLdsExperts];
+  __shared__ int32_t s_cur[kPrepLdsExperts];   // bucket cursors
+  __shared__ int32_t s_sc[kPrepThreads], s_sa[kPrepThreads];
+  const int tid = threadIdx.x;
+  const int ne = (int)E;
+  for (int e = tid; e < ne; e += kPrepThreads) s_cnt[e] = 0;
+  __syncthreads();
+  for (int64_t p = tid; p < P; p += kPrepThreads) {
+    const int32_t e = ids[p];
+    if (e >= 0 && e < ne) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  // per-thread run [lo, hi) of experts; inclusive scan of the run totals
+  const int chunk = (ne + kPrepThreads - 1) / kPrepThreads;
+  const int lo = tid * chunk < ne ? tid * chunk : ne;
+  const int hi = lo + chunk < ne ? lo + chunk : ne;
+  int c_sum = 0, a_sum = 0;
+  for (int e = lo; e < hi; ++e) {
+    c_sum += s_cnt[e];
+    a_sum += s_cnt[e] > 0 ? 1 : 0;
+  }
+  s_sc[tid] = c_sum;
+  s_sa[tid] = a_sum;
+  __syncthreads();
+  for (int off = 1; off < kPrepThreads; off <<= 1) {
+    const int vc = tid >= off ? s_sc[tid - off] : 0;
+    const int va = tid >= off ? s_sa[tid - off] : 0;
+    __syncthreads();
+    s_sc[tid] += vc;
+    s_sa[tid] += va;
+    __syncthreads();
+  }
+  int c_run = s_sc[tid] - c_sum, a_run = s_sa[tid] - a_sum;
+  for (int e = lo; e < hi; ++e) {
+    const int c = s_cnt[e];
+    counts[e] = c;
+    offsets[e] = c_run;
+    s_cur[e] = c_run;
+    if (c > 0) active[a_run++] = e;
+    c_run += c;
+  }
+  if (tid == kPrepThreads - 1) *num_active = s_sa[tid];
+  __syncthreads();
+  for (int64_t p = tid; p < P; p += kPrepThreads) {
+    const int32_t e = ids[p];
+    if (e >= 0 && e < ne) order[atomicAdd(&s_cur[e], 1)] = (int32_t)p;
+  }
+}
+
+// Prep with the counters in the workspace, for any number of experts.
 __global__ __launch_bounds__(kPrepThreads) void moe_prep_kernel(
     const int32_t* __restrict__ ids, int64_t P, int64_t E, int32_t* __restrict__ counts,
     int32_t* __restrict__ fill, int32_t* __restrict__ offsets, int32_t* __restrict__ order,
@@ -176,6 +238,56 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
   }
 }
 
+// Gathered product with the expert's rows loaded once: wavefront w of
+// workgroup (bx, slot) owns rows n0 = (bx * kLdsWaves + w) * kLdsRows ..
+// n0 + kLdsRows - 1 of expert active[slot]; row geometry fixed at compile
+// time as in the dense decode kernel.
+template <int FULL, int TAIL>
+__global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ ws, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
+    float* __restrict__ partial, int64_t topk, int64_t N, int64_t K, int rem) {
+  constexpr int R = kLdsRows;
+  constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
+  __shared__ float4 xs[S * 8 * kWave];
+  const int slot = blockIdx.y;
+  if (slot >= *num_active) return;                 // whole workgroup
+  const int32_t e = active[slot];
+  const int32_t start = offsets[e];
+  const int32_t cnt = counts[e];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = ((int64_t)blockIdx.x * kLdsWaves + wave) * R;
+  const bool live = n0 < N;
+  const int64_t nl = live ? n0 : N - 1;
+  const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
+  const uint8_t* wq_e = wq + (int64_t)e * N * (K / 2);
+  const uint16_t* ws_e = ws + (int64_t)e * N * (K / kBlock);
+  UpfrontLoads<R, FULL, TAIL> b;
+  upfront_load<R, FULL, TAIL>(b, wq_e, ws_e, nl, room, K, rem, lane);
+  for (int32_t i = 0; i < cnt; ++i) {
+    const int32_t p = order[start + i];
+    const int64_t t = p / topk;
+    if (i > 0) __syncthreads();                    // xs no longer read
+    stage_x_f32<1, S, kLdsWaves * 64>(x + t * K, K, xs);
+    __syncthreads();
+    if (live) {
+      float out[R][1];
+      upfront_compute<1, R, FULL, TAIL>(b, xs, rem, lane, out);
+      if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (n0 + r < N) partial[(int64_t)p * N + n0 + r] = out[r][0];
+      }
+    }
+  }
+}
+
+// y[t][n] = sum_j g[t][j] * partial[t * topk + j][n], j ascending; slots
+// with an id outside [0, E) add nothing.  The ids, gates and partials of
+// eight slots are loaded before any is used.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restrict__ ids,
                                                           const float* __restrict__ gates,
                                                           const float* __restrict__ partial,
@@ -185,10 +297,20 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T * N; i += stride) {
     const int64_t t = i / N, n = i - t * N;
     float acc = 0.0f;
-    for (int64_t j = 0; j < topk; ++j) {
-      const int64_t p = t * topk + j;
-      const int32_t e = ids[p];
-      if (e >= 0 && e < E) acc = __builtin_fmaf(gates[p], partial[p * N + n], acc);
+    for (int64_t j0 = 0; j0 < topk; j0 += 8) {
+      int32_t e[8];
+      float g[8], v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int64_t j = j0 + jj < topk ? j0 + jj : topk - 1;   // in bounds
+        const int64_t p = t * topk + j;
+        e[jj] = ids[p];
+        g[jj] = gates[p];
+        v[jj] = partial[p * N + n];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < topk && e[jj] >= 0 && e[jj] < E) acc = __builtin_fmaf(g[jj], v[jj], acc);
     }
     y[i] = acc;
   }
@@ -210,16 +332,34 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
   const int64_t P = T * topk;
   const int64_t max_active = P < E ? P : E;
 
-  moe_prep_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(ids, P, E, counts, fill, offsets,
-                                                              order, active, num_active);
+  if (E <= kPrepLdsExperts)
+    moe_prep_lds_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(ids, P, E, counts, offsets,
+                                                                   order, active, num_active);
+  else
+    moe_prep_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(ids, P, E, counts, fill, offsets,
+                                                                order, active, num_active);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (max_active > 65535) return hipErrorInvalidValue;
   if (max_active > 0) {
-    const int64_t row_blocks = (N + kRowsPerWg - 1) / kRowsPerWg;
-    if (row_blocks > 0x7FFFFFFF || max_active > 65535) return hipErrorInvalidValue;
-    moe_gemv_kernel<<<dim3((unsigned)row_blocks, (unsigned)max_active), dim3(256), 0, stream>>>(
-        x, wq, ws, counts, offsets, order, active, num_active, partial, topk, N, K);
-    err = hipGetLastError();
+    if (x_stages(K) <= kLdsMaxStages) {
+      const int64_t row_blocks = (N + kLdsWaves * kLdsRows - 1) / (kLdsWaves * kLdsRows);
+      if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+      const int rem = row_leftover(K);
+      const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
+      err = dispatch_row_geometry(K, [&](auto full, auto tail) {
+        moe_lds_kernel<decltype(full)::value, decltype(tail)::value>
+            <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, counts, offsets, order, active,
+                                                        num_active, partial, topk, N, K, rem);
+        return hipGetLastError();
+      });
+    } else {
+      const int64_t row_blocks = (N + kRowsPerWg - 1) / kRowsPerWg;
+      if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+      moe_gemv_kernel<<<dim3((unsigned)row_blocks, (unsigned)max_active), dim3(256), 0, stream>>>(
+          x, wq, ws, counts, offsets, order, active, num_active, partial, topk, N, K);
+      err = hipGetLastError();
+    }
     if (err != hipSuccess) return err;
   }
   int64_t grid = (T * N + 255) / 256;
