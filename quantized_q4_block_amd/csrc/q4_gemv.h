@@ -213,28 +213,46 @@ __host__ __device__ __forceinline__ int64_t xlds_bytes(int64_t M, int64_t K) {
 }
 
 // Copies the M activation rows into that layout (whole workgroup of
-// THREADS threads, S stages per row).
+// THREADS threads, S stages per row), in two steps so that a kernel can
+// issue the activation loads before its weight loads and convert them
+// while the weights are in flight: the memory counter waits for loads in
+// issue order, so data loaded first can be used without waiting for the
+// rest.
 template <int M, int S, int THREADS>
-__device__ __forceinline__ void stage_x_f32(const uint16_t* __restrict__ x, int64_t K,
-                                            float4* __restrict__ xs) {
-  constexpr int row_chunks = S * 8 * kWave;
+struct XStager {
+  static constexpr int kRowChunks = S * 8 * kWave;
+  static constexpr int kPer = (kRowChunks + THREADS - 1) / THREADS;
+  uint2 d[M][kPer];
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int64_t K) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-    for (int c0 = 0; c0 < row_chunks; c0 += THREADS) {
-      const int c = c0 + (int)threadIdx.x;
-      if (row_chunks % THREADS != 0 && c >= row_chunks) break;
-      const int st = c >> 9, q = (c >> 6) & 7, l = c & 63;
-      const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 4;
-      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (k < K) {
-        const uint2 d = *reinterpret_cast<const uint2*>(x + m * K + k);
-        v = make_float4(bf16_lo(d.x), bf16_hi(d.x), bf16_lo(d.y), bf16_hi(d.y));
+      for (int i = 0; i < kPer; ++i) {
+        const int c = i * THREADS + (int)threadIdx.x;
+        const int st = c >> 9, q = (c >> 6) & 7, l = c & 63;
+        const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 4;
+        const bool ok = (kRowChunks % THREADS == 0 || c < kRowChunks) && k < K;
+        // unconditional load from a clamped address, masked afterwards with
+        // a mask the compiler cannot trace back to `ok` (else it turns the
+        // load into a branch, and every branch waits for earlier loads)
+        const uint2 v = *reinterpret_cast<const uint2*>(x + m * K + (ok ? k : 0));
+        const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
+        d[m][i] = make_uint2(v.x & keep, v.y & keep);
       }
-      xs[m * row_chunks + c] = v;
-    }
   }
-}
+  __device__ __forceinline__ void store(float4* __restrict__ xs) const {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = i * THREADS + (int)threadIdx.x;
+        if (kRowChunks % THREADS != 0 && c >= kRowChunks) break;
+        xs[m * kRowChunks + c] =
+            make_float4(bf16_lo(d[m][i].x), bf16_hi(d[m][i].x), bf16_lo(d[m][i].y), bf16_hi(d[m][i].y));
+      }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // One task of R rows with the activations in LDS and every code and scale
@@ -290,8 +308,14 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL>& b,
 
 // Rows per task and wavefronts per workgroup of the kernels built on the
 // up-front loads; rows of at most kLdsMaxStages stages (K <= 8192).
-constexpr int kLdsRows = 2;
-constexpr int kLdsWaves = 8;
+#ifndef Q4_LDS_ROWS
+#define Q4_LDS_ROWS 2
+#endif
+#ifndef Q4_LDS_WAVES
+#define Q4_LDS_WAVES 8
+#endif
+constexpr int kLdsRows = Q4_LDS_ROWS;
+constexpr int kLdsWaves = Q4_LDS_WAVES;
 constexpr int kLdsMaxStages = 4;
 
 // Calls f(FULL, TAIL) -- both std::integral_constant -- with the row

@@ -64,15 +64,21 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(const uint16_t
   const bool live = n0 < N;
   const int64_t nl = live ? n0 : N - 1;
   const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
-  // weight loads first: the staging below runs while they are in flight
+  // activation loads, then weight loads; the activations are converted
+  // into LDS while the weights are in flight
+  XStager<M, S, kLdsWaves * 64> xst;
+  xst.load(x, K);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq, ws, nl, room, K, rem, lane);
-  stage_x_f32<M, S, kLdsWaves * 64>(x, K, xs);
+  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
+  xst.store(xs);
   __syncthreads();
-  if (!live) return;
+  // a wavefront past the last row computes on clamped rows and stores
+  // nothing (an early exit would let the compiler sink its loads past the
+  // barrier)
   float out[R][M];
   upfront_compute<M, R, FULL, TAIL>(b, xs, rem, lane, out);
-  store_rows<M, R>(y, y_bf16, N, n0, out);
+  if (live) store_rows<M, R>(y, y_bf16, N, n0, out);
 }
 
 template <int M, int FULL, int TAIL>

@@ -265,17 +265,24 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
   const uint8_t* wq_e = wq + (int64_t)e * N * (K / 2);
   const uint16_t* ws_e = ws + (int64_t)e * N * (K / kBlock);
+  // the first token's activation loads go out before the weight loads
+  XStager<1, S, kLdsWaves * 64> xst;
+  int32_t p = cnt > 0 ? order[start] : 0;
+  if (cnt > 0) xst.load(x + (int64_t)(p / topk) * K, K);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq_e, ws_e, nl, room, K, rem, lane);
+  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   for (int32_t i = 0; i < cnt; ++i) {
-    const int32_t p = order[start + i];
-    const int64_t t = p / topk;
-    if (i > 0) __syncthreads();                    // xs no longer read
-    stage_x_f32<1, S, kLdsWaves * 64>(x + t * K, K, xs);
+    if (i > 0) {
+      p = order[start + i];
+      xst.load(x + (int64_t)(p / topk) * K, K);
+      __syncthreads();                             // xs no longer read
+    }
+    xst.store(xs);
     __syncthreads();
+    float out[R][1];
+    upfront_compute<1, R, FULL, TAIL>(b, xs, rem, lane, out);   // all waves (no load sinking)
     if (live) {
-      float out[R][1];
-      upfront_compute<1, R, FULL, TAIL>(b, xs, rem, lane, out);
       if (lane == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
