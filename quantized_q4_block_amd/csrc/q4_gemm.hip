@@ -103,11 +103,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
       half2v p[4];
       unpack(dw[i], p);
       // elements 8i..8i+7 are p0.lo p1.lo p2.lo p3.lo p0.hi p1.hi p2.hi p3.hi
+      // fma(h, s, 0) with an fp16 h is one v_fma_mix_f32: the widening is
+      // folded into the multiply, and the product is exact in fp32
       uint4 o;
-      o.x = pack_bf16x2((float)p[0][0] * b_scale, (float)p[1][0] * b_scale);
-      o.y = pack_bf16x2((float)p[2][0] * b_scale, (float)p[3][0] * b_scale);
-      o.z = pack_bf16x2((float)p[0][1] * b_scale, (float)p[1][1] * b_scale);
-      o.w = pack_bf16x2((float)p[2][1] * b_scale, (float)p[3][1] * b_scale);
+      o.x = pack_bf16x2(__builtin_fmaf((float)p[0][0], b_scale, 0.0f),
+                        __builtin_fmaf((float)p[1][0], b_scale, 0.0f));
+      o.y = pack_bf16x2(__builtin_fmaf((float)p[2][0], b_scale, 0.0f),
+                        __builtin_fmaf((float)p[3][0], b_scale, 0.0f));
+      o.z = pack_bf16x2(__builtin_fmaf((float)p[0][1], b_scale, 0.0f),
+                        __builtin_fmaf((float)p[1][1], b_scale, 0.0f));
+      o.w = pack_bf16x2(__builtin_fmaf((float)p[2][1], b_scale, 0.0f),
+                        __builtin_fmaf((float)p[3][1], b_scale, 0.0f));
       bd[i] = o;
     }
   };
