@@ -2,7 +2,8 @@
 
 Headline workload: decode_gate_up -- the fused gate+up projection at decode,
 M = 1, K = 5120, N = 34816 (int4 codes, 32-element blocks, fp16 scales,
-bf16 activations, fp32 output).  A step is one q4_matmul call over one
+bf16 activations, fp32 output).  A step is one q4_matmul_ex call (with the
+workspace it asks for, none for this shape) over one
 activation row, i.e. the whole decode hot path (activation staging, weight
 and scale streaming, unpack + dequant, contraction, reduction, store).  The
 weights rotate over byte-identical copies totalling more than 1 GB so that
@@ -87,18 +88,22 @@ class Dense:
         self.bf16 = c["out"] == "bf16"
         self.y = torch.empty((self.M, self.N), device=dev,
                              dtype=torch.bfloat16 if self.bf16 else torch.float32)
+        # workspace for cutting long rows into slices, where the call can use one
+        need = q4.q4_matmul_workspace_bytes(self.M, self.N, self.K)
+        self.work = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         P = ctypes.c_void_p
-        self.fn = q4.lib.q4_matmul
+        wptr = P(self.work.data_ptr()) if need else P(0)
+        self.fn = q4.lib.q4_matmul_ex
         self.args = [(P(self.x.data_ptr()), P(self.wq[i].data_ptr()), P(self.ws[i].data_ptr()),
                       P(self.y.data_ptr()), q4.Q4_BF16 if self.bf16 else q4.Q4_F32,
-                      self.M, self.N, self.K) for i in range(n)]
+                      self.M, self.N, self.K, wptr, need) for i in range(n)]
         self.wbytes = wb
         self.flops = 2 * self.M * self.N * self.K
 
     def step(self, i, stream):
         st = self.fn(*self.args[i % self.copies], stream)
         if st:
-            raise RuntimeError(f"q4_matmul failed with status {st}")
+            raise RuntimeError(f"q4_matmul_ex failed with status {st}")
 
 
 class MoE:

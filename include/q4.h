@@ -45,7 +45,8 @@
  *   - The call returns once the work is enqueued on `stream` (a hipStream_t;
  *     NULL is the default stream).  The caller owns and frees every buffer,
  *     synchronises the stream, and keeps the buffers alive until the work
- *     completes.  The library allocates no device memory.
+ *     completes.  The library allocates no device memory; where a call can
+ *     use scratch memory it takes a caller-owned workspace.
  *   - Calls are thread-safe; calls on one stream execute in order.
  *   - No C++ exception crosses this boundary.
  */
@@ -65,7 +66,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 
 /* Status codes. */
 #define Q4_OK            0
@@ -73,7 +74,7 @@ extern "C" {
 #define Q4_ERR_SHAPE     2  /* negative size, K <= 0, K % 32 != 0, or size overflow */
 #define Q4_ERR_ALIGN     3  /* a tensor pointer is not 16-byte aligned */
 #define Q4_ERR_DTYPE     4  /* unknown output dtype */
-#define Q4_ERR_WORKSPACE 5  /* MoE workspace NULL/misaligned or too small */
+#define Q4_ERR_WORKSPACE 5  /* workspace NULL (MoE), misaligned or too small */
 #define Q4_ERR_DEVICE    6  /* no current HIP device, or it is not gfx950 */
 #define Q4_ERR_LAUNCH    7  /* the HIP runtime reported an error at enqueue */
 
@@ -111,6 +112,27 @@ Q4_API int32_t q4_matmul_path(int64_t M);
 Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
                          void *y, int32_t y_dtype,
                          int64_t M, int64_t N, int64_t K, q4_stream_t stream);
+
+/* Device workspace (bytes) that lets q4_matmul_ex cut long rows into
+ * slices (currently M <= 4 with K above 8192 or activations too large for
+ * one workgroup's LDS): slices * M * N fp32 partial sums.  0 when the call
+ * needs none, or for sizes q4_matmul would reject. */
+Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* q4_matmul with an optional workspace.  workspace == NULL: exactly
+ * q4_matmul.  Otherwise it must be 16-byte aligned and hold at least
+ * q4_matmul_workspace_bytes(M, N, K) bytes (else Q4_ERR_WORKSPACE, checked
+ * after the NULL and alignment checks of the tensors); its contents on
+ * entry do not matter, and calls that may run concurrently must not share
+ * it.  With a workspace, long rows are split into slices whose fp32 partial
+ * sums are added in slice order: the result is the same function of the
+ * inputs on every run, though its rounding can differ from the unsplit
+ * call's in the last bits. */
+Q4_API int32_t q4_matmul_ex(const void *x, const void *w_q, const void *w_s,
+                            void *y, int32_t y_dtype,
+                            int64_t M, int64_t N, int64_t K,
+                            void *workspace, size_t workspace_bytes,
+                            q4_stream_t stream);
 
 /* Dequantise W to fp32 ((c-8)*s, exact) or bf16 (that value rounded
  * nearest-even): w_out [N][K] device, out_dtype Q4_F32 or Q4_BF16.  Same

@@ -76,7 +76,7 @@ Q4_API const char* q4_status_str(int32_t status) {
     case Q4_ERR_SHAPE: return "invalid shape (negative size, K not a positive multiple of 32, or overflow)";
     case Q4_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case Q4_ERR_DTYPE: return "unknown output dtype";
-    case Q4_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case Q4_ERR_WORKSPACE: return "workspace missing (MoE), misaligned or too small";
     case Q4_ERR_DEVICE: return "no current HIP device or it is not gfx950";
     case Q4_ERR_LAUNCH: return "HIP runtime error at enqueue";
     default: return "unknown status";
@@ -88,9 +88,18 @@ Q4_API int32_t q4_matmul_path(int64_t M) {
   return M <= kGemvMaxRows ? Q4_PATH_GEMV : Q4_PATH_MFMA;
 }
 
-Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* y,
-                         int32_t y_dtype, int64_t M, int64_t N, int64_t K,
-                         q4_stream_t stream) {
+Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 0;
+  if (q4_matmul_path(M) != Q4_PATH_GEMV) return 0;
+  const int64_t slices = q4::gemv_split_slices(M, K);
+  int64_t mn, total;
+  if (slices == 0 || !mul_ok(M, N, &mn) || !mul_ok(mn, slices * 4, &total)) return 0;
+  return (size_t)total;
+}
+
+Q4_API int32_t q4_matmul_ex(const void* x, const void* w_q, const void* w_s, void* y,
+                            int32_t y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                            size_t workspace_bytes, q4_stream_t stream) {
   if (y_dtype != Q4_F32 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
   if (M < 0) return Q4_ERR_SHAPE;
   if (int32_t s = check_weights(N, K)) return s;
@@ -99,6 +108,12 @@ Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* 
   if (M == 0 || N == 0) return Q4_OK;
   if (!x || !w_q || !w_s || !y) return Q4_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y)) return Q4_ERR_ALIGN;
+  float* partial = nullptr;
+  if (workspace) {
+    const size_t need = q4_matmul_workspace_bytes(M, N, K);
+    if (!aligned16(workspace) || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+    if (need > 0) partial = static_cast<float*>(workspace);
+  }
   if (int32_t s = check_device()) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = y_dtype == Q4_BF16;
@@ -106,8 +121,14 @@ Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* 
   const auto* wp = static_cast<const uint8_t*>(w_q);
   const auto* sp = static_cast<const uint16_t*>(w_s);
   if (q4_matmul_path(M) == Q4_PATH_GEMV)
-    return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, st));
+    return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, partial, st));
   return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, st));
+}
+
+Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* y,
+                         int32_t y_dtype, int64_t M, int64_t N, int64_t K,
+                         q4_stream_t stream) {
+  return q4_matmul_ex(x, w_q, w_s, y, y_dtype, M, N, K, nullptr, 0, stream);
 }
 
 Q4_API int32_t q4_dequantize(const void* w_q, const void* w_s, void* w_out, int32_t out_dtype,

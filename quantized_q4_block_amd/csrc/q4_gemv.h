@@ -224,7 +224,9 @@ struct XStager {
   static constexpr int kPer = (kRowChunks + THREADS - 1) / THREADS;
   uint2 d[M][kPer];
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int64_t K) {
+  // x: row 0 of the activations at the first element of the row piece; K:
+  // length of the piece; ldx: distance between rows (elements).
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int64_t K, int64_t ldx) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -236,7 +238,7 @@ struct XStager {
         // unconditional load from a clamped address, masked afterwards with
         // a mask the compiler cannot trace back to `ok` (else it turns the
         // load into a branch, and every branch waits for earlier loads)
-        const uint2 v = *reinterpret_cast<const uint2*>(x + m * K + (ok ? k : 0));
+        const uint2 v = *reinterpret_cast<const uint2*>(x + m * ldx + (ok ? k : 0));
         const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
         d[m][i] = make_uint2(v.x & keep, v.y & keep);
       }
@@ -274,16 +276,16 @@ struct UpfrontLoads {
   _Float16 st[TR > 0 ? TR : 1];
 };
 
-// room = rows that exist past n0 (>= 0); rem = leftover blocks per row.
+// cbase / sbase: codes and scales of the task's first row at the first
+// block of the row piece; row_bytes / row_sc: distance between rows (bytes,
+// scales); room = rows that exist past the first (>= 0); rem = leftover
+// blocks of the piece.
 template <int R, int FULL, int TAIL>
 __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL>& b,
-                                             const uint8_t* __restrict__ wq,
-                                             const uint16_t* __restrict__ ws, int64_t n0,
-                                             int room, int64_t K, int rem, int lane) {
-  const uint32_t row_bytes = (uint32_t)(K / 2);
-  const uint32_t row_sc = (uint32_t)(K / kBlock);
-  const uint8_t* cbase = wq + n0 * (int64_t)row_bytes;   // wave-uniform
-  const uint16_t* sbase = ws + n0 * (int64_t)row_sc;
+                                             const uint8_t* __restrict__ cbase,
+                                             const uint16_t* __restrict__ sbase,
+                                             uint32_t row_bytes, uint32_t row_sc, int room,
+                                             int rem, int lane) {
   auto load = [&](int row, uint32_t blk, uint4& c, _Float16& s) {
     row = row < room ? row : room;
     c = *reinterpret_cast<const uint4*>(cbase + (uint32_t)row * row_bytes + blk * 16);
@@ -308,14 +310,8 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL>& b,
 
 // Rows per task and wavefronts per workgroup of the kernels built on the
 // up-front loads; rows of at most kLdsMaxStages stages (K <= 8192).
-#ifndef Q4_LDS_ROWS
-#define Q4_LDS_ROWS 2
-#endif
-#ifndef Q4_LDS_WAVES
-#define Q4_LDS_WAVES 8
-#endif
-constexpr int kLdsRows = Q4_LDS_ROWS;
-constexpr int kLdsWaves = Q4_LDS_WAVES;
+constexpr int kLdsRows = 2;
+constexpr int kLdsWaves = 8;
 constexpr int kLdsMaxStages = 4;
 
 // Calls f(FULL, TAIL) -- both std::integral_constant -- with the row

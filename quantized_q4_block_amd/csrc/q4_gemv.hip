@@ -48,13 +48,20 @@ __device__ __forceinline__ void store_rows(void* __restrict__ y, int y_bf16, int
 
 // Rows of FULL whole stages plus a leftover stage of kind TAIL (so the row
 // geometry, and with it the register budget, is fixed at compile time).
+//
+// The kernel works on a piece of each row: blocks blk0 .. blk0 + K/32 - 1
+// with blk0 = (slice0 + blockIdx.y) * slice_blocks, rows ld_blocks blocks
+// apart.  A whole-row call has one slice (blk0 = 0, ld_blocks = K/32) and
+// writes y; a split call (long rows) cuts the rows into one-stage slices
+// (FULL = 0, TAIL = kWideTail, rem < 0: each slice takes up to 64 blocks,
+// lanes past the row's end add zero) and writes the fp32 partial sums of
+// slice s to partial[s][M][N], which gemv_combine_kernel then adds in slice
+// order.
 template <int M, int FULL, int TAIL>
-__global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(const uint16_t* __restrict__ x,
-                                                                  const uint8_t* __restrict__ wq,
-                                                                  const uint16_t* __restrict__ ws,
-                                                                  void* __restrict__ y,
-                                                                  int y_bf16, int64_t N,
-                                                                  int64_t K, int rem) {
+__global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t N, int64_t K,
+    int rem, int64_t ld_blocks, int slice0, int slice_blocks, float* __restrict__ partial) {
   constexpr int R = kLdsRows;
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[M * S * 8 * kWave];
@@ -64,12 +71,22 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(const uint16_t
   const bool live = n0 < N;
   const int64_t nl = live ? n0 : N - 1;
   const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
+  const int slice = slice0 + (int)blockIdx.y;
+  const int64_t blk0 = (int64_t)slice * slice_blocks;
+  if (rem < 0) {   // one-stage slices: this slice's blocks (the last may be short)
+    const int64_t left = ld_blocks - blk0;
+    rem = (int)(left < kWave ? left : kWave);
+    K = (int64_t)rem * kBlock;
+  }
+  const uint32_t row_bytes = (uint32_t)(ld_blocks * 16), row_sc = (uint32_t)ld_blocks;
   // activation loads, then weight loads; the activations are converted
   // into LDS while the weights are in flight
   XStager<M, S, kLdsWaves * 64> xst;
-  xst.load(x, K);
+  xst.load(x + blk0 * kBlock, K, ld_blocks * kBlock);
   UpfrontLoads<R, FULL, TAIL> b;
-  upfront_load<R, FULL, TAIL>(b, wq, ws, nl, room, K, rem, lane);
+  upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes + blk0 * 16,
+                              ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
+                              lane);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.store(xs);
   __syncthreads();
@@ -78,23 +95,54 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(const uint16_t
   // barrier)
   float out[R][M];
   upfront_compute<M, R, FULL, TAIL>(b, xs, rem, lane, out);
-  if (live) store_rows<M, R>(y, y_bf16, N, n0, out);
+  if (!live) return;
+  if (partial)
+    store_rows<M, R>(partial + (int64_t)slice * M * N, 0, N, n0, out);
+  else
+    store_rows<M, R>(y, y_bf16, N, n0, out);
+}
+
+// y[i] = sum over slices s = 0 .. slices-1, in order, of partial[s][i].
+__global__ __launch_bounds__(256) void gemv_combine_kernel(const float* __restrict__ partial,
+                                                           void* __restrict__ y, int y_bf16,
+                                                           int64_t MN, int slices) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+    float acc = partial[i];
+    for (int s = 1; s < slices; ++s) acc += partial[(int64_t)s * MN + i];
+    if (y_bf16)
+      static_cast<uint16_t*>(y)[i] = to_bf16(acc);
+    else
+      static_cast<float*>(y)[i] = acc;
+  }
 }
 
 template <int M, int FULL, int TAIL>
 static hipError_t launch_lds(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                             int yb, int64_t N, int64_t K, int rem, hipStream_t stream) {
+                             int yb, int64_t N, int64_t K, int rem, int64_t ld_blocks,
+                             int slice0, int slices, int slice_blocks, float* partial,
+                             hipStream_t stream) {
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   if constexpr ((int64_t)M * S * 8 * kWave * 16 > kLdsLimit) {
     return hipErrorInvalidValue;   // never chosen (the caller checks the size)
   } else {
     const int64_t tasks = (N + kLdsRows - 1) / kLdsRows;
     const int64_t grid = (tasks + kLdsWaves - 1) / kLdsWaves;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemv_lds_kernel<M, FULL, TAIL><<<dim3((unsigned)grid), dim3(kLdsWaves * 64), 0, stream>>>(
-        x, wq, ws, y, yb, N, K, rem);
+    if (grid > 0x7FFFFFFF || slices > 65535) return hipErrorInvalidValue;
+    gemv_lds_kernel<M, FULL, TAIL>
+        <<<dim3((unsigned)grid, (unsigned)slices), dim3(kLdsWaves * 64), 0, stream>>>(
+            x, wq, ws, y, yb, N, K, rem, ld_blocks, slice0, slice_blocks, partial);
     return hipGetLastError();
   }
+}
+
+// Rows longer than the LDS kernel takes in one piece are cut into one-stage
+// slices (64 blocks, the last one shorter) when the caller gives a workspace
+// for the fp32 partial sums.
+int64_t gemv_split_slices(int64_t M, int64_t K) {
+  if (M < 1 || M > 4) return 0;
+  if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) return 0;
+  return x_stages(K);
 }
 
 // One task of R rows per wavefront, starting at row `row0`; activations
@@ -118,15 +166,29 @@ __global__ __launch_bounds__(256) void gemv_glb_kernel(const uint16_t* __restric
 
 template <int M, int R>
 static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                           bool y_bf16, int64_t N, int64_t K, hipStream_t stream) {
+                           bool y_bf16, int64_t N, int64_t K, float* partial,
+                           hipStream_t stream) {
+  const int yb = y_bf16 ? 1 : 0;
   if constexpr (M <= 4) {
+    const int64_t bpr = K / kBlock;
     if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) {
-      const int yb = y_bf16 ? 1 : 0;
       const int rem = row_leftover(K);
       return dispatch_row_geometry(K, [&](auto full, auto tail) {
-        return launch_lds<M, decltype(full)::value, decltype(tail)::value>(x, wq, ws, y, yb, N, K,
-                                                                          rem, stream);
+        return launch_lds<M, decltype(full)::value, decltype(tail)::value>(
+            x, wq, ws, y, yb, N, K, rem, bpr, 0, 1, 0, nullptr, stream);
       });
+    }
+    if (partial) {
+      const int64_t slices = gemv_split_slices(M, K);
+      hipError_t e = launch_lds<M, 0, kWideTail>(x, wq, ws, y, yb, N, kWave * kBlock, -1, bpr, 0,
+                                                 (int)slices, kWave, partial, stream);
+      if (e != hipSuccess) return e;
+      const int64_t MN = (int64_t)M * N;
+      int64_t grid = (MN + 255) / 256;
+      if (grid > 65536) grid = 65536;
+      gemv_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(partial, y, yb, MN,
+                                                                          (int)slices);
+      return hipGetLastError();
     }
   }
   {
@@ -134,22 +196,23 @@ static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t*
     const int64_t grid = (tasks + 3) / 4;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     gemv_glb_kernel<M, R><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
-        x, wq, ws, y, y_bf16 ? 1 : 0, N, K, 0);
+        x, wq, ws, y, yb, N, K, 0);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                       hipStream_t stream) {
   switch (M) {
-    case 1: return launch_m<1, GemvRows<1>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 2: return launch_m<2, GemvRows<2>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 3: return launch_m<3, GemvRows<3>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 4: return launch_m<4, GemvRows<4>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 5: return launch_m<5, GemvRows<5>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 6: return launch_m<6, GemvRows<6>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 7: return launch_m<7, GemvRows<7>::R>(x, wq, ws, y, y_bf16, N, K, stream);
-    case 8: return launch_m<8, GemvRows<8>::R>(x, wq, ws, y, y_bf16, N, K, stream);
+    case 1: return launch_m<1, GemvRows<1>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 2: return launch_m<2, GemvRows<2>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 3: return launch_m<3, GemvRows<3>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 4: return launch_m<4, GemvRows<4>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 5: return launch_m<5, GemvRows<5>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 6: return launch_m<6, GemvRows<6>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 7: return launch_m<7, GemvRows<7>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
+    case 8: return launch_m<8, GemvRows<8>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -11,8 +11,15 @@ hipError_t launch_dequant(const uint8_t* wq, const uint16_t* ws, void* out, bool
                           int64_t N, int64_t K, hipStream_t stream);
 
 // M <= 8 rows: fused dequant + matrix-vector product, exact weights.
+// partial: NULL, or fp32 scratch of gemv_split_slices(M, K) * M * N floats
+// that lets long rows be cut into slices.
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                       hipStream_t stream);
+
+// Slices a row of K is cut into on the matrix-vector path when scratch is
+// given (0: never cut).
+int64_t gemv_split_slices(int64_t M, int64_t K);
 
 // M > 8 rows: dequant to bf16 in LDS + bf16 MFMA.
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,

@@ -268,14 +268,16 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   // the first token's activation loads go out before the weight loads
   XStager<1, S, kLdsWaves * 64> xst;
   int32_t p = cnt > 0 ? order[start] : 0;
-  if (cnt > 0) xst.load(x + (int64_t)(p / topk) * K, K);
+  if (cnt > 0) xst.load(x + (int64_t)(p / topk) * K, K, K);
+  const uint32_t row_bytes = (uint32_t)(K / 2), row_sc = (uint32_t)(K / kBlock);
   UpfrontLoads<R, FULL, TAIL> b;
-  upfront_load<R, FULL, TAIL>(b, wq_e, ws_e, nl, room, K, rem, lane);
+  upfront_load<R, FULL, TAIL>(b, wq_e + nl * (int64_t)row_bytes, ws_e + nl * (int64_t)row_sc,
+                              row_bytes, row_sc, room, rem, lane);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   for (int32_t i = 0; i < cnt; ++i) {
     if (i > 0) {
       p = order[start + i];
-      xst.load(x + (int64_t)(p / topk) * K, K);
+      xst.load(x + (int64_t)(p / topk) * K, K, K);
       __syncthreads();                             // xs no longer read
     }
     xst.store(xs);

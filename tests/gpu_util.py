@@ -35,6 +35,12 @@ def matmul(x, w_q, w_s, out_dtype=torch.float32):
     return host(y)
 
 
+def matmul_ex(x, w_q, w_s, out_dtype=torch.float32, workspace="auto"):
+    y = q4.q4_matmul_ex(dev(x), dev(w_q), dev(w_s), out_dtype=out_dtype, workspace=workspace)
+    torch.cuda.synchronize()
+    return host(y)
+
+
 def moe(x, w_q, w_s, ids, gates):
     y = q4.q4_moe_matmul(dev(x), dev(w_q), dev(w_s), dev(ids), dev(gates))
     torch.cuda.synchronize()

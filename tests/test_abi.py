@@ -47,7 +47,8 @@ def _gpu_present() -> bool:
 def test_header_declares_the_abi():
     syms = _declared_symbols()
     assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
-                         "q4_dequantize", "q4_moe_workspace_bytes", "q4_moe_matmul"}
+                         "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
+                         "q4_moe_workspace_bytes", "q4_moe_matmul"}
 
 
 def test_every_declared_symbol_is_exported():
@@ -126,11 +127,48 @@ def test_matmul_argument_errors():
     assert _mm(L, x=0, K=33) == q4.Q4_ERR_SHAPE
 
 
+def test_matmul_workspace_bytes():
+    q4, _ = _lib()
+    # rows that fit one workgroup's LDS, the matrix-core path and bad shapes need none
+    assert q4.q4_matmul_workspace_bytes(1, 34816, 5120) == 0
+    assert q4.q4_matmul_workspace_bytes(512, 34816, 5120) == 0
+    assert q4.q4_matmul_workspace_bytes(5, 5120, 17408) == 0
+    assert q4.q4_matmul_workspace_bytes(4, 5120, 48) == 0
+    assert q4.q4_matmul_workspace_bytes(-1, 5120, 17408) == 0
+    # long rows at M <= 4: one fp32 partial sum per 64-block slice, output and row
+    for M in (1, 2, 3, 4):
+        slices = -(-(17408 // 32) // 64)
+        assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == slices * M * 5120 * 4
+    # activations over 64 KB of LDS (M = 4, K = 5120) are cut as well
+    assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 3 * 4 * 100 * 4
+
+
+def _mmx(L, ws_ptr, ws_bytes, x=A, M=4, N=32, K=17408):
+    P = ctypes.c_void_p
+    return L.q4_matmul_ex(P(x), P(A), P(A), P(A), 0, M, N, K, P(ws_ptr), ws_bytes, None)
+
+
+def test_matmul_ex_workspace_errors():
+    q4, L = _lib()
+    need = q4.q4_matmul_workspace_bytes(4, 32, 17408)
+    assert need > 0
+    assert _mmx(L, A, need - 1) == q4.Q4_ERR_WORKSPACE
+    assert _mmx(L, MIS, need) == q4.Q4_ERR_WORKSPACE
+    # tensor NULL / alignment checks come first
+    assert _mmx(L, A, 0, x=0) == q4.Q4_ERR_NULL
+    assert _mmx(L, A, 0, x=MIS) == q4.Q4_ERR_ALIGN
+    # zero-size is a no-op whatever the workspace
+    assert _mmx(L, 0, 0, M=0) == q4.Q4_OK
+
+
 @pytest.mark.skipif(_gpu_present(), reason="would launch on fake pointers")
 def test_matmul_without_gpu_is_device_error():
     q4, L = _lib()
     assert _mm(L) == q4.Q4_ERR_DEVICE
     assert _mm(L, M=64, dt=1) == q4.Q4_ERR_DEVICE
+    need = q4.q4_matmul_workspace_bytes(4, 32, 17408)
+    assert _mmx(L, A, need) == q4.Q4_ERR_DEVICE
+    assert _mmx(L, 0, 0) == q4.Q4_ERR_DEVICE
 
 
 def test_dequantize_argument_errors():

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import synthetic
-from gpu_util import dev, host, matmul, moe
+from gpu_util import dev, host, matmul, matmul_ex, moe
 from helpers import RTOL, assert_parity, bf16_half_ulp, load_golden
 
 pytestmark = pytest.mark.gpu
@@ -112,6 +112,41 @@ def test_tiny_gemv_config():
 def test_gemv_parity(M, N, K):
     d = synthetic.dense_case(1000 * M + N, M, N, K)
     _check_dense(d, F32, what=f"gemv M={M} N={N} K={K}")
+
+
+# Long rows cut into 64-block slices (q4_matmul_ex with a workspace): whole
+# slices, a last slice of 1, 32 (split between half-waves) or 50 (one block
+# per lane) blocks, and activations too large for one workgroup's LDS.
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,K", [(37, 8192 + 32), (300, 17408), (65, 5696), (17, 16384)])
+def test_gemv_split_parity(M, N, K):
+    d = synthetic.dense_case(5000 + 10 * M + N, M, N, K)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"split M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"split bf16 M={M} N={N} K={K}")
+    # without a workspace the same call takes the unsplit path
+    y0 = matmul_ex(d.x, d.w_q, d.w_s, F32, workspace=None)
+    assert_parity(y0, y_ref, t, RTOL, what=f"unsplit M={M} N={N} K={K}")
+
+
+def test_gemv_split_deterministic_and_workspace_reuse():
+    d = synthetic.dense_case(5100, 4, 300, 17408)
+    x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
+    need = q4.q4_matmul_workspace_bytes(4, 300, 17408)
+    work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)   # junk contents
+    y1 = q4.q4_matmul_ex(x, wq, ws, workspace=work)
+    y2 = q4.q4_matmul_ex(x, wq, ws, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    # a smaller problem in the same workspace
+    e = synthetic.dense_case(5101, 2, 50, 9216)
+    y3 = host(q4.q4_matmul_ex(dev(e.x), dev(e.w_q), dev(e.w_s), workspace=work))
+    y_ref, t = oracle.matmul(e.x, e.w_q, e.w_s)
+    assert_parity(y3, y_ref, t, RTOL, what="reused workspace")
+    with pytest.raises(q4.Q4Error):
+        q4.q4_matmul_ex(x, wq, ws, workspace=work[: need - 16])
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
@@ -234,6 +269,8 @@ def test_batched_down_full_size():
     d, y = _full_dense("batched_down", F32)
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     assert_parity(y, y_ref, t, RTOL, what="batched_down")
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)           # split into slices
+    assert_parity(y, y_ref, t, RTOL, what="batched_down with workspace")
 
 
 def test_prefill_full_size_sampled():
