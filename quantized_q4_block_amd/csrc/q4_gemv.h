@@ -212,17 +212,17 @@ __host__ __device__ __forceinline__ int64_t xlds_bytes(int64_t M, int64_t K) {
   return M * x_stages(K) * 8 * kWave * 16;
 }
 
-// Copies the M activation rows into that layout (whole workgroup of
-// THREADS threads, S stages per row), in two steps so that a kernel can
+// Copies the M activation rows into that layout (whole workgroup
+// of THREADS threads, S stages per row), in two steps so that a kernel can
 // issue the activation loads before its weight loads and convert them
 // while the weights are in flight: the memory counter waits for loads in
 // issue order, so data loaded first can be used without waiting for the
-// rest.
+// rest.  Each thread holds whole 8-element chunks.
 template <int M, int S, int THREADS>
 struct XStager {
-  static constexpr int kRowChunks = S * 8 * kWave;
+  static constexpr int kRowChunks = S * 4 * kWave;   // 8-element chunks per row
   static constexpr int kPer = (kRowChunks + THREADS - 1) / THREADS;
-  uint2 d[M][kPer];
+  uint4 d[M][kPer];
 
   // x: row 0 of the activations at the first element of the row piece; K:
   // length of the piece; ldx: distance between rows (elements).
@@ -232,26 +232,40 @@ struct XStager {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int c = i * THREADS + (int)threadIdx.x;
-        const int st = c >> 9, q = (c >> 6) & 7, l = c & 63;
-        const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 4;
+        const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
+        const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 8;
         const bool ok = (kRowChunks % THREADS == 0 || c < kRowChunks) && k < K;
         // unconditional load from a clamped address, masked afterwards with
         // a mask the compiler cannot trace back to `ok` (else it turns the
         // load into a branch, and every branch waits for earlier loads)
-        const uint2 v = *reinterpret_cast<const uint2*>(x + m * ldx + (ok ? k : 0));
+        const uint4 v = *reinterpret_cast<const uint4*>(x + m * ldx + (ok ? k : 0));
         const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
-        d[m][i] = make_uint2(v.x & keep, v.y & keep);
+        d[m][i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
       }
   }
-  __device__ __forceinline__ void store(float4* __restrict__ xs) const {
+  // Marks the loaded activations as used here, so that the compiler cannot
+  // sink a load into the conditional store of a thread's last chunk (that
+  // load would then be issued after, and wait for, the weight loads).
+  __device__ __forceinline__ void pin() const {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        asm volatile("" ::"v"(d[m][i].x), "v"(d[m][i].y), "v"(d[m][i].z), "v"(d[m][i].w));
+  }
+  __device__ __forceinline__ void store_f32(float4* __restrict__ xs) const {
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int c = i * THREADS + (int)threadIdx.x;
         if (kRowChunks % THREADS != 0 && c >= kRowChunks) break;
-        xs[m * kRowChunks + c] =
-            make_float4(bf16_lo(d[m][i].x), bf16_hi(d[m][i].x), bf16_lo(d[m][i].y), bf16_hi(d[m][i].y));
+        const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
+        float4* row = xs + m * (2 * kRowChunks) + st * 8 * kWave + l;
+        row[(2 * q) * kWave] = make_float4(bf16_lo(d[m][i].x), bf16_hi(d[m][i].x),
+                                           bf16_lo(d[m][i].y), bf16_hi(d[m][i].y));
+        row[(2 * q + 1) * kWave] = make_float4(bf16_lo(d[m][i].z), bf16_hi(d[m][i].z),
+                                               bf16_lo(d[m][i].w), bf16_hi(d[m][i].w));
       }
   }
 };
@@ -359,7 +373,10 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-  auto read_x = [&](int st, int l, float (&xv)[M][32]) {
+  // acc += block products of stage st for rows c/s, activations of lane l
+  auto rows = [&](int st, int l, const auto& c, const auto& s, auto& a) __attribute__((always_inline)) {
+    constexpr int RR = sizeof(c) / sizeof(c[0]);
+    float xv[M][32];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -370,24 +387,19 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
         xv[m][4 * q + 2] = v.z;
         xv[m][4 * q + 3] = v.w;
       }
+    block_rows_f32<M, RR>(unpack, c, s, xv, a);
   };
 #pragma unroll
-  for (int st = 0; st < FULL; ++st) {
-    float xv[M][32];
-    read_x(st, lane, xv);
-    block_rows_f32<M, R>(unpack, b.c[st], b.s[st], xv, acc);
-  }
+  for (int st = 0; st < FULL; ++st) rows(st, lane, b.c[st], b.s[st], acc);
   if constexpr (TAIL == kSplitTail) {
     constexpr int H = R / 2;
     const int sub = lane & 31, half = lane >> 5;
-    float xv[M][32];
-    read_x(FULL, sub, xv);
     float t[H][M];
 #pragma unroll
     for (int j = 0; j < H; ++j)
 #pragma unroll
       for (int m = 0; m < M; ++m) t[j][m] = 0.0f;
-    block_rows_f32<M, H>(unpack, b.ct, b.st, xv, t);
+    rows(FULL, sub, b.ct, b.st, t);
     // slot j of half h is row h*H + j; only lanes with a leftover block add
     const bool ok = sub < rem;
 #pragma unroll
@@ -401,13 +413,11 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
     // A lane past the leftover blocks reads zero activations (LDS holds 0
     // past K) and gets scale 0, so it adds exactly zero whatever its
     // (clamped, real) codes and scale are.
-    float xv[M][32];
-    read_x(FULL, lane, xv);
     const bool ok = lane < rem;
     _Float16 sc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (_Float16)0.0f;
-    block_rows_f32<M, R>(unpack, b.ct, sc, xv, acc);
+    rows(FULL, lane, b.ct, sc, acc);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

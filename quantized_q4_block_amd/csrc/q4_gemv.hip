@@ -52,11 +52,11 @@ __device__ __forceinline__ void store_rows(void* __restrict__ y, int y_bf16, int
 // The kernel works on a piece of each row: blocks blk0 .. blk0 + K/32 - 1
 // with blk0 = (slice0 + blockIdx.y) * slice_blocks, rows ld_blocks blocks
 // apart.  A whole-row call has one slice (blk0 = 0, ld_blocks = K/32) and
-// writes y; a split call (long rows) cuts the rows into one-stage slices
-// (FULL = 0, TAIL = kWideTail, rem < 0: each slice takes up to 64 blocks,
-// lanes past the row's end add zero) and writes the fp32 partial sums of
-// slice s to partial[s][M][N], which gemv_combine_kernel then adds in slice
-// order.
+// writes y; a split call (long rows, rem < 0) cuts the rows into slices of
+// slice_blocks blocks (the last one shorter) that are FULL whole stages
+// plus a partial one (TAIL = kWideTail; lanes past the slice's end add
+// zero) and writes the fp32 partial sums of slice s to partial[s][M][N],
+// which gemv_combine_kernel then adds in slice order.
 template <int M, int FULL, int TAIL>
 __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
@@ -73,10 +73,11 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
   const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
   const int slice = slice0 + (int)blockIdx.y;
   const int64_t blk0 = (int64_t)slice * slice_blocks;
-  if (rem < 0) {   // one-stage slices: this slice's blocks (the last may be short)
+  if (rem < 0) {   // slices of FULL whole stages plus a partial one
     const int64_t left = ld_blocks - blk0;
-    rem = (int)(left < kWave ? left : kWave);
-    K = (int64_t)rem * kBlock;
+    const int len = (int)(left < slice_blocks ? left : slice_blocks);
+    rem = len - FULL * kWave;
+    K = (int64_t)len * kBlock;
   }
   const uint32_t row_bytes = (uint32_t)(ld_blocks * 16), row_sc = (uint32_t)ld_blocks;
   // activation loads, then weight loads; the activations are converted
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
                               ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
                               lane);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
-  xst.store(xs);
+  xst.pin();
+  xst.store_f32(xs);
   __syncthreads();
   // a wavefront past the last row computes on clamped rows and stores
   // nothing (an early exit would let the compiler sink its loads past the
@@ -136,14 +138,38 @@ static hipError_t launch_lds(const uint16_t* x, const uint8_t* wq, const uint16_
   }
 }
 
-// Rows longer than the LDS kernel takes in one piece are cut into one-stage
-// slices (64 blocks, the last one shorter) when the caller gives a workspace
-// for the fp32 partial sums.
-int64_t gemv_split_slices(int64_t M, int64_t K) {
-  if (M < 1 || M > 4) return 0;
-  if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) return 0;
-  return x_stages(K);
+// Rows longer than the LDS kernel takes in one piece are cut into slices
+// when the caller gives a workspace for the fp32 partial sums.  For M <= 2:
+// as few slices of 65 .. 128 blocks (two stages, the second partial) as
+// cover the row, when the last one also gets more than 64 blocks.
+// Otherwise (and for M = 3, 4, whose two-stage tables would halve the
+// workgroups per CU) slices of up to 64 blocks (one stage).
+struct SplitPlan {
+  int64_t slices = 0;
+  int slice_blocks = 0;
+  int full = 0;          // whole stages per slice before the partial one
+};
+
+static SplitPlan split_plan(int64_t M, int64_t K) {
+  SplitPlan p;
+  if (M < 1 || M > 4) return p;
+  if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) return p;
+  const int64_t bpr = K / kBlock;
+  const int64_t ns = (bpr + 2 * kWave - 1) / (2 * kWave);
+  const int64_t sb = (bpr + ns - 1) / ns;
+  if (M <= 2 && sb > kWave && bpr - (ns - 1) * sb > kWave) {
+    p.slices = ns;
+    p.slice_blocks = (int)sb;
+    p.full = 1;
+  } else {
+    p.slices = (bpr + kWave - 1) / kWave;
+    p.slice_blocks = kWave;
+    p.full = 0;
+  }
+  return p;
 }
+
+int64_t gemv_split_slices(int64_t M, int64_t K) { return split_plan(M, K).slices; }
 
 // One task of R rows per wavefront, starting at row `row0`; activations
 // read from global memory.
@@ -179,9 +205,14 @@ static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t*
       });
     }
     if (partial) {
-      const int64_t slices = gemv_split_slices(M, K);
-      hipError_t e = launch_lds<M, 0, kWideTail>(x, wq, ws, y, yb, N, kWave * kBlock, -1, bpr, 0,
-                                                 (int)slices, kWave, partial, stream);
+      const SplitPlan sp = split_plan(M, K);
+      const int64_t slices = sp.slices;
+      hipError_t e =
+          sp.full == 1
+              ? launch_lds<M, 1, kWideTail>(x, wq, ws, y, yb, N, 0, -1, bpr, 0, (int)slices,
+                                            sp.slice_blocks, partial, stream)
+              : launch_lds<M, 0, kWideTail>(x, wq, ws, y, yb, N, 0, -1, bpr, 0, (int)slices,
+                                            sp.slice_blocks, partial, stream);
       if (e != hipSuccess) return e;
       const int64_t MN = (int64_t)M * N;
       int64_t grid = (MN + 255) / 256;

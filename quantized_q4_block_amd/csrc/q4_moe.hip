@@ -267,23 +267,26 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   const uint16_t* ws_e = ws + (int64_t)e * N * (K / kBlock);
   // the first token's activation loads go out before the weight loads
   XStager<1, S, kLdsWaves * 64> xst;
-  int32_t p = cnt > 0 ? order[start] : 0;
-  if (cnt > 0) xst.load(x + (int64_t)(p / topk) * K, K, K);
+  int32_t p = order[start];   // an active expert has at least one pair
+  xst.load(x + (int64_t)(p / topk) * K, K, K);
   const uint32_t row_bytes = (uint32_t)(K / 2), row_sc = (uint32_t)(K / kBlock);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq_e + nl * (int64_t)row_bytes, ws_e + nl * (int64_t)row_sc,
                               row_bytes, row_sc, room, rem, lane);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
+  xst.pin();
   for (int32_t i = 0; i < cnt; ++i) {
     if (i > 0) {
       p = order[start + i];
       xst.load(x + (int64_t)(p / topk) * K, K, K);
       __syncthreads();                             // xs no longer read
     }
-    xst.store(xs);
+    // fp32 activations: one compute path keeps the register count (and with
+    // it the occupancy) of this token loop low
+    xst.store_f32(xs);
     __syncthreads();
-    float out[R][1];
-    upfront_compute<1, R, FULL, TAIL>(b, xs, rem, lane, out);   // all waves (no load sinking)
+    float out[R][1];   // computed by all waves (no load sinking)
+    upfront_compute<1, R, FULL, TAIL>(b, xs, rem, lane, out);
     if (live) {
       if (lane == 0) {
 #pragma unroll

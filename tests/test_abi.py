@@ -135,12 +135,19 @@ def test_matmul_workspace_bytes():
     assert q4.q4_matmul_workspace_bytes(5, 5120, 17408) == 0
     assert q4.q4_matmul_workspace_bytes(4, 5120, 48) == 0
     assert q4.q4_matmul_workspace_bytes(-1, 5120, 17408) == 0
-    # long rows at M <= 4: one fp32 partial sum per 64-block slice, output and row
-    for M in (1, 2, 3, 4):
-        slices = -(-(17408 // 32) // 64)
+    # long rows at M <= 4: one fp32 partial sum per slice, output and row;
+    # 544 blocks make 5 two-stage slices of 108-109 blocks at M <= 2 and 9
+    # one-stage slices at M = 3, 4
+    for M, slices in ((1, 5), (2, 5), (3, 9), (4, 9)):
         assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == slices * M * 5120 * 4
-    # activations over 64 KB of LDS (M = 4, K = 5120) are cut as well
+    # activations over 64 KB of LDS as fp32 (M = 4, K = 5120: 160 blocks)
     assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 3 * 4 * 100 * 4
+    assert q4.q4_matmul_workspace_bytes(2, 100, 8192) == 0
+    # 257 blocks (K = 8224): 3 slices of 86 blocks
+    assert q4.q4_matmul_workspace_bytes(1, 7, 8224) == 3 * 1 * 7 * 4
+    # 8065 blocks: two-stage slices would leave a last slice of 64, so
+    # one-stage slices (127 of them)
+    assert q4.q4_matmul_workspace_bytes(2, 5, 258080) == 127 * 2 * 5 * 4
 
 
 def _mmx(L, ws_ptr, ws_bytes, x=A, M=4, N=32, K=17408):

@@ -114,11 +114,14 @@ def test_gemv_parity(M, N, K):
     _check_dense(d, F32, what=f"gemv M={M} N={N} K={K}")
 
 
-# Long rows cut into 64-block slices (q4_matmul_ex with a workspace): whole
-# slices, a last slice of 1, 32 (split between half-waves) or 50 (one block
-# per lane) blocks, and activations too large for one workgroup's LDS.
+# Long rows cut into slices (q4_matmul_ex with a workspace): at M <= 2
+# two-stage slices of 86 (K = 8224), 108/109 (17408) and 128 (16384)
+# blocks, at M = 3, 4 one-stage slices (the last of 1, 32 or 64 blocks);
+# K = 258080 (8065 blocks) takes one-stage slices at every M, and K = 5696
+# (178 blocks, 3 stages) is cut only at M = 4 (activations over 64 KB).
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-@pytest.mark.parametrize("N,K", [(37, 8192 + 32), (300, 17408), (65, 5696), (17, 16384)])
+@pytest.mark.parametrize("N,K", [(37, 8192 + 32), (300, 17408), (65, 5696), (17, 16384),
+                                 (5, 258080)])
 def test_gemv_split_parity(M, N, K):
     d = synthetic.dense_case(5000 + 10 * M + N, M, N, K)
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
