@@ -303,8 +303,13 @@ def test_moe_config_full():
     assert_parity(y, y_ref, t, RTOL, what="moe")
 
 
+# Up to 512 (token, slot) pairs the expert workgroups find their pairs
+# themselves; (80, 8, ...) has 640 pairs and goes through the prep kernel;
+# K = 8192 + 32 (more than 4 stages) takes the chunked global-activation
+# kernel.
 @pytest.mark.parametrize("T,topk,E,N,K", [(1, 1, 1, 33, 64), (5, 3, 4, 100, 256),
-                                          (64, 2, 4, 96, 512), (3, 4, 50, 70, 2048 + 32)])
+                                          (64, 2, 4, 96, 512), (3, 4, 50, 70, 2048 + 32),
+                                          (80, 8, 16, 40, 256), (4, 2, 6, 20, 8192 + 32)])
 def test_moe_parity_shapes(T, topk, E, N, K):
     m = synthetic.moe_case(6000 + T + E, T, topk, E, N, K)
     y = moe(m.x, m.w_q, m.w_s, m.ids, m.gates)
