@@ -9,6 +9,10 @@
 // the gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16) does the products with
 // fp32 accumulation.
 //
+// Two kernels with the same tiling: gemm_dma_kernel (K a multiple of 64)
+// loads the activation tile straight into LDS, gemm_kernel (any K) through
+// registers.
+//
 // Tile: 128 (activation rows) x 128 (weight rows) per workgroup of 4
 // wavefronts (2 x 2, each 64 x 64 = 2 x 2 MFMA 32x32 tiles), K step 64.
 // Each thread stages 32 activations (4 x 128-bit loads) and one 32-element
@@ -186,13 +190,152 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   }
 }
 
+// K a multiple of 64: the activation tile goes global -> LDS directly
+// (global_load_lds_dwordx4, no registers, no LDS store instructions) into a
+// double buffer, so the next tile streams in during the MFMAs; the
+// dequantised weights still pass through registers into one LDS buffer.
+// Unpadded 128-byte rows (64 bf16) with an XOR swizzle: 16-byte chunk c of
+// row r sits at chunk r*8 + (c ^ ((r >> 1) & 7)), which keeps the fragment
+// reads (32 rows at one k offset) free of bank conflicts and lets every
+// wavefront's load instruction fill 1 KB of consecutive LDS.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __restrict__ x,
+                                                const uint8_t* __restrict__ wq,
+                                                const uint16_t* __restrict__ ws,
+                                                void* __restrict__ y, int y_bf16,
+                                                int64_t M, int64_t N, int64_t K,
+                                                int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * 64];
+  const int total = tiles_m * tiles_n;
+  int c = blockIdx.x;
+  if (total % 8 == 0) c = (c % 8) * (total / 8) + c / 8;
+  const int tile_n = c / tiles_m, tile_m = c % tiles_m;
+  const int64_t m0 = (int64_t)tile_m * 128, n0 = (int64_t)tile_n * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t bpr = K / 32;
+  // activation tile: wavefront w issues 4 loads j; lane l fills physical
+  // chunk p = (w*4 + j)*64 + l, i.e. row p/8, logical chunk (p%8) ^ swizzle.
+  // Rows past M read row M-1 (their outputs are discarded).
+  const uint16_t* a_src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = (wave * 4 + j) * 64 + lane;
+    const int r = p >> 3, cl = (p & 7) ^ ((r >> 1) & 7);
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    a_src[j] = x + m * K + cl * 8;
+  }
+  auto dma = [&](int buf, int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(a_src[j] + k0),
+          (__attribute__((address_space(3))) void*)(&As[buf][(wave * 4 + j) * 64 * 8]), 16, 0, 0);
+  };
+  // weight staging: thread -> (row srow, half shalf): one 32-element block;
+  // rows past N get scale 0
+  const int srow = tid >> 1, shalf = tid & 1;
+  const int64_t bn = n0 + srow;
+  const bool b_ok = bn < N;
+  const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
+  const uint16_t* s_src = ws + (b_ok ? bn : 0) * bpr;
+  const CodeUnpacker unpack;
+  uint4 b_codes;
+  float b_scale;
+  auto load_b = [&](int64_t k0) __attribute__((always_inline)) {
+    const int64_t blk = k0 / 32 + shalf;
+    b_codes = *reinterpret_cast<const uint4*>(b_src + blk * 16);
+    b_scale = b_ok ? fp16_to_f32(s_src[blk]) : 0.0f;
+  };
+  auto store_b = [&]() __attribute__((always_inline)) {
+    const uint32_t dw[4] = {b_codes.x, b_codes.y, b_codes.z, b_codes.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2v p[4];
+      unpack(dw[i], p);
+      u32x4 o;
+      o[0] = pack_bf16x2(__builtin_fmaf((float)p[0][0], b_scale, 0.f), __builtin_fmaf((float)p[1][0], b_scale, 0.f));
+      o[1] = pack_bf16x2(__builtin_fmaf((float)p[2][0], b_scale, 0.f), __builtin_fmaf((float)p[3][0], b_scale, 0.f));
+      o[2] = pack_bf16x2(__builtin_fmaf((float)p[0][1], b_scale, 0.f), __builtin_fmaf((float)p[1][1], b_scale, 0.f));
+      o[3] = pack_bf16x2(__builtin_fmaf((float)p[2][1], b_scale, 0.f), __builtin_fmaf((float)p[3][1], b_scale, 0.f));
+      *reinterpret_cast<u32x4*>(&Bs[swz(srow, shalf * 4 + i) * 8]) = o;
+    }
+  };
+  f32x16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int64_t nk = K / 64;
+  dma(0, 0);
+  load_b(0);
+  store_b();
+  __builtin_amdgcn_s_waitcnt(0);   // the tile loads are not tied to registers
+  __syncthreads();
+  const int frow = lane & 31, fh = lane >> 5;
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt & 1);
+    const int64_t kn = (kt + 1 < nk ? kt + 1 : kt) * 64;
+    dma(cur ^ 1, kn);
+    load_b(kn);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8v af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + frow;
+        af[i] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const u32x4*>(&As[cur][swz(r, kk * 2 + fh) * 8]));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + frow;
+        bfr[j] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const u32x4*>(&Bs[swz(r, kk * 2 + fh) * 8]));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    store_b();
+    __builtin_amdgcn_s_waitcnt(0);   // next activation tile landed in LDS
+    __syncthreads();
+  }
+  const int col = lane & 31, rbase = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 32 + col;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v / 4) + rbase + (v % 4);
+        if (m < M) {
+          if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(acc[i][j][v]);
+          else static_cast<float*>(y)[m * N + n] = acc[i][j][v];
+        }
+      }
+    }
+}
+
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t tm = (M + BM - 1) / BM;
   const int64_t tn = (N + BN - 1) / BN;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-  gemm_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-      x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
+  if (K % BK == 0)
+    gemm_dma_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
+  else
+    gemm_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
   return hipGetLastError();
 }
 
