@@ -1,0 +1,77 @@
+"""CPU checks of bench.py's contract pieces: the multi-GPU refusal and the
+counter-to-traffic arithmetic (no GPU needed)."""
+from __future__ import annotations
+
+import csv
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_weight_bytes_formula():
+    b = _bench()
+    # decode_gate_up: 34816 rows of 5120 codes (2560 B) and 160 fp16 scales (320 B)
+    assert b.weight_bytes(34816, 5120) == 34816 * (2560 + 320) == 100270080
+
+
+def _write_counters(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "1_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_summarize_pmc_scales_by_the_copy(tmp_path):
+    b = _bench()
+    mib = 256
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    # the copy reads 256 MiB but FETCH_SIZE shows half; WRITE_SIZE shows all
+    _write_counters(fetch, [
+        {"Kernel_Name": "neg_kernel", "Counter_Name": "FETCH_SIZE", "Counter_Value": mib * 512},
+        {"Kernel_Name": "q4::gemv_lds_kernel<1,2,1>", "Counter_Name": "FETCH_SIZE",
+         "Counter_Value": 1000.0},
+        {"Kernel_Name": "q4::gemv_lds_kernel<1,2,1>", "Counter_Name": "FETCH_SIZE",
+         "Counter_Value": 1002.0},
+    ])
+    _write_counters(write, [
+        {"Kernel_Name": "neg_kernel", "Counter_Name": "WRITE_SIZE", "Counter_Value": mib * 1024},
+        {"Kernel_Name": "q4::gemv_lds_kernel<1,2,1>", "Counter_Name": "WRITE_SIZE",
+         "Counter_Value": 10.0},
+    ])
+    out = str(tmp_path / "rec.json")
+    b.summarize_pmc(fetch, write, mib, "t", "gemv_lds_kernel", 2_000_000, out)
+    rec = json.load(open(out))
+    assert rec["calibration"]["read_factor"] == 2.0
+    assert rec["calibration"]["write_factor"] == 1.0
+    assert rec["hbm_bytes_per_launch"] == round(1001.0 * 1024 * 2 + 10.0 * 1024)
+    assert rec["dispatches"] == {"FETCH_SIZE": 2, "WRITE_SIZE": 1}
+
+
+def test_traffic_record_is_ignored_for_other_sources(tmp_path, monkeypatch):
+    b = _bench()
+    d = tmp_path / "profiles"
+    d.mkdir()
+    (d / "k_pmc.json").write_text(json.dumps({"csrc_digest": "old", "hbm_bytes_per_launch": 5}))
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    assert b.traffic_from_profile("k", "new") is None
+    assert b.traffic_from_profile("k", "old") == 5
