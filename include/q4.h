@@ -25,10 +25,13 @@
  *   y    fp32 or bf16 [M][N]
  * K must be a positive multiple of 32.
  *
- * Numerics.  Products and sums are fp32.  Matrix-vector path (M <= 8):
- * every weight (c-8)*s enters exactly (no rounding before the product).
- * Matrix-core path (M > 8): every weight is rounded to bf16 (nearest-even)
- * and the bf16 matrix cores accumulate in fp32.  bf16 outputs are rounded
+ * Numerics.  Products and sums are fp32.  The matrix-vector path and the
+ * few-row matrix-core path (Q4_PATH_GEMV, Q4_PATH_SMALL) use every weight
+ * (c-8)*s exactly: each 32-element block's sum of x * (c - 8) is formed
+ * first (exact products) and its scale applied once in fp32.  The tiled
+ * matrix-core path (Q4_PATH_MFMA) rounds every weight to bf16
+ * (nearest-even) and the bf16 matrix cores accumulate in fp32.
+ * q4_matmul_path tells which path a shape takes.  bf16 outputs are rounded
  * nearest-even from the fp32 result.  Results are bit-identical from run to
  * run (no floating-point atomics).
  *
@@ -66,7 +69,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 2
+#define Q4_ABI_VERSION 3
 
 /* Status codes. */
 #define Q4_OK            0
@@ -83,8 +86,10 @@ extern "C" {
 #define Q4_BF16 1
 
 /* Paths chosen by q4_matmul. */
-#define Q4_PATH_GEMV 0      /* M <= 8: fused dequant + matrix-vector, exact weights */
-#define Q4_PATH_MFMA 1      /* M > 8: dequant to bf16 in LDS + bf16 matrix cores */
+#define Q4_PATH_GEMV  0     /* fused dequant + matrix-vector, exact weights */
+#define Q4_PATH_MFMA  1     /* dequant to bf16 in LDS + bf16 matrix-core tiles */
+#define Q4_PATH_SMALL 2     /* exact (c - 8) on bf16 matrix cores, fp32 block
+                               scales: exact weights */
 
 typedef void *q4_stream_t;  /* a hipStream_t */
 
@@ -96,9 +101,14 @@ Q4_API int32_t q4_abi_version(void);
  * (unknown codes map to "unknown status"). */
 Q4_API const char *q4_status_str(int32_t status);
 
-/* Path q4_matmul takes for M rows (Q4_PATH_GEMV or Q4_PATH_MFMA); -1 if
- * M < 0.  Host-only: enqueues nothing. */
-Q4_API int32_t q4_matmul_path(int64_t M);
+/* Path q4_matmul takes for an [M][K] x [N][K] product; -1 for sizes
+ * q4_matmul would reject (M or N negative, K not a positive multiple of 32).
+ *   M <= 2                                         Q4_PATH_GEMV
+ *   3 <= M <= 32                                   Q4_PATH_SMALL
+ *   M <= 128 and ceil(M/128) * ceil(N/128) < 256   Q4_PATH_SMALL
+ *   otherwise                                      Q4_PATH_MFMA
+ * Host-only: enqueues nothing. */
+Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K);
 
 /* y = x * dequant(W)^T.
  *   x       bf16  [M][K]    device
@@ -114,8 +124,8 @@ Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
                          int64_t M, int64_t N, int64_t K, q4_stream_t stream);
 
 /* Device workspace (bytes) that lets q4_matmul_ex cut long rows into
- * slices (currently M <= 4 with K above 8192 or activations too large for
- * one workgroup's LDS): slices * M * N fp32 partial sums.  0 when the call
+ * slices (Q4_PATH_GEMV shapes with K above 8192 or activations too large
+ * for one workgroup's LDS): slices * M * N fp32 partial sums.  0 when the call
  * needs none, or for sizes q4_matmul would reject. */
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

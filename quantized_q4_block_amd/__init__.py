@@ -8,7 +8,7 @@ of the C ABI in ``include/q4.h``:
 
     q4_abi_version()                        -> int
     q4_status_str(status)                   -> str
-    q4_matmul_path(M)                       -> Q4_PATH_GEMV | Q4_PATH_MFMA
+    q4_matmul_path(M, N, K)                 -> Q4_PATH_GEMV | Q4_PATH_SMALL | Q4_PATH_MFMA
     q4_matmul(x, w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> y
     q4_matmul_workspace_bytes(M, N, K)      -> int
     q4_matmul_ex(x, w_q, w_s, out=None, out_dtype=torch.float32, workspace="auto",
@@ -33,7 +33,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 2
+Q4_ABI_VERSION = 3
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -46,6 +46,7 @@ Q4_F32 = 0
 Q4_BF16 = 1
 Q4_PATH_GEMV = 0
 Q4_PATH_MFMA = 1
+Q4_PATH_SMALL = 2
 
 __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
@@ -71,7 +72,7 @@ def _open():
     L.q4_abi_version.restype = I32
     L.q4_status_str.argtypes = [I32]
     L.q4_status_str.restype = ctypes.c_char_p
-    L.q4_matmul_path.argtypes = [I64]
+    L.q4_matmul_path.argtypes = [I64, I64, I64]
     L.q4_matmul_path.restype = I32
     L.q4_matmul.argtypes = [P, P, P, P, I32, I64, I64, I64, P]
     L.q4_matmul.restype = I32
@@ -101,8 +102,8 @@ def q4_status_str(status: int) -> str:
     return lib.q4_status_str(int(status)).decode()
 
 
-def q4_matmul_path(M: int) -> int:
-    return int(lib.q4_matmul_path(int(M)))
+def q4_matmul_path(M: int, N: int, K: int) -> int:
+    return int(lib.q4_matmul_path(int(M), int(N), int(K)))
 
 
 # ---------------------------------------------------------------- tensors

@@ -15,7 +15,18 @@
 
 namespace {
 
-constexpr int64_t kGemvMaxRows = 8;   // M <= 8 takes the matrix-vector path
+// Path choice (measured on MI355X; see q4_matmul_path in q4.h):
+//  * M <= 2: the matrix-vector kernel streams W at close to HBM rate;
+//  * 3 <= M <= 32: the exact-weight matrix-core kernel (the vector kernel is
+//    bound by one fma per weight per row from 3 rows on);
+//  * M <= 128 while the tiled kernel would have fewer 128 x 128 tiles than
+//    the chip has compute units: still the exact-weight kernel, in slabs of
+//    32 rows (the tiled kernel would leave most of the chip idle);
+//  * otherwise the tiled bf16 kernel.
+constexpr int64_t kGemvMaxRows = 2;
+constexpr int64_t kSmallMaxRows = 32;
+constexpr int64_t kSmallSlabMaxRows = 128;
+constexpr int64_t kTiledMinTiles = 256;
 constexpr int kMaxDevices = 64;
 
 // 0 = unknown, 1 = gfx950, 2 = other.
@@ -83,14 +94,18 @@ Q4_API const char* q4_status_str(int32_t status) {
   }
 }
 
-Q4_API int32_t q4_matmul_path(int64_t M) {
-  if (M < 0) return -1;
-  return M <= kGemvMaxRows ? Q4_PATH_GEMV : Q4_PATH_MFMA;
+Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return -1;
+  if (M <= kGemvMaxRows) return Q4_PATH_GEMV;
+  if (M <= kSmallMaxRows) return Q4_PATH_SMALL;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (M <= kSmallSlabMaxRows && tiles < kTiledMinTiles) return Q4_PATH_SMALL;
+  return Q4_PATH_MFMA;
 }
 
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 0;
-  if (q4_matmul_path(M) != Q4_PATH_GEMV) return 0;
+  if (q4_matmul_path(M, N, K) != Q4_PATH_GEMV) return 0;
   const int64_t slices = q4::gemv_split_slices(M, K);
   int64_t mn, total;
   if (slices == 0 || !mul_ok(M, N, &mn) || !mul_ok(mn, slices * 4, &total)) return 0;
@@ -120,9 +135,11 @@ Q4_API int32_t q4_matmul_ex(const void* x, const void* w_q, const void* w_s, voi
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint8_t*>(w_q);
   const auto* sp = static_cast<const uint16_t*>(w_s);
-  if (q4_matmul_path(M) == Q4_PATH_GEMV)
-    return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, partial, st));
-  return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, st));
+  switch (q4_matmul_path(M, N, K)) {
+    case Q4_PATH_GEMV: return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, partial, st));
+    case Q4_PATH_SMALL: return launched(q4::launch_small(xp, wp, sp, y, bf16, M, N, K, st));
+    default: return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, st));
+  }
 }
 
 Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* y,

@@ -10,7 +10,8 @@ namespace q4 {
 hipError_t launch_dequant(const uint8_t* wq, const uint16_t* ws, void* out, bool bf16,
                           int64_t N, int64_t K, hipStream_t stream);
 
-// M <= 8 rows: fused dequant + matrix-vector product, exact weights.
+// Few rows (the library uses it for M <= 2): fused dequant + matrix-vector
+// product, exact weights.
 // partial: NULL, or fp32 scratch of gemv_split_slices(M, K) * M * N floats
 // that lets long rows be cut into slices.
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
@@ -21,7 +22,12 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
 // given (0: never cut).
 int64_t gemv_split_slices(int64_t M, int64_t K);
 
-// M > 8 rows: dequant to bf16 in LDS + bf16 MFMA.
+// Few rows (3 <= M, at most 65535 slabs of 32): exact (c - 8) on the bf16
+// matrix cores, block scales applied in fp32; exact weights.
+hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Many rows: dequant to bf16 in LDS + bf16 MFMA tiles (weights rounded to bf16).
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 

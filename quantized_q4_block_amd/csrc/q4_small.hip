@@ -1,0 +1,243 @@
+// q4_small.hip -- few activation rows (3 <= M <= 32, or up to 128 when the
+// tiled path would have too few tiles): exact-weight matrix-core kernel.
+//
+// The quantised GEMM of the T0 kernel tier ("spec: specialized model
+// runtimes", sections "Architecture" and "Feasibility gate") between the
+// decode and the prefill shapes.  The matrix-vector kernel spends one fma per
+// weight per activation row, so from about 3 rows on it is bound by vector
+// ALU issue; the tiled bf16 kernel rounds the weights to bf16 and needs
+// hundreds of 128 x 128 tiles to fill the chip.  This kernel keeps the
+// weights exact and puts the products on the matrix cores:
+//
+//  * (c - 8) is a small integer, exact in bf16, so each 32-element block's
+//    partial sum sum_k x[m][k] * (c[n][k] - 8) is one
+//    v_mfma_f32_16x16x32_bf16 (16 activation rows x 16 weight rows x the
+//    block's 32 k): products exact, fp32 sums;
+//  * the block's fp16 scale is applied to that 16 x 16 partial in fp32 (one
+//    fma per output per block), which is the groupwise definition
+//    y = sum_blocks s * sum_k x * (c - 8) and needs no rounding of weights.
+//    A block of all-8 codes contributes exactly zero.
+//
+// Operand layout (wave64, lane = 16 * g + r):
+//  * A (activations): lane holds x[m = r][32 b + 8 g .. + 7] (16 bytes);
+//  * B (weights):     lane holds the 8 codes k = 32 b + 8 g .. + 7 of weight
+//                     row n = r, i.e. dword g of block b;
+//  * D:               lane holds rows m = 4 g .. 4 g + 3 of column n = r, so
+//                     a lane needs the one scale s[n][b].
+// Codes are read as 16 bytes per lane -- lane (r, g) takes block b0 + g of
+// row r, so the 4 lane groups read 64 consecutive bytes of each row -- and a
+// 4 x 4 transpose across the lane groups (v_permlane16_swap and
+// v_permlane32_swap) then gives lane (r, g) dword g of blocks b0 .. b0 + 3.
+//
+// Work split: a workgroup of kWaves wavefronts owns kNg * 16 weight rows and
+// one slab of 16 * MG activation rows; its wavefronts take consecutive
+// stretches of the row's 4-block groups, each keeping two groups of loads in
+// flight, and their partial sums are added in wavefront order through LDS
+// (deterministic).
+#include "q4_device.h"
+#include "q4_launch.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kNg = 2;      // 16-row weight groups per workgroup
+constexpr int kWaves = 4;   // wavefronts per workgroup (split of K)
+constexpr int kDepth = 2;   // 4-block groups in flight per wavefront
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 (c - 8) of the 8 codes of d, in k order (exact: small integers).
+__device__ __forceinline__ bf16x8v codes_to_bf16(uint32_t d, const CodeUnpacker& unpack) {
+  half2v p[4];
+  unpack(d, p);
+  u32x4 o;
+  o[0] = pack_bf16x2((float)p[0][0], (float)p[1][0]);
+  o[1] = pack_bf16x2((float)p[2][0], (float)p[3][0]);
+  o[2] = pack_bf16x2((float)p[0][1], (float)p[1][1]);
+  o[3] = pack_bf16x2((float)p[2][1], (float)p[3][1]);
+  return __builtin_bit_cast(bf16x8v, o);
+}
+
+// Before: register j of lane group g (16 lanes) holds E[g][j].
+// After:  register j of lane group g holds E[j][g].
+__device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
+  const auto a = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(r[2], r[3], false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+  r[0] = c[0];
+  r[2] = c[1];
+  r[1] = d[0];
+  r[3] = d[1];
+}
+
+// SCALE4: K/32 is a multiple of 4, so a row's 4 scales of a group are one
+// aligned 8-byte load.
+template <int MG, bool SCALE4>
+__global__ __launch_bounds__(kWaves * 64) void small_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint16_t* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
+    int64_t K, int64_t groups_per_wave) {
+  __shared__ f32x4v red[kWaves][kNg][MG][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t bpr = K / 32;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * kNg);
+  const int64_t m0 = (int64_t)blockIdx.y * (16 * MG);
+  // Rows past N (M) read row N-1 (M-1); their outputs are not stored.
+  const uint8_t* wrow[kNg];
+  const uint16_t* srow[kNg];
+#pragma unroll
+  for (int ng = 0; ng < kNg; ++ng) {
+    const int64_t n = n0 + ng * 16 + r;
+    const int64_t nn = n < N ? n : N - 1;
+    wrow[ng] = wq + nn * (K / 2);
+    srow[ng] = ws + nn * bpr;
+  }
+  const uint16_t* xrow[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) {
+    const int64_t m = m0 + mg * 16 + r;
+    xrow[mg] = x + (m < M ? m : M - 1) * K + 8 * g;
+  }
+  const CodeUnpacker unpack;
+  const f32x4v zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4v acc[kNg][MG];
+#pragma unroll
+  for (int ng = 0; ng < kNg; ++ng)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) acc[ng][mg] = zero;
+
+  // Ring of kDepth groups.  Slot loads are unconditional: a group index past
+  // the row's end reads the row's last group again (never out of bounds) and
+  // is skipped when computed.
+  uint32_t codes[kDepth][kNg][4];
+  float scale[kDepth][kNg][4];
+  bf16x8v xf[kDepth][4][MG];
+  auto load = [&](int64_t q, auto slot) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+    int64_t b0 = q * 4;
+    if (b0 >= bpr) b0 = (bpr - 1) & ~int64_t(3);
+    const int64_t bl = b0 + g < bpr ? b0 + g : bpr - 1;
+#pragma unroll
+    for (int ng = 0; ng < kNg; ++ng) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wrow[ng] + bl * 16);
+      codes[d][ng][0] = v[0];
+      codes[d][ng][1] = v[1];
+      codes[d][ng][2] = v[2];
+      codes[d][ng][3] = v[3];
+      if constexpr (SCALE4) {
+        const u32x2 s = *reinterpret_cast<const u32x2*>(srow[ng] + b0);
+        scale[d][ng][0] = fp16_to_f32((uint16_t)(s[0] & 0xFFFFu));
+        scale[d][ng][1] = fp16_to_f32((uint16_t)(s[0] >> 16));
+        scale[d][ng][2] = fp16_to_f32((uint16_t)(s[1] & 0xFFFFu));
+        scale[d][ng][3] = fp16_to_f32((uint16_t)(s[1] >> 16));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          scale[d][ng][j] = fp16_to_f32(srow[ng][b0 + j < bpr ? b0 + j : bpr - 1]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t bj = b0 + j < bpr ? b0 + j : bpr - 1;
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg)
+        xf[d][j][mg] = *reinterpret_cast<const bf16x8v*>(xrow[mg] + bj * 32);
+    }
+  };
+  auto block = [&](int j, auto slot) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+#pragma unroll
+    for (int ng = 0; ng < kNg; ++ng) {
+      const bf16x8v w = codes_to_bf16(codes[d][ng][j], unpack);
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) {
+        const f32x4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[d][j][mg], w, zero, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[ng][mg][e] = __builtin_fmaf(scale[d][ng][j], p[e], acc[ng][mg][e]);
+      }
+    }
+  };
+  auto compute = [&](int64_t q, auto slot) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+#pragma unroll
+    for (int ng = 0; ng < kNg; ++ng) transpose_groups(codes[d][ng]);
+    const int64_t left = bpr - q * 4;   // blocks of this group inside the row
+    if (left >= 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) block(j, slot);
+    } else if (left > 0) {
+      block(0, slot);
+      if (left > 1) block(1, slot);
+      if (left > 2) block(2, slot);
+    }
+  };
+  static_assert(kDepth == 2, "the ring below is written for two slots");
+  const std::integral_constant<int, 0> s0;
+  const std::integral_constant<int, 1> s1;
+  const int64_t q0 = (int64_t)wave * groups_per_wave;
+  load(q0, s0);
+  load(q0 + 1, s1);
+  for (int64_t i = 0; i < groups_per_wave; i += kDepth) {
+    const int64_t q = q0 + i;
+    compute(q, s0);
+    load(q + kDepth, s0);
+    compute(q + 1, s1);
+    load(q + 1 + kDepth, s1);
+  }
+
+#pragma unroll
+  for (int ng = 0; ng < kNg; ++ng)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) red[wave][ng][mg][lane] = acc[ng][mg];
+  __syncthreads();
+  // Output (m, n) of the workgroup, n fastest: lane 16 * (m / 4) + n of each
+  // wavefront's tile holds it in element m % 4.
+  constexpr int kOut = kNg * 16 * MG * 16;
+  for (int o = threadIdx.x; o < kOut; o += kWaves * 64) {
+    const int nl = o % (kNg * 16), ml = o / (kNg * 16);
+    const int ng = nl / 16, mg = ml / 16, mi = ml % 16;
+    const int src = (mi / 4) * 16 + nl % 16;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[w][ng][mg][src][mi % 4];
+    const int64_t m = m0 + ml, n = n0 + nl;
+    if (m < M && n < N) {
+      if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(s);
+      else static_cast<float*>(y)[m * N + n] = s;
+    }
+  }
+}
+
+template <int MG>
+hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                     bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t bpr = K / 32, groups = (bpr + 3) / 4;
+  int64_t gpw = (groups + kWaves - 1) / kWaves;
+  gpw = (gpw + kDepth - 1) / kDepth * kDepth;
+  const int64_t gx = (N + 16 * kNg - 1) / (16 * kNg), gy = (M + 16 * MG - 1) / (16 * MG);
+  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)gy);
+  if (bpr % 4 == 0)
+    small_kernel<MG, true><<<grid, dim3(kWaves * 64), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0,
+                                                                    M, N, K, gpw);
+  else
+    small_kernel<MG, false><<<grid, dim3(kWaves * 64), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0,
+                                                                     M, N, K, gpw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M <= 16) return launch_mg<1>(x, wq, ws, y, y_bf16, M, N, K, stream);
+  return launch_mg<2>(x, wq, ws, y, y_bf16, M, N, K, stream);
+}
+
+}  // namespace q4

@@ -68,7 +68,7 @@ def test_constants_match_header():
     d = _defines()
     for name in ("Q4_ABI_VERSION", "Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN",
                  "Q4_ERR_DTYPE", "Q4_ERR_WORKSPACE", "Q4_ERR_DEVICE", "Q4_ERR_LAUNCH",
-                 "Q4_F32", "Q4_BF16", "Q4_PATH_GEMV", "Q4_PATH_MFMA"):
+                 "Q4_F32", "Q4_BF16", "Q4_PATH_GEMV", "Q4_PATH_MFMA", "Q4_PATH_SMALL"):
         assert getattr(q4, name) == d[name], name
     assert L.q4_abi_version() == d["Q4_ABI_VERSION"]
 
@@ -87,11 +87,22 @@ def test_status_strings():
 
 def test_path_dispatch():
     q4, _ = _lib()
-    for M in range(0, 9):
-        assert q4.q4_matmul_path(M) == q4.Q4_PATH_GEMV
-    for M in (9, 16, 127, 128, 512, 1 << 20):
-        assert q4.q4_matmul_path(M) == q4.Q4_PATH_MFMA
-    assert q4.q4_matmul_path(-1) == -1
+    for N, K in ((34816, 5120), (5120, 17408), (7, 32)):
+        for M in range(0, 3):
+            assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_GEMV
+        for M in (3, 4, 8, 9, 16, 17, 32):
+            assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_SMALL
+    # past 32 rows: tiles of 128 x 128 decide (fewer than 256 -> small path,
+    # up to 128 rows)
+    assert q4.q4_matmul_path(33, 34816, 5120) == q4.Q4_PATH_MFMA      # 272 tiles
+    assert q4.q4_matmul_path(128, 32640, 5120) == q4.Q4_PATH_SMALL    # 255 tiles
+    assert q4.q4_matmul_path(128, 32641, 5120) == q4.Q4_PATH_MFMA     # 256 tiles
+    assert q4.q4_matmul_path(64, 5120, 17408) == q4.Q4_PATH_SMALL
+    assert q4.q4_matmul_path(129, 5120, 17408) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path(512, 34816, 5120) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path(1 << 20, 64, 64) == q4.Q4_PATH_MFMA
+    for bad in ((-1, 8, 32), (4, -1, 32), (4, 8, 0), (4, 8, 48)):
+        assert q4.q4_matmul_path(*bad) == -1
 
 
 A = 1 << 20          # a 16-byte aligned fake address
@@ -129,19 +140,19 @@ def test_matmul_argument_errors():
 
 def test_matmul_workspace_bytes():
     q4, _ = _lib()
-    # rows that fit one workgroup's LDS, the matrix-core path and bad shapes need none
+    # rows that fit one workgroup's LDS, the matrix-core paths and bad
+    # shapes need none
     assert q4.q4_matmul_workspace_bytes(1, 34816, 5120) == 0
     assert q4.q4_matmul_workspace_bytes(512, 34816, 5120) == 0
-    assert q4.q4_matmul_workspace_bytes(5, 5120, 17408) == 0
-    assert q4.q4_matmul_workspace_bytes(4, 5120, 48) == 0
+    for M in (3, 4, 5, 32):
+        assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == 0
+    assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 0
+    assert q4.q4_matmul_workspace_bytes(2, 5120, 48) == 0
     assert q4.q4_matmul_workspace_bytes(-1, 5120, 17408) == 0
-    # long rows at M <= 4: one fp32 partial sum per slice, output and row;
-    # 544 blocks make 5 two-stage slices of 108-109 blocks at M <= 2 and 9
-    # one-stage slices at M = 3, 4
-    for M, slices in ((1, 5), (2, 5), (3, 9), (4, 9)):
+    # long rows on the matrix-vector path: one fp32 partial sum per slice,
+    # output and row; 544 blocks make 5 two-stage slices of 108-109 blocks
+    for M, slices in ((1, 5), (2, 5)):
         assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == slices * M * 5120 * 4
-    # activations over 64 KB of LDS as fp32 (M = 4, K = 5120: 160 blocks)
-    assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 3 * 4 * 100 * 4
     assert q4.q4_matmul_workspace_bytes(2, 100, 8192) == 0
     # 257 blocks (K = 8224): 3 slices of 86 blocks
     assert q4.q4_matmul_workspace_bytes(1, 7, 8224) == 3 * 1 * 7 * 4
@@ -150,14 +161,14 @@ def test_matmul_workspace_bytes():
     assert q4.q4_matmul_workspace_bytes(2, 5, 258080) == 127 * 2 * 5 * 4
 
 
-def _mmx(L, ws_ptr, ws_bytes, x=A, M=4, N=32, K=17408):
+def _mmx(L, ws_ptr, ws_bytes, x=A, M=2, N=32, K=17408):
     P = ctypes.c_void_p
     return L.q4_matmul_ex(P(x), P(A), P(A), P(A), 0, M, N, K, P(ws_ptr), ws_bytes, None)
 
 
 def test_matmul_ex_workspace_errors():
     q4, L = _lib()
-    need = q4.q4_matmul_workspace_bytes(4, 32, 17408)
+    need = q4.q4_matmul_workspace_bytes(2, 32, 17408)
     assert need > 0
     assert _mmx(L, A, need - 1) == q4.Q4_ERR_WORKSPACE
     assert _mmx(L, MIS, need) == q4.Q4_ERR_WORKSPACE
@@ -173,7 +184,7 @@ def test_matmul_without_gpu_is_device_error():
     q4, L = _lib()
     assert _mm(L) == q4.Q4_ERR_DEVICE
     assert _mm(L, M=64, dt=1) == q4.Q4_ERR_DEVICE
-    need = q4.q4_matmul_workspace_bytes(4, 32, 17408)
+    need = q4.q4_matmul_workspace_bytes(2, 32, 17408)
     assert _mmx(L, A, need) == q4.Q4_ERR_DEVICE
     assert _mmx(L, 0, 0) == q4.Q4_ERR_DEVICE
 

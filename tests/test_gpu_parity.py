@@ -31,9 +31,11 @@ F32, BF16 = torch.float32, torch.bfloat16
 
 
 def _check_dense(d, out_dtype=F32, what=""):
-    M = d.x.shape[0]
+    M, K = d.x.shape
+    N = d.w_q.shape[0]
     y = matmul(d.x, d.w_q, d.w_s, out_dtype)
-    mfma = q4.q4_matmul_path(M) == q4.Q4_PATH_MFMA
+    # only the tiled path rounds weights to bf16
+    mfma = q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=mfma)
     extra = bf16_half_ulp(y_ref) if out_dtype == BF16 else 0.0
     assert_parity(y, y_ref, t, RTOL, extra, what=what)
@@ -114,11 +116,11 @@ def test_gemv_parity(M, N, K):
     _check_dense(d, F32, what=f"gemv M={M} N={N} K={K}")
 
 
-# Long rows cut into slices (q4_matmul_ex with a workspace): at M <= 2
-# two-stage slices of 86 (K = 8224), 108/109 (17408) and 128 (16384)
-# blocks, at M = 3, 4 one-stage slices (the last of 1, 32 or 64 blocks);
-# K = 258080 (8065 blocks) takes one-stage slices at every M, and K = 5696
-# (178 blocks, 3 stages) is cut only at M = 4 (activations over 64 KB).
+# Long rows cut into slices (q4_matmul_ex with a workspace, matrix-vector
+# path): two-stage slices of 86 (K = 8224), 108/109 (17408) and 128 (16384)
+# blocks; K = 258080 (8065 blocks) takes one-stage slices; K = 5696 (178
+# blocks, 3 stages) fits one workgroup and is not cut.  At M = 3, 4 the call
+# takes the few-row matrix-core path, which needs no workspace.
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("N,K", [(37, 8192 + 32), (300, 17408), (65, 5696), (17, 16384),
                                  (5, 258080)])
@@ -135,16 +137,17 @@ def test_gemv_split_parity(M, N, K):
 
 
 def test_gemv_split_deterministic_and_workspace_reuse():
-    d = synthetic.dense_case(5100, 4, 300, 17408)
+    d = synthetic.dense_case(5100, 2, 300, 17408)
     x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
-    need = q4.q4_matmul_workspace_bytes(4, 300, 17408)
+    need = q4.q4_matmul_workspace_bytes(2, 300, 17408)
+    assert need > 0
     work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)   # junk contents
     y1 = q4.q4_matmul_ex(x, wq, ws, workspace=work)
     y2 = q4.q4_matmul_ex(x, wq, ws, workspace=work)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     # a smaller problem in the same workspace
-    e = synthetic.dense_case(5101, 2, 50, 9216)
+    e = synthetic.dense_case(5101, 1, 50, 9216)
     y3 = host(q4.q4_matmul_ex(dev(e.x), dev(e.w_q), dev(e.w_s), workspace=work))
     y_ref, t = oracle.matmul(e.x, e.w_q, e.w_s)
     assert_parity(y3, y_ref, t, RTOL, what="reused workspace")
@@ -158,17 +161,61 @@ def test_gemv_bf16_output(M):
     _check_dense(d, BF16, what=f"gemv bf16 M={M}")
 
 
+# ------------------------------------- few rows (exact-weight matrix cores)
+
+
+# 16-row weight groups with a ragged last one (N = 1, 37, 65, 300), rows of
+# 1 block, of 7 and 257 blocks (not a whole number of 4-block groups), of 129
+# blocks and of 544 blocks (several groups per wavefront); M covers one and
+# two 16-row activation groups with ragged ends.
+@pytest.mark.parametrize("M", [3, 5, 16, 17, 32])
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 224), (65, 8224), (300, 4096 + 32), (64, 17408)])
+def test_small_parity(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_SMALL
+    d = synthetic.dense_case(6000 + 10 * M + N, M, N, K)
+    _check_dense(d, F32, what=f"small M={M} N={N} K={K}")
+
+
+# Past 32 rows while the tiled path would have fewer tiles than compute
+# units: slabs of 32 activation rows (the last one ragged).
+@pytest.mark.parametrize("M", [33, 64, 100, 128])
+@pytest.mark.parametrize("N,K", [(300, 640), (31, 2048 + 32)])
+def test_small_slab_parity(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_SMALL
+    d = synthetic.dense_case(6500 + M + N, M, N, K)
+    _check_dense(d, F32, what=f"small slabs M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [4, 24])
+def test_small_bf16_output(M):
+    d = synthetic.dense_case(6800 + M, M, 257, 1024)
+    _check_dense(d, BF16, what=f"small bf16 M={M}")
+
+
+def test_small_ignores_a_workspace():
+    d = synthetic.dense_case(6900, 4, 300, 17408)
+    assert q4.q4_matmul_workspace_bytes(4, 300, 17408) == 0
+    work = torch.full((4096,), 0x7F, dtype=torch.uint8, device="cuda:0")
+    y = host(q4.q4_matmul_ex(dev(d.x), dev(d.w_q), dev(d.w_s), workspace=work))
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    assert_parity(y, y_ref, t, RTOL, what="small with workspace")
+
+
 # ---------------------------------------------------- prefill (MFMA)
 
 
-@pytest.mark.parametrize("M,N,K", [(9, 1, 32), (17, 100, 96), (127, 128, 64), (128, 129, 640),
-                                   (129, 257, 1024), (256, 384, 2048 + 32), (300, 77, 160)])
+# Tiled path: more than 128 rows, or 33..128 rows with at least 256 tiles
+# (N >= 32641); ragged tiles in M, N and K steps of 64.
+@pytest.mark.parametrize("M,N,K", [(33, 34816, 64), (100, 32641 + 30, 96), (128, 34816, 32),
+                                   (129, 257, 1024), (256, 384, 2048 + 32), (300, 77, 160),
+                                   (129, 1, 32)])
 def test_mfma_parity(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
     d = synthetic.dense_case(3000 + M + N, M, N, K)
     _check_dense(d, F32, what=f"mfma M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 200, 512), (512, 256, 5120)])
+@pytest.mark.parametrize("M,N,K", [(160, 200, 512), (512, 256, 5120)])
 def test_mfma_bf16_output(M, N, K):
     d = synthetic.dense_case(4000 + M, M, N, K)
     _check_dense(d, BF16, what=f"mfma bf16 M={M}")
@@ -178,8 +225,9 @@ def test_mfma_bf16_output(M, N, K):
 
 
 def test_identity_activations_give_dequantised_weights():
-    """x = I (K x K): y[m][n] = w[n][m]; exact fp32 weights on the GEMV
-    path (row slices), bf16-rounded weights on the matrix-core path."""
+    """x = I (K x K): y[m][n] = w[n][m]; bf16-rounded weights on the tiled
+    matrix-core path, exact fp32 weights on the few-row matrix-core path and
+    the matrix-vector path (row slices)."""
     K, N = 256, 192
     d = synthetic.dense_case(5000, 1, N, K)
     eye = np.zeros((K, K), dtype=np.uint16)
@@ -189,9 +237,12 @@ def test_identity_activations_give_dequantised_weights():
     wbf = (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.array_equal(y, wbf.T)
     wf = oracle.dequant_f32(d.w_q, d.w_s).astype(np.float64)
-    for m0 in range(0, K, 8):                           # M = 8 slices: GEMV
+    for m0 in range(0, K, 8):                           # M = 8 slices: few-row path
         ys = matmul(eye[m0:m0 + 8], d.w_q, d.w_s)
         assert np.array_equal(ys, wf[:, m0:m0 + 8].T)
+    for m0 in (0, 30, 254):                             # M = 2: matrix-vector
+        ys = matmul(eye[m0:m0 + 2], d.w_q, d.w_s)
+        assert np.array_equal(ys, wf[:, m0:m0 + 2].T)
     for m0 in (0, 31, 32, 255):                         # M = 1, across block edges
         ys = matmul(eye[m0:m0 + 1], d.w_q, d.w_s)
         assert np.array_equal(ys[0], wf[:, m0])
@@ -272,8 +323,8 @@ def test_batched_down_full_size():
     d, y = _full_dense("batched_down", F32)
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     assert_parity(y, y_ref, t, RTOL, what="batched_down")
-    y = matmul_ex(d.x, d.w_q, d.w_s, F32)           # split into slices
-    assert_parity(y, y_ref, t, RTOL, what="batched_down with workspace")
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)           # needs no workspace at M = 4
+    assert_parity(y, y_ref, t, RTOL, what="batched_down through q4_matmul_ex")
 
 
 def test_prefill_full_size_sampled():
@@ -375,7 +426,8 @@ def test_output_guard_bands_untouched(M, out_dtype):
     q4.q4_matmul(dev(d.x), dev(d.w_q), dev(d.w_s), out=y)
     torch.cuda.synchronize()
     assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + M * N:] == 7.0)
-    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=M > 8)
+    mfma = q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=mfma)
     extra = bf16_half_ulp(y_ref) if out_dtype == BF16 else 0.0
     assert_parity(host(y), y_ref, t, RTOL, extra, what="guard")
 
