@@ -73,10 +73,12 @@ __device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
   r[3] = d[1];
 }
 
+}  // namespace
+
 // SCALE4: K/32 is a multiple of 4, so a row's 4 scales of a group are one
 // aligned 8-byte load.
 template <int MG, bool SCALE4>
-__global__ __launch_bounds__(kWaves * 64) void small_kernel(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void small_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
     int64_t K, int64_t groups_per_wave) {
@@ -213,6 +215,8 @@ __global__ __launch_bounds__(kWaves * 64) void small_kernel(
     }
   }
 }
+
+namespace {
 
 template <int MG>
 hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
