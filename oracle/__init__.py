@@ -14,7 +14,11 @@ all 65,536 fp16 scale patterns against numpy's fp16 decoding and torch's
 float32->bf16 rounding; a hand-written nibble-order fixture; closed forms on
 constant and alternating inputs; exact rational brute force on 8x64 tiles;
 agreement with a float64 library matmul of the dequantised weights; MoE
-reductions to the dense case.
+reductions to the dense case.  The routed FFN (tests/test_oracle_ffn.py):
+closed forms with a saturated and a shut SwiGLU gate, an exact bound when the
+up product cancels, exact zeros, the composition of pinned dense products
+with numpy, and scalar brute force on a tiny case; planted mistakes in it are
+caught (tests/test_oracle_mutants.py).
 """
 from __future__ import annotations
 
@@ -73,6 +77,7 @@ def _load():
     lib.oracle_matmul_sampled.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int,
                                           P, P, I64, P, P]
     lib.oracle_moe.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, P, P]
+    lib.oracle_moe_ffn.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P]
     _lib = lib
     return lib
 
@@ -187,3 +192,31 @@ def moe(x: np.ndarray, w_q: np.ndarray, w_s: np.ndarray, ids: np.ndarray,
     _load().oracle_moe(_ptr(x), _ptr(wq), _ptr(ws), _ptr(ids), _ptr(gates),
                        T, topk, E, N, K, _ptr(y), _ptr(t))
     return y, t
+
+
+def moe_ffn(x: np.ndarray, w13_q: np.ndarray, w13_s: np.ndarray, w2_q: np.ndarray,
+            w2_s: np.ndarray, ids: np.ndarray, gates: np.ndarray):
+    """(y, b): double [T][H] routed expert FFN -- gate/up (rows 2f / 2f+1 of
+    w13), a = silu(gate) * up, down (w2), weighted sum over the slots -- and
+    its tolerance scale b (see oracle_moe_ffn in q4_oracle.c)."""
+    E, F2, Hh = w13_q.shape
+    F = F2 // 2
+    H = Hh * 2
+    if F2 % 2 or w13_s.shape != (E, F2, H // 32) or w2_q.shape != (E, H, F // 2) \
+            or w2_s.shape != (E, H, F // 32) or H % 32 or F % 32:
+        raise ValueError("inconsistent FFN weight shapes")
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    if x.shape != (T, H):
+        raise ValueError("x must be [T][H]")
+    ids = _c(ids, np.int32)
+    gates = _c(gates, np.float32)
+    topk = ids.shape[1]
+    if ids.shape != (T, topk) or gates.shape != (T, topk):
+        raise ValueError("ids / gates must be [T][topk]")
+    a = [_c(w13_q, np.uint8), _c(w13_s, np.uint16), _c(w2_q, np.uint8), _c(w2_s, np.uint16)]
+    y = np.empty((T, H), dtype=np.float64)
+    b = np.empty((T, H), dtype=np.float64)
+    _load().oracle_moe_ffn(_ptr(x), _ptr(a[0]), _ptr(a[1]), _ptr(a[2]), _ptr(a[3]),
+                           _ptr(ids), _ptr(gates), T, topk, E, H, F, _ptr(y), _ptr(b))
+    return y, b

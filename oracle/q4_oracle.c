@@ -16,6 +16,12 @@
  *   MoE:  y[t,n] = sum_j g[t,j] * (sum_k x[t,k] * w_{id[t,j]}[n,k])
  *         t[t,n] = sum_j |g[t,j]| * (sum_k |x[t,k] * w_{id[t,j]}[n,k]|)
  *
+ *   Routed expert FFN (gate/up, SwiGLU, down, weighted sum), per selected
+ *   expert e = id[t,j]:
+ *         gate_f = sum_k x[t,k] * w13_e[2f,k],  up_f = sum_k x[t,k] * w13_e[2f+1,k]
+ *         a_f    = silu(gate_f) * up_f,  silu(z) = z / (1 + exp(-z))
+ *         y[t,h] = sum_j g[t,j] * sum_f a_f * w2_e[h,f]
+ *
  * Sources.  The specialised-runtime spec ("spec: specialized model runtimes")
  * names quant/dequant and GEMM as T0 kernel-tier ops (section
  * "Architecture"), a quantised GEMM as the first measured kernel (section
@@ -25,7 +31,9 @@
  * portability contract", rule 1).  The layer-package spec ("Layer Package
  * Repository Spec", the MoE fixture paragraph under "Policy Resolution")
  * describes routed top-k expert matmuls followed by a weighted sum over the
- * selected experts.  The pages fix no bit layout; the readings used here are:
+ * selected experts, and a routed FFN layer as gate/up expert matmuls, a
+ * fused SwiGLU split (silu(gate) * up), the down expert matmul and that
+ * weighted sum.  The pages fix no bit layout; the readings used here are:
  *   - a code is 4 bits, value = code - 8 (symmetric, no zero point);
  *   - one IEEE binary16 scale per 32 consecutive k of a row;
  *   - codes of row n are packed two per byte, k = 2j in the LOW nibble of
@@ -33,7 +41,10 @@
  *   - scales of row n are K/32 consecutive fp16 values;
  *   - activations are bf16, row-major [M][K];
  *   - the prefill (matrix-core) variant rounds each dequantised weight to
- *     bf16, nearest-even, before the product (oracle option bf16_weights).
+ *     bf16, nearest-even, before the product (oracle option bf16_weights);
+ *   - FFN: gate and up weights of an expert are one [2F][H] matrix whose row
+ *     2f is the gate row and row 2f+1 the up row of hidden unit f; the
+ *     SwiGLU output a_f feeds the down product unrounded.
  *
  * Floating point: every fp16 / bf16 value is decoded from its IEEE fields
  * into a double (exact); (c-8)*s is exact in double and in float; products
@@ -224,4 +235,57 @@ void oracle_moe(const uint16_t *x, const uint8_t *wq, const uint16_t *ws,
             t[tok * N + n] = mag;
         }
     }
+}
+
+/* Routed expert FFN.  x: bf16 [T][H]; w13q: [E][2F][H/2]; w13s: [E][2F][H/32]
+ * (row 2f = gate row, row 2f+1 = up row of unit f); w2q: [E][H][F/2];
+ * w2s: [E][H][F/32]; ids: int32 [T][topk]; gates: float [T][topk];
+ * y, b: double [T][H].  An id outside [0, E) adds nothing.
+ *
+ * b is the tolerance scale: each first-stage sum may be off by a fraction of
+ * its own |.|-sum (tg, tu), carried to first order through the SwiGLU
+ * (|silu'| <= 1.1), plus the down product's own |.|-sum:
+ *   b[t,h] = sum_j |g[t,j]| * sum_f |w2_e[h,f]| * (|a_f| + 1.1*|up_f|*tg_f + |silu(gate_f)|*tu_f)
+ */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+void oracle_moe_ffn(const uint16_t *x, const uint8_t *w13q, const uint16_t *w13s,
+                    const uint8_t *w2q, const uint16_t *w2s, const int32_t *ids,
+                    const float *gates, int64_t T, int64_t topk, int64_t E, int64_t H,
+                    int64_t F, double *y, double *b) {
+    double *a = (double *)malloc(sizeof(double) * (size_t)(F > 0 ? F : 1));
+    double *da = (double *)malloc(sizeof(double) * (size_t)(F > 0 ? F : 1));
+    for (int64_t i = 0; i < T * H; ++i) { y[i] = 0.0; b[i] = 0.0; }
+    for (int64_t tok = 0; tok < T; ++tok) {
+        for (int64_t j = 0; j < topk; ++j) {
+            int64_t e = ids[tok * topk + j];
+            if (e < 0 || e >= E) continue;
+            double g = (double)gates[tok * topk + j];
+            #pragma omp parallel for schedule(static)
+            for (int64_t f = 0; f < F; ++f) {
+                int64_t rg = e * 2 * F + 2 * f, ru = rg + 1;
+                double gv, tg, uv, tu;
+                dot_one(x + tok * H, w13q + rg * (H / 2), w13s + rg * (H / Q4O_BLOCK), H, 0, &gv, &tg);
+                dot_one(x + tok * H, w13q + ru * (H / 2), w13s + ru * (H / Q4O_BLOCK), H, 0, &uv, &tu);
+                double sg = silu(gv);
+                a[f] = sg * uv;
+                da[f] = fabs(a[f]) + 1.1 * fabs(uv) * tg + fabs(sg) * tu;
+            }
+            #pragma omp parallel for schedule(static)
+            for (int64_t h = 0; h < H; ++h) {
+                const uint8_t *wr = w2q + (e * H + h) * (F / 2);
+                const uint16_t *sr = w2s + (e * H + h) * (F / Q4O_BLOCK);
+                double o = 0.0, m = 0.0;
+                for (int64_t f = 0; f < F; ++f) {
+                    double w = weight_at(wr, sr, f, 0);
+                    o += a[f] * w;
+                    m += fabs(w) * da[f];
+                }
+                y[tok * H + h] += g * o;
+                b[tok * H + h] += fabs(g) * m;
+            }
+        }
+    }
+    free(a);
+    free(da);
 }

@@ -73,6 +73,17 @@ class MoECase:
     gates: np.ndarray  # float32 [T][topk]
 
 
+@dataclass
+class MoEFFNCase:
+    x: np.ndarray      # uint16 [T][H]
+    w13_q: np.ndarray  # uint8  [E][2F][H/2]  (row 2f gate, row 2f+1 up of unit f)
+    w13_s: np.ndarray  # uint16 [E][2F][H/32]
+    w2_q: np.ndarray   # uint8  [E][H][F/2]
+    w2_s: np.ndarray   # uint16 [E][H][F/32]
+    ids: np.ndarray    # int32  [T][topk]
+    gates: np.ndarray  # float32 [T][topk]
+
+
 def _weights(rng: np.random.Generator, lead: tuple, N: int, K: int, scale_std: float):
     w_q = rng.integers(0, 256, size=lead + (N, K // 2), dtype=np.uint8)
     s = np.abs(rng.standard_normal(lead + (N, K // BLOCK))) * scale_std
@@ -108,6 +119,33 @@ def moe_case(seed: int, T: int, topk: int, E: int, N: int, K: int,
     return MoECase(x=x, w_q=w_q, w_s=w_s, ids=ids, gates=gates)
 
 
+def _route(rng: np.random.Generator, T: int, topk: int, E: int):
+    ids = np.empty((T, topk), dtype=np.int32)
+    gates = np.empty((T, topk), dtype=np.float32)
+    for t in range(T):
+        ids[t] = rng.choice(E, size=topk, replace=False)
+        logits = rng.standard_normal(topk)
+        e = np.exp(logits - logits.max())
+        gates[t] = (e / e.sum()).astype(np.float32)
+    return ids, gates
+
+
+def moe_ffn_case(seed: int, T: int, topk: int, E: int, H: int, F: int,
+                 scale_std: float = 0.02) -> MoEFFNCase:
+    """Routed FFN inputs: gate/up weights [E][2F][H], down weights [E][H][F],
+    bf16 tokens [T][H], router as in moe_case."""
+    if H % BLOCK or F % BLOCK:
+        raise ValueError("H and F must be multiples of 32")
+    if topk > E:
+        raise ValueError("topk distinct experts need topk <= E")
+    rng = np.random.default_rng(seed)
+    w13_q, w13_s = _weights(rng, (E,), 2 * F, H, scale_std)
+    w2_q, w2_s = _weights(rng, (E,), H, F, scale_std)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    ids, gates = _route(rng, T, topk, E)
+    return MoEFFNCase(x=x, w13_q=w13_q, w13_s=w13_s, w2_q=w2_q, w2_s=w2_s, ids=ids, gates=gates)
+
+
 # The five workloads: shapes, seeds and output dtype.
 CONFIGS = {
     "tiny_gemv":      dict(kind="dense", M=1, K=256, N=512, seed=0, out="f32"),
@@ -115,6 +153,12 @@ CONFIGS = {
     "batched_down":   dict(kind="dense", M=4, K=17408, N=5120, seed=2, out="f32"),
     "prefill":        dict(kind="dense", M=512, K=5120, N=34816, seed=3, out="bf16"),
     "moe":            dict(kind="moe", T=8, topk=8, E=128, K=4096, N=1536, seed=4, out="f32"),
+}
+
+# The routed FFN around the moe workload's expert shape: hidden H = 4096,
+# expert width F = 1536 (gate/up [2F][H], down [H][F]).
+FFN_CONFIGS = {
+    "moe_ffn":        dict(kind="moe_ffn", T=8, topk=8, E=128, H=4096, F=1536, seed=5, out="f32"),
 }
 
 

@@ -34,6 +34,39 @@ MUTANTS = {
 }
 
 
+# Mutants of the routed FFN, run against tests/test_oracle_ffn.py.
+FFN_MUTANTS = {
+    "ffn_gate_up_swapped": ("int64_t rg = e * 2 * F + 2 * f, ru = rg + 1;",
+                            "int64_t ru = e * 2 * F + 2 * f, rg = ru + 1;"),
+    "ffn_silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "ffn_silu_dropped": ("double sg = silu(gv);", "double sg = gv;"),
+    "ffn_route_weight_dropped": ("y[tok * H + h] += g * o;", "y[tok * H + h] += o;"),
+    "ffn_down_rows_transposed": ("const uint8_t *wr = w2q + (e * H + h) * (F / 2);",
+                                 "const uint8_t *wr = w2q + (h * E + e) * (F / 2);"),
+    "ffn_bound_propagation_dropped": (
+        "da[f] = fabs(a[f]) + 1.1 * fabs(uv) * tg + fabs(sg) * tu;", "da[f] = fabs(a[f]);"),
+}
+
+
+def _run_suite_on_mutant(old, new, suite, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not unique"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    oracle.compile_to(str(mpath), lib)
+    env = dict(os.environ, Q4_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", suite)],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name", sorted(FFN_MUTANTS))
+def test_ffn_pins_catch_mutant(name, tmp_path):
+    r = _run_suite_on_mutant(*FFN_MUTANTS[name], "test_oracle_ffn.py", tmp_path)
+    assert r.returncode != 0, f"mutant {name} passed every FFN pin:\n{r.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
     old, new = MUTANTS[name]
