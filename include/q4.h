@@ -69,7 +69,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 3
+#define Q4_ABI_VERSION 4
 
 /* Status codes. */
 #define Q4_OK            0
@@ -179,6 +179,37 @@ Q4_API int32_t q4_moe_matmul(const void *x, const void *w_q, const void *w_s,
                              int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes,
                              q4_stream_t stream);
+
+/* Device workspace (bytes) q4_moe_ffn needs for these sizes; 0 if a size is
+ * negative or the size overflows. */
+Q4_API size_t q4_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H,
+                                         int64_t F);
+
+/* Routed expert FFN of one MoE layer (the routed gate/up and down expert
+ * matmuls, the fused SwiGLU split and the weighted sum that the "Layer
+ * Package Repository Spec" measures on its MoE fixture, paragraph under
+ * "Policy Resolution"):
+ *   for each slot j of token t, e = id[t][j]:
+ *     gate_f = sum_k x[t][k] * w13_e[2f][k],  up_f = sum_k x[t][k] * w13_e[2f+1][k]
+ *     a_f    = silu(gate_f) * up_f,   silu(z) = z / (1 + exp(-z))   (fp32, not rounded)
+ *     y[t][h] += g[t][j] * sum_f a_f * w2_e[h][f]
+ *   x         bf16  [T][H]             device
+ *   w13_q     uint8 [E][2F][H/2]       device; row 2f is the gate row and
+ *   w13_s     fp16  [E][2F][H/32]      row 2f+1 the up row of unit f
+ *   w2_q      uint8 [E][H][F/2]        device; down projection
+ *   w2_s      fp16  [E][H][F/32]
+ *   topk_ids, topk_w, workspace        as for q4_moe_matmul (workspace of at
+ *                                      least q4_moe_ffn_workspace_bytes bytes)
+ *   y         fp32  [T][H]             device, fully overwritten
+ * H and F must be positive multiples of 32 and at most 8192 (else
+ * Q4_ERR_SHAPE).  Weights enter exactly (as on the matrix-vector path).
+ * Every touched expert's weights are read once per call; results are
+ * bit-identical from run to run.  T == 0 is a no-op. */
+Q4_API int32_t q4_moe_ffn(const void *x, const void *w13_q, const void *w13_s,
+                          const void *w2_q, const void *w2_s,
+                          const int32_t *topk_ids, const float *topk_w, float *y,
+                          int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
+                          void *workspace, size_t workspace_bytes, q4_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,9 @@ of the C ABI in ``include/q4.h``:
     q4_moe_workspace_bytes(T, topk, E, N)   -> int
     q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None,
                   stream=None) -> y
+    q4_moe_ffn_workspace_bytes(T, topk, E, H, F) -> int
+    q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None,
+               workspace=None, stream=None) -> y
 
 Tensor conventions (all CUDA/HIP device tensors, contiguous):
     x    torch.bfloat16 [M][K]       (or int16/uint16 holding bf16 bits)
@@ -33,7 +36,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 3
+Q4_ABI_VERSION = 4
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -51,7 +54,7 @@ Q4_PATH_SMALL = 2
 __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
-    "q4_moe_matmul",
+    "q4_moe_matmul", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn",
 ]
 
 
@@ -86,6 +89,11 @@ def _open():
     L.q4_moe_workspace_bytes.restype = ctypes.c_size_t
     L.q4_moe_matmul.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     L.q4_moe_matmul.restype = I32
+    L.q4_moe_ffn_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    L.q4_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+    L.q4_moe_ffn.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t,
+                             P]
+    L.q4_moe_ffn.restype = I32
     if L.q4_abi_version() != Q4_ABI_VERSION:
         raise ImportError(f"libq4 ABI version {L.q4_abi_version()} != {Q4_ABI_VERSION}")
     return L
@@ -254,4 +262,48 @@ def q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None, strea
                            _stream_handle(stream, x.device))
     if st != Q4_OK:
         raise Q4Error(st, "q4_moe_matmul")
+    return out
+
+
+def q4_moe_ffn_workspace_bytes(T: int, topk: int, E: int, H: int, F: int) -> int:
+    return int(lib.q4_moe_ffn_workspace_bytes(int(T), int(topk), int(E), int(H), int(F)))
+
+
+def q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None, workspace=None,
+               stream=None):
+    """Routed expert FFN: y[T][H] = sum_j topk_w[t][j] *
+    (silu(x W_gate^T) * (x W_up^T)) W_down^T of expert topk_ids[t][j]; gate and
+    up rows interleaved in w13 (row 2f gate, 2f+1 up), down weights w2 (fp32 y)."""
+    torch = _torch()
+    _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _check_dev(w13_q, "w13_q", (torch.uint8,), 3)
+    _check_dev(w13_s, "w13_s", (torch.float16, torch.int16, torch.uint16), 3)
+    _check_dev(w2_q, "w2_q", (torch.uint8,), 3)
+    _check_dev(w2_s, "w2_s", (torch.float16, torch.int16, torch.uint16), 3)
+    _check_dev(topk_ids, "topk_ids", (torch.int32,), 2)
+    _check_dev(topk_w, "topk_w", (torch.float32,), 2)
+    T, H = x.shape
+    E, F2 = w13_q.shape[0], w13_q.shape[1]
+    F = F2 // 2
+    topk = topk_ids.shape[1]
+    if (F2 % 2 or w13_q.shape[2] * 2 != H or tuple(w13_s.shape) != (E, F2, H // 32)
+            or tuple(w2_q.shape) != (E, H, F // 2) or tuple(w2_s.shape) != (E, H, F // 32)):
+        raise ValueError("weight shapes do not match x")
+    if tuple(topk_ids.shape) != (T, topk) or tuple(topk_w.shape) != (T, topk):
+        raise ValueError("topk_ids / topk_w must be [T][topk]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    else:
+        _check_dev(out, "out", (torch.float32,), 2)
+        if tuple(out.shape) != (T, H):
+            raise ValueError("out has the wrong shape")
+    need = q4_moe_ffn_workspace_bytes(T, topk, E, H, F)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.q4_moe_ffn(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
+                        _ptr(topk_ids), _ptr(topk_w), _ptr(out), T, topk, E, H, F,
+                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_moe_ffn")
     return out

@@ -197,4 +197,43 @@ Q4_API int32_t q4_moe_matmul(const void* x, const void* w_q, const void* w_s,
                                  E, N, K, workspace, static_cast<hipStream_t>(stream)));
 }
 
+Q4_API size_t q4_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H,
+                                         int64_t F) {
+  int64_t P, PH, PF;
+  if (T < 0 || topk < 0 || E < 0 || H < 0 || F < 0) return 0;
+  if (!mul_ok(T, topk, &P) || !mul_ok(P, H, &PH) || !mul_ok(P, F, &PF)) return 0;
+  if (PH > (int64_t(1) << 40) || PF > (int64_t(1) << 40) || E > (int64_t(1) << 40)) return 0;
+  return q4::moe_ffn_workspace_layout(T, topk, E, H, F).total;
+}
+
+Q4_API int32_t q4_moe_ffn(const void* x, const void* w13_q, const void* w13_s, const void* w2_q,
+                          const void* w2_s, const int32_t* topk_ids, const float* topk_w,
+                          float* y, int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
+                          void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  if (T < 0 || topk < 0 || E < 0) return Q4_ERR_SHAPE;
+  if (H <= 0 || F <= 0 || H % 32 != 0 || F % 32 != 0) return Q4_ERR_SHAPE;
+  if (H > q4::kMoeFfnMaxWidth || F > q4::kMoeFfnMaxWidth) return Q4_ERR_SHAPE;
+  int64_t P, th, e2f, e2fh, eh, ehf;
+  if (!mul_ok(T, topk, &P) || !mul_ok(T, H, &th) || !mul_ok(E, 2 * F, &e2f) ||
+      !mul_ok(e2f, H, &e2fh) || !mul_ok(E, H, &eh) || !mul_ok(eh, F, &ehf))
+    return Q4_ERR_SHAPE;
+  if ((P < E ? P : E) > 65535) return Q4_ERR_SHAPE;
+  if (T == 0) return Q4_OK;
+  if (!y || !x || (topk > 0 && (!topk_ids || !topk_w))) return Q4_ERR_NULL;
+  if (E > 0 && topk > 0 && (!w13_q || !w13_s || !w2_q || !w2_s)) return Q4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_w && !aligned16(topk_w)) || (w13_q && !aligned16(w13_q)) ||
+      (w13_s && !aligned16(w13_s)) || (w2_q && !aligned16(w2_q)) || (w2_s && !aligned16(w2_s)))
+    return Q4_ERR_ALIGN;
+  const size_t need = q4_moe_ffn_workspace_bytes(T, topk, E, H, F);
+  if (need == 0 || !workspace || !aligned16(workspace) || workspace_bytes < need)
+    return Q4_ERR_WORKSPACE;
+  if (int32_t s = check_device()) return s;
+  return launched(q4::launch_moe_ffn(
+      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w13_q),
+      static_cast<const uint16_t*>(w13_s), static_cast<const uint8_t*>(w2_q),
+      static_cast<const uint16_t*>(w2_s), topk_ids, topk_w, y, T, topk, E, H, F, workspace,
+      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

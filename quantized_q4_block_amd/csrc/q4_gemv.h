@@ -270,6 +270,48 @@ struct XStager {
   }
 };
 
+// The same staging for one activation row that is already fp32 (the routed
+// FFN's SwiGLU output): two 16-byte loads per 8-element chunk, stored as is.
+template <int S, int THREADS>
+struct XStagerF32 {
+  static constexpr int kRowChunks = S * 4 * kWave;
+  static constexpr int kPer = (kRowChunks + THREADS - 1) / THREADS;
+  uint4 d[kPer][2];
+
+  __device__ __forceinline__ void load(const float* __restrict__ x, int64_t K) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * THREADS + (int)threadIdx.x;
+      const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
+      const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 8;
+      const bool ok = (kRowChunks % THREADS == 0 || c < kRowChunks) && k < K;
+      const uint4* src = reinterpret_cast<const uint4*>(x + (ok ? k : 0));
+      const uint4 v0 = src[0], v1 = src[1];
+      const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
+      d[i][0] = make_uint4(v0.x & keep, v0.y & keep, v0.z & keep, v0.w & keep);
+      d[i][1] = make_uint4(v1.x & keep, v1.y & keep, v1.z & keep, v1.w & keep);
+    }
+  }
+  __device__ __forceinline__ void pin() const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        asm volatile("" ::"v"(d[i][h].x), "v"(d[i][h].y), "v"(d[i][h].z), "v"(d[i][h].w));
+  }
+  __device__ __forceinline__ void store_f32(float4* __restrict__ xs) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = i * THREADS + (int)threadIdx.x;
+      if (kRowChunks % THREADS != 0 && c >= kRowChunks) break;
+      const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
+      float4* row = xs + st * 8 * kWave + l;
+      row[(2 * q) * kWave] = __builtin_bit_cast(float4, d[i][0]);
+      row[(2 * q + 1) * kWave] = __builtin_bit_cast(float4, d[i][1]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // One task of R rows with the activations in LDS and every code and scale
 // load issued up front, for rows of FULL whole stages plus a leftover stage

@@ -42,4 +42,19 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
                       int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
                       hipStream_t stream);
 
+// Routed expert FFN; the MoE layout for N = H followed by the SwiGLU
+// outputs act [T * topk][F] (fp32).  H and F at most 8192 (4 stages).
+struct MoeFfnLayout {
+  MoeLayout base;
+  size_t act, total;
+};
+MoeFfnLayout moe_ffn_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t H,
+                                      int64_t F);
+constexpr int64_t kMoeFfnMaxWidth = 8192;
+
+hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t* w13s,
+                          const uint8_t* w2q, const uint16_t* w2s, const int32_t* ids,
+                          const float* gates, float* y, int64_t T, int64_t topk, int64_t E,
+                          int64_t H, int64_t F, void* workspace, hipStream_t stream);
+
 }  // namespace q4

@@ -242,14 +242,26 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
 // workgroup (bx, slot) owns rows n0 = (bx * kLdsWaves + w) * kLdsRows ..
 // n0 + kLdsRows - 1 of expert active[slot]; row geometry fixed at compile
 // time as in the dense decode kernel.
-template <int FULL, int TAIL>
+//
+// MODE selects the activation rows and the output:
+//  kRowsPlain  x: bf16 token rows (pair p reads token p / topk); writes the
+//              fp32 partial row of pair p;
+//  kRowsGlu    the same rows against a gate/up matrix whose rows 2f, 2f+1 are
+//              the gate and up rows of unit f (a wavefront's 2 rows are one
+//              such pair); writes act[p][f] = silu(gate) * up (fp32);
+//  kRowsDown   x: fp32 rows, one per pair (the SwiGLU output); writes the
+//              fp32 partial row of pair p.
+enum MoeRows { kRowsPlain = 0, kRowsGlu = 1, kRowsDown = 2 };
+
+template <int FULL, int TAIL, int MODE>
 __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const void* __restrict__ xv, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ ws, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ order,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
     float* __restrict__ partial, int64_t topk, int64_t N, int64_t K, int rem) {
   constexpr int R = kLdsRows;
+  static_assert(MODE != kRowsGlu || R == 2, "a gate/up pair is one wavefront task");
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[S * 8 * kWave];
   const int slot = blockIdx.y;
@@ -265,10 +277,18 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
   const uint8_t* wq_e = wq + (int64_t)e * N * (K / 2);
   const uint16_t* ws_e = ws + (int64_t)e * N * (K / kBlock);
-  // the first token's activation loads go out before the weight loads
-  XStager<1, S, kLdsWaves * 64> xst;
+  // the first pair's activation loads go out before the weight loads
+  using Stager = typename std::conditional<MODE == kRowsDown, XStagerF32<S, kLdsWaves * 64>,
+                                           XStager<1, S, kLdsWaves * 64>>::type;
+  Stager xst;
+  auto stage = [&](int32_t pp) __attribute__((always_inline)) {
+    if constexpr (MODE == kRowsDown)
+      xst.load(static_cast<const float*>(xv) + (int64_t)pp * K, K);
+    else
+      xst.load(static_cast<const uint16_t*>(xv) + (int64_t)(pp / topk) * K, K, K);
+  };
   int32_t p = order[start];   // an active expert has at least one pair
-  xst.load(x + (int64_t)(p / topk) * K, K, K);
+  stage(p);
   const uint32_t row_bytes = (uint32_t)(K / 2), row_sc = (uint32_t)(K / kBlock);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq_e + nl * (int64_t)row_bytes, ws_e + nl * (int64_t)row_sc,
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   for (int32_t i = 0; i < cnt; ++i) {
     if (i > 0) {
       p = order[start + i];
-      xst.load(x + (int64_t)(p / topk) * K, K, K);
+      stage(p);
       __syncthreads();                             // xs no longer read
     }
     // fp32 activations: one compute path keeps the register count (and with
@@ -289,9 +309,14 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
     upfront_compute<1, R, FULL, TAIL>(b, xs, rem, lane, out);
     if (live) {
       if (lane == 0) {
+        if constexpr (MODE == kRowsGlu) {
+          const float g = out[0][0], u = out[1][0];
+          partial[(int64_t)p * (N / 2) + n0 / 2] = g / (1.0f + expf(-g)) * u;
+        } else {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (n0 + r < N) partial[(int64_t)p * N + n0 + r] = out[r][0];
+          for (int r = 0; r < R; ++r)
+            if (n0 + r < N) partial[(int64_t)p * N + n0 + r] = out[r][0];
+        }
       }
     }
   }
@@ -328,57 +353,119 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
   }
 }
 
-hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
-                      const int32_t* ids, const float* gates, float* y, int64_t T,
-                      int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
-                      hipStream_t stream) {
-  const MoeLayout L = moe_workspace_layout(T, topk, E, N);
-  char* wsp = static_cast<char*>(workspace);
-  int32_t* counts = reinterpret_cast<int32_t*>(wsp + L.counts);
-  int32_t* fill = reinterpret_cast<int32_t*>(wsp + L.fill);
-  int32_t* offsets = reinterpret_cast<int32_t*>(wsp + L.offsets);
-  int32_t* order = reinterpret_cast<int32_t*>(wsp + L.order);
-  int32_t* active = reinterpret_cast<int32_t*>(wsp + L.active);
-  int32_t* num_active = reinterpret_cast<int32_t*>(wsp + L.num_active);
-  float* partial = reinterpret_cast<float*>(wsp + L.partial);
-  const int64_t P = T * topk;
-  const int64_t max_active = P < E ? P : E;
+namespace {
 
+struct MoeBuffers {
+  int32_t *counts, *fill, *offsets, *order, *active, *num_active;
+};
+
+MoeBuffers moe_buffers(void* workspace, const MoeLayout& L) {
+  char* w = static_cast<char*>(workspace);
+  return {reinterpret_cast<int32_t*>(w + L.counts), reinterpret_cast<int32_t*>(w + L.fill),
+          reinterpret_cast<int32_t*>(w + L.offsets), reinterpret_cast<int32_t*>(w + L.order),
+          reinterpret_cast<int32_t*>(w + L.active), reinterpret_cast<int32_t*>(w + L.num_active)};
+}
+
+hipError_t moe_prep(const int32_t* ids, int64_t P, int64_t E, const MoeBuffers& b,
+                    hipStream_t stream) {
   if (E <= kPrepLdsExperts)
-    moe_prep_lds_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(ids, P, E, counts, offsets,
-                                                                   order, active, num_active);
+    moe_prep_lds_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(
+        ids, P, E, b.counts, b.offsets, b.order, b.active, b.num_active);
   else
-    moe_prep_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(ids, P, E, counts, fill, offsets,
-                                                                order, active, num_active);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (max_active > 65535) return hipErrorInvalidValue;
-  if (max_active > 0) {
-    if (x_stages(K) <= kLdsMaxStages) {
-      const int64_t row_blocks = (N + kLdsWaves * kLdsRows - 1) / (kLdsWaves * kLdsRows);
-      if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-      const int rem = row_leftover(K);
-      const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
-      err = dispatch_row_geometry(K, [&](auto full, auto tail) {
-        moe_lds_kernel<decltype(full)::value, decltype(tail)::value>
-            <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, counts, offsets, order, active,
-                                                        num_active, partial, topk, N, K, rem);
-        return hipGetLastError();
-      });
-    } else {
-      const int64_t row_blocks = (N + kRowsPerWg - 1) / kRowsPerWg;
-      if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-      moe_gemv_kernel<<<dim3((unsigned)row_blocks, (unsigned)max_active), dim3(256), 0, stream>>>(
-          x, wq, ws, counts, offsets, order, active, num_active, partial, topk, N, K);
-      err = hipGetLastError();
-    }
-    if (err != hipSuccess) return err;
-  }
+    moe_prep_kernel<<<dim3(1), dim3(kPrepThreads), 0, stream>>>(
+        ids, P, E, b.counts, b.fill, b.offsets, b.order, b.active, b.num_active);
+  return hipGetLastError();
+}
+
+// One gathered product over every touched expert (LDS kernel; rows of at
+// most kLdsMaxStages stages).
+template <int MODE>
+hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
+                         const MoeBuffers& b, float* out, int64_t topk, int64_t N, int64_t K,
+                         int64_t max_active, hipStream_t stream) {
+  const int64_t row_blocks = (N + kLdsWaves * kLdsRows - 1) / (kLdsWaves * kLdsRows);
+  if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int rem = row_leftover(K);
+  const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
+  return dispatch_row_geometry(K, [&](auto full, auto tail) {
+    moe_lds_kernel<decltype(full)::value, decltype(tail)::value, MODE>
+        <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, b.counts, b.offsets, b.order,
+                                                    b.active, b.num_active, out, topk, N, K, rem);
+    return hipGetLastError();
+  });
+}
+
+hipError_t moe_combine(const int32_t* ids, const float* gates, const float* partial, float* y,
+                       int64_t T, int64_t topk, int64_t E, int64_t N, hipStream_t stream) {
   int64_t grid = (T * N + 255) / 256;
   if (grid > 65536) grid = 65536;
   moe_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(ids, gates, partial, y, T,
                                                                      topk, E, N);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
+                      const int32_t* ids, const float* gates, float* y, int64_t T,
+                      int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
+                      hipStream_t stream) {
+  const MoeLayout L = moe_workspace_layout(T, topk, E, N);
+  const MoeBuffers b = moe_buffers(workspace, L);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.partial);
+  const int64_t P = T * topk;
+  const int64_t max_active = P < E ? P : E;
+  hipError_t err = moe_prep(ids, P, E, b, stream);
+  if (err != hipSuccess) return err;
+  if (max_active > 65535) return hipErrorInvalidValue;
+  if (max_active > 0) {
+    if (x_stages(K) <= kLdsMaxStages) {
+      err = moe_stage_lds<kRowsPlain>(x, wq, ws, b, partial, topk, N, K, max_active, stream);
+    } else {
+      const int64_t row_blocks = (N + kRowsPerWg - 1) / kRowsPerWg;
+      if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+      moe_gemv_kernel<<<dim3((unsigned)row_blocks, (unsigned)max_active), dim3(256), 0, stream>>>(
+          x, wq, ws, b.counts, b.offsets, b.order, b.active, b.num_active, partial, topk, N, K);
+      err = hipGetLastError();
+    }
+    if (err != hipSuccess) return err;
+  }
+  return moe_combine(ids, gates, partial, y, T, topk, E, N, stream);
+}
+
+MoeFfnLayout moe_ffn_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t H,
+                                      int64_t F) {
+  MoeFfnLayout L;
+  L.base = moe_workspace_layout(T, topk, E, H);
+  L.act = L.base.total;
+  L.total = align_up(L.act + 4 * (size_t)T * (size_t)topk * (size_t)F);
+  return L;
+}
+
+// Routed expert FFN: prep, gate/up product with the SwiGLU in its store
+// (act[p][f], fp32), down product over the same buckets with act as the
+// activation rows, weighted sum.
+hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t* w13s,
+                          const uint8_t* w2q, const uint16_t* w2s, const int32_t* ids,
+                          const float* gates, float* y, int64_t T, int64_t topk, int64_t E,
+                          int64_t H, int64_t F, void* workspace, hipStream_t stream) {
+  const MoeFfnLayout L = moe_ffn_workspace_layout(T, topk, E, H, F);
+  const MoeBuffers b = moe_buffers(workspace, L.base);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.base.partial);
+  float* act = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.act);
+  const int64_t P = T * topk;
+  const int64_t max_active = P < E ? P : E;
+  if (x_stages(H) > kLdsMaxStages || x_stages(F) > kLdsMaxStages) return hipErrorInvalidValue;
+  hipError_t err = moe_prep(ids, P, E, b, stream);
+  if (err != hipSuccess) return err;
+  if (max_active > 65535) return hipErrorInvalidValue;
+  if (max_active > 0) {
+    err = moe_stage_lds<kRowsGlu>(x, w13q, w13s, b, act, topk, 2 * F, H, max_active, stream);
+    if (err != hipSuccess) return err;
+    err = moe_stage_lds<kRowsDown>(act, w2q, w2s, b, partial, 1, H, F, max_active, stream);
+    if (err != hipSuccess) return err;
+  }
+  return moe_combine(ids, gates, partial, y, T, topk, E, H, stream);
 }
 
 }  // namespace q4

@@ -45,3 +45,11 @@ def moe(x, w_q, w_s, ids, gates):
     y = q4.q4_moe_matmul(dev(x), dev(w_q), dev(w_s), dev(ids), dev(gates))
     torch.cuda.synchronize()
     return host(y)
+
+
+def moe_ffn(c, ids=None, gates=None, workspace=None):
+    y = q4.q4_moe_ffn(dev(c.x), dev(c.w13_q), dev(c.w13_s), dev(c.w2_q), dev(c.w2_s),
+                      dev(c.ids if ids is None else ids), dev(c.gates if gates is None else gates),
+                      workspace=workspace)
+    torch.cuda.synchronize()
+    return host(y)

@@ -48,7 +48,8 @@ def test_header_declares_the_abi():
     syms = _declared_symbols()
     assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
                          "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
-                         "q4_moe_workspace_bytes", "q4_moe_matmul"}
+                         "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_ffn_workspace_bytes",
+                         "q4_moe_ffn"}
 
 
 def test_every_declared_symbol_is_exported():
@@ -244,6 +245,44 @@ def test_moe_argument_errors():
     assert moe(wb=need - 1) == q4.Q4_ERR_WORKSPACE
     if not _gpu_present():
         assert moe() == q4.Q4_ERR_DEVICE
+
+
+def test_moe_ffn_workspace_bytes():
+    q4, _ = _lib()
+    assert q4.q4_moe_ffn_workspace_bytes(-1, 8, 128, 4096, 1536) == 0
+    assert q4.q4_moe_ffn_workspace_bytes(8, 8, 128, -1, 1536) == 0
+    assert q4.q4_moe_ffn_workspace_bytes(1 << 40, 1 << 20, 4, 32, 32) == 0
+    b = q4.q4_moe_ffn_workspace_bytes(8, 8, 128, 4096, 1536)
+    # the down partial rows [P][H] and the SwiGLU outputs [P][F], fp32
+    assert b >= 64 * (4096 + 1536) * 4
+    assert b % 256 == 0
+    assert b > q4.q4_moe_workspace_bytes(8, 8, 128, 4096)
+
+
+def test_moe_ffn_argument_errors():
+    q4, L = _lib()
+    P = ctypes.c_void_p
+    T, topk, E, H, F = 8, 8, 128, 4096, 1536
+    need = q4.q4_moe_ffn_workspace_bytes(T, topk, E, H, F)
+
+    def ffn(x=A, w13q=A, w13s=A, w2q=A, w2s=A, ids=A, g=A, y=A, T=T, topk=topk, E=E, H=H, F=F,
+            w=A, wb=need):
+        return L.q4_moe_ffn(P(x), P(w13q), P(w13s), P(w2q), P(w2s), P(ids), P(g), P(y), T, topk,
+                            E, H, F, P(w), wb, None)
+
+    for bad in (dict(H=100), dict(F=48), dict(H=0), dict(F=0), dict(H=8192 + 32),
+                dict(F=8192 + 32), dict(T=-1), dict(E=-1), dict(topk=-1),
+                dict(T=70000, topk=1, E=70000)):
+        assert ffn(**bad) == q4.Q4_ERR_SHAPE, bad
+    assert ffn(x=0, w13q=0, w13s=0, w2q=0, w2s=0, ids=0, g=0, y=0, w=0, T=0) == q4.Q4_OK
+    for kw in ("x", "w13q", "w13s", "w2q", "w2s", "ids", "g", "y"):
+        assert ffn(**{kw: 0}) == q4.Q4_ERR_NULL, kw
+        assert ffn(**{kw: MIS}) == q4.Q4_ERR_ALIGN, kw
+    assert ffn(w=0) == q4.Q4_ERR_WORKSPACE
+    assert ffn(w=MIS) == q4.Q4_ERR_WORKSPACE
+    assert ffn(wb=need - 1) == q4.Q4_ERR_WORKSPACE
+    if not _gpu_present():
+        assert ffn() == q4.Q4_ERR_DEVICE
 
 
 def test_binding_rejects_host_tensors():
