@@ -13,8 +13,8 @@ step streams its 100.27 MB of codes and scales from HBM.
 Printed: one JSON line with value = weight+scale GB/s (whole job), the
 roofline of the dominant kernel (the decode GEMV) from HIP events over the
 timed region, the CPU oracle's rate on the host, and the other workloads
-(batched decode M = 4, prefill M = 512, MoE) measured the same way as
-extra context.
+(batched decode M = 4, prefill M = 512, MoE, and the routed expert FFN
+built around the MoE expert shape) measured the same way as extra context.
 """
 from __future__ import annotations
 
@@ -141,6 +141,49 @@ class MoE:
         st = self.fn(*self.args[i % self.copies], stream)
         if st:
             raise RuntimeError(f"q4_moe_matmul failed with status {st}")
+
+
+class MoeFfn:
+    """The routed expert FFN around the moe workload's expert shape (hidden
+    H = 4096, F = 1536 per expert, T = 8 tokens, top-8 of E = 128): gate/up
+    product with the SwiGLU in its store, down product, weighted sum."""
+
+    def __init__(self, torch, q4, copies=None):
+        import synthetic
+        c = synthetic.FFN_CONFIGS["moe_ffn"]
+        self.T, self.topk, self.E, self.H, self.F = c["T"], c["topk"], c["E"], c["H"], c["F"]
+        m = synthetic.moe_ffn_case(c["seed"], self.T, self.topk, self.E, self.H, self.F)
+        dev = "cuda:0"
+        per_expert = weight_bytes(2 * self.F, self.H) + weight_bytes(self.H, self.F)
+        n = copies or max(2, -(-ROTATE_BYTES // (per_expert * self.E)) + 1)
+        self.copies = n
+
+        def put(a, i16=False):
+            t = torch.from_numpy(a.view(np.int16) if i16 else a).to(dev)
+            return [t] + [t.clone() for _ in range(n - 1)]
+        self.x = torch.from_numpy(m.x.view(np.int16)).to(dev)
+        self.w13q, self.w13s = put(m.w13_q), put(m.w13_s, True)
+        self.w2q, self.w2s = put(m.w2_q), put(m.w2_s, True)
+        self.ids = torch.from_numpy(m.ids).to(dev)
+        self.g = torch.from_numpy(m.gates).to(dev)
+        self.y = torch.empty((self.T, self.H), device=dev, dtype=torch.float32)
+        need = q4.q4_moe_ffn_workspace_bytes(self.T, self.topk, self.E, self.H, self.F)
+        self.wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_moe_ffn
+        self.args = [(P(self.x.data_ptr()), P(self.w13q[i].data_ptr()), P(self.w13s[i].data_ptr()),
+                      P(self.w2q[i].data_ptr()), P(self.w2s[i].data_ptr()),
+                      P(self.ids.data_ptr()), P(self.g.data_ptr()), P(self.y.data_ptr()),
+                      self.T, self.topk, self.E, self.H, self.F, P(self.wsp.data_ptr()), need)
+                     for i in range(n)]
+        self.touched = len(np.unique(m.ids))
+        self.wbytes = self.touched * per_expert     # every touched expert read once
+        self.flops = 2 * self.T * self.topk * 3 * self.H * self.F
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_moe_ffn failed with status {st}")
 
 
 def calibration_copy(torch, mib, reps=3):
@@ -332,6 +375,17 @@ def main():
                          "touched_experts": w.touched, "avg_call_us": round(ev * 1e3, 2),
                          "touched_weight_GB/s": round(gbs, 1),
                          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del w
+        torch.cuda.empty_cache()
+        progress("moe_ffn: generating inputs")
+        w = MoeFfn(torch, q4)
+        progress("moe_ffn: timing")
+        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+        gbs = w.wbytes / (ev * 1e-3) / 1e9
+        others["moe_ffn"] = {"T": w.T, "topk": w.topk, "E": w.E, "H": w.H, "F": w.F,
+                             "touched_experts": w.touched, "avg_call_us": round(ev * 1e3, 2),
+                             "touched_weight_GB/s": round(gbs, 1),
+                             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del w
         torch.cuda.empty_cache()
 

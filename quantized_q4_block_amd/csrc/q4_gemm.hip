@@ -236,8 +236,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
           (__attribute__((address_space(3))) void*)(&As[buf][(wave * 4 + j) * 64 * 8]), 16, 0, 0);
   };
   // weight staging: thread -> (row srow, half shalf): one 32-element block;
-  // rows past N get scale 0
-  const int srow = tid >> 1, shalf = tid & 1;
+  // rows past N get scale 0.  The 128-bit LDS stores go out 8 lanes at a
+  // time, so every 8 consecutive lanes take rows 2q + b (q = 0..3, b fixed)
+  // of an 8-row group, both halves: with the XOR swizzle their 16-byte chunks
+  // fall in 8 distinct bank groups (lanes 2i, 2i+1 on rows i would pair up).
+  const int sl = tid & 63;
+  const int srow = (tid >> 6) * 32 + ((sl >> 4) << 3) + (((sl >> 1) & 3) << 1) + ((sl >> 3) & 1);
+  const int shalf = sl & 1;
   const int64_t bn = n0 + srow;
   const bool b_ok = bn < N;
   const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
