@@ -288,10 +288,66 @@ def cpu_baseline(min_seconds=12.0, max_reps=100000):
         if el >= min_seconds or reps >= max_reps:
             break
     gbs = reps * weight_bytes(c["N"], c["K"]) / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+    cores = oracle.max_threads()
+    # the same oracle on one thread, over the first 2048 weight rows
+    rows = 2048
+    oracle.set_threads(1)
+    try:
+        reps1, t0 = 0, time.perf_counter()
+        while True:
+            oracle.matmul(d.x, d.w_q[:rows], d.w_s[:rows])
+            reps1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= min_seconds / 4 or reps1 >= max_reps:
+                break
+    finally:
+        oracle.set_threads(cores)
+    gbs1 = reps1 * weight_bytes(rows, c["K"]) / el1 / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"full decode_gate_up (M=1, K=5120, N=34816) x {reps} reps, "
-                      f"{el:.1f} s, double accumulation"}
+                      f"{el:.1f} s, double accumulation",
+            "host_cpu": host_cpu_model(),
+            "single_thread": {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"decode_gate_up rows 0..{rows - 1} x {reps1} reps, "
+                                        f"{el1:.1f} s"}}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def summarize_trace(run_dir):
+    """Per-kernel dispatch count, mean, p10, median, p90, min and max duration
+    (us) from the kernel_trace.csv files a rocprofv3 --kernel-trace run wrote
+    under run_dir."""
+    import csv
+    durs = {}
+    for dirpath, _, files in os.walk(run_dir):
+        for fn in files:
+            if not fn.endswith("kernel_trace.csv"):
+                continue
+            with open(os.path.join(dirpath, fn), newline="") as f:
+                for row in csv.DictReader(f):
+                    name = row["Kernel_Name"].replace("void ", "").split("(")[0]
+                    d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                    durs.setdefault(name, []).append(d)
+    out = {}
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        a = np.asarray(v)
+        out[name] = {"calls": int(a.size), "mean_us": round(float(a.mean()), 2),
+                     "p10_us": round(float(np.percentile(a, 10)), 2),
+                     "median_us": round(float(np.median(a)), 2),
+                     "p90_us": round(float(np.percentile(a, 90)), 2),
+                     "min_us": round(float(a.min()), 2), "max_us": round(float(a.max()), 2)}
+    return out
 
 
 def main():
@@ -303,11 +359,17 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain copy kernel of this many MiB (for counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print per-kernel duration statistics (mean, p10, median, p90) of a "
+                         "rocprofv3 --kernel-trace run of this script (no GPU needed)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script with --calibrate-copy-mib 256 into the decode kernel's "
                          "HBM traffic record under profiles/ (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], 256,
                       "gemv_decode_gate_up", "gemv_lds_kernel", weight_bytes(34816, 5120),
@@ -405,6 +467,8 @@ def main():
                    "rotating_weight_copies": copies, "csrc_digest": digest},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "env": {"device": torch.cuda.get_device_properties(0).gcnArchName,
+                "hip_runtime": torch.version.hip, "torch": torch.__version__},
         "other_workloads": others,
     }
     print(json.dumps(out), flush=True)

@@ -75,3 +75,25 @@ def test_traffic_record_is_ignored_for_other_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(b, "ROOT", str(tmp_path))
     assert b.traffic_from_profile("k", "new") is None
     assert b.traffic_from_profile("k", "old") == 5
+
+
+def test_summarize_trace_percentiles(tmp_path):
+    b = _bench()
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    with open(d / "7_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        # kernel a: 1..10 us; kernel b: one 100 us launch
+        for i in range(1, 11):
+            w.writerow({"Kernel_Name": "void q4::a<1>(int)", "Start_Timestamp": 1000 * i,
+                        "End_Timestamp": 1000 * i + 1000 * i})
+        w.writerow({"Kernel_Name": "q4::b(float*)", "Start_Timestamp": 0,
+                    "End_Timestamp": 100000})
+    s = b.summarize_trace(str(tmp_path / "trace"))
+    assert list(s) == ["q4::b", "q4::a<1>"]          # by total time
+    a = s["q4::a<1>"]
+    assert a["calls"] == 10 and a["mean_us"] == 5.5 and a["median_us"] == 5.5
+    assert a["p10_us"] == 1.9 and a["p90_us"] == 9.1
+    assert a["min_us"] == 1.0 and a["max_us"] == 10.0
+    assert s["q4::b"]["calls"] == 1 and s["q4::b"]["median_us"] == 100.0
