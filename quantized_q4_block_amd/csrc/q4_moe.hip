@@ -239,8 +239,8 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
 }
 
 // Gathered product with the expert's rows loaded once: wavefront w of
-// workgroup (bx, slot) owns rows n0 = (bx * kLdsWaves + w) * kLdsRows ..
-// n0 + kLdsRows - 1 of expert active[slot]; row geometry fixed at compile
+// workgroup (bx, slot) owns rows n0 = (bx * kLdsWaves + w) * RT ..
+// n0 + RT - 1 of expert active[slot]; row geometry fixed at compile
 // time as in the dense decode kernel.
 //
 // MODE selects the activation rows and the output:
@@ -253,14 +253,20 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
 //              fp32 partial row of pair p.
 enum MoeRows { kRowsPlain = 0, kRowsGlu = 1, kRowsDown = 2 };
 
-template <int FULL, int TAIL, int MODE>
+#ifndef Q4_MOE_SHORT_ROWS
+#define Q4_MOE_SHORT_ROWS 4
+#endif
+// Rows per wavefront task when a row is at most one stage (K <= 2048).
+constexpr int kMoeShortRows = Q4_MOE_SHORT_ROWS;
+
+template <int FULL, int TAIL, int MODE, int RT>
 __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ ws, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ order,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
     float* __restrict__ partial, int64_t topk, int64_t N, int64_t K, int rem) {
-  constexpr int R = kLdsRows;
+  constexpr int R = RT;
   static_assert(MODE != kRowsGlu || R == 2, "a gate/up pair is one wavefront task");
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[S * 8 * kWave];
@@ -383,12 +389,17 @@ template <int MODE>
 hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
                          const MoeBuffers& b, float* out, int64_t topk, int64_t N, int64_t K,
                          int64_t max_active, hipStream_t stream) {
-  const int64_t row_blocks = (N + kLdsWaves * kLdsRows - 1) / (kLdsWaves * kLdsRows);
-  if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int rem = row_leftover(K);
-  const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
   return dispatch_row_geometry(K, [&](auto full, auto tail) {
-    moe_lds_kernel<decltype(full)::value, decltype(tail)::value, MODE>
+    constexpr int FULL = decltype(full)::value;
+    // a row of one (partial) stage is little work for a wavefront: give it
+    // more rows, so the activation staging and the reduction are shared by
+    // more weight bytes (gate/up tasks stay one gate and one up row)
+    constexpr int RT = (MODE != kRowsGlu && FULL == 0) ? kMoeShortRows : kLdsRows;
+    const int64_t row_blocks = (N + kLdsWaves * RT - 1) / (kLdsWaves * RT);
+    if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
+    moe_lds_kernel<FULL, decltype(tail)::value, MODE, RT>
         <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, b.counts, b.offsets, b.order,
                                                     b.active, b.num_active, out, topk, N, K, rem);
     return hipGetLastError();
