@@ -18,7 +18,10 @@ reductions to the dense case.  The routed FFN (tests/test_oracle_ffn.py):
 closed forms with a saturated and a shut SwiGLU gate, an exact bound when the
 up product cancels, exact zeros, the composition of pinned dense products
 with numpy, and scalar brute force on a tiny case; planted mistakes in it are
-caught (tests/test_oracle_mutants.py).
+caught (tests/test_oracle_mutants.py).  The 4-bit float block variant
+(tests/test_oracle_mx.py): the E8M0 scales against torch's float8_e8m0fnu
+decoding, the e2m1 element set by the properties that identify it, closed
+forms, exact rational brute force and a float64 library matmul.
 """
 from __future__ import annotations
 
@@ -78,6 +81,12 @@ def _load():
                                           P, P, I64, P, P]
     lib.oracle_moe.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, P, P]
     lib.oracle_moe_ffn.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P]
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_int]
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
+    lib.oracle_mx_matmul.argtypes = [P, P, P, I64, I64, I64, P, P]
     _lib = lib
     return lib
 
@@ -220,3 +229,45 @@ def moe_ffn(x: np.ndarray, w13_q: np.ndarray, w13_s: np.ndarray, w2_q: np.ndarra
     _load().oracle_moe_ffn(_ptr(x), _ptr(a[0]), _ptr(a[1]), _ptr(a[2]), _ptr(a[3]),
                            _ptr(ids), _ptr(gates), T, topk, E, H, F, _ptr(y), _ptr(b))
     return y, b
+
+
+# ---- 4-bit float blocks (e2m1 elements, E8M0 block scales) ----------------
+
+def e2m1_value(code: int) -> float:
+    return float(_load().oracle_e2m1_value(int(code)))
+
+
+def e8m0_value(bits: int) -> float:
+    return float(_load().oracle_e8m0_value(int(bits)))
+
+
+def _check_mx(w_q, w_e):
+    N, kh = w_q.shape[-2:]
+    K = 2 * kh
+    if K % BLOCK or w_e.shape[-1] != K // BLOCK or w_e.shape[-2] != N:
+        raise ValueError("inconsistent w_q / w_e shapes")
+    return N, K
+
+
+def mx_dequant(w_q: np.ndarray, w_e: np.ndarray) -> np.ndarray:
+    """float64 [N][K]: e2m1(code) * 2^(E - 127), exact."""
+    N, K = _check_mx(w_q, w_e)
+    wq, we = _c(w_q, np.uint8), _c(w_e, np.uint8)
+    out = np.empty((N, K), dtype=np.float64)
+    _load().oracle_mx_dequant(_ptr(wq), _ptr(we), N, K, _ptr(out))
+    return out
+
+
+def mx_matmul(x: np.ndarray, w_q: np.ndarray, w_e: np.ndarray):
+    """(y, t): double [M][N] product with 4-bit float block weights and
+    sum_k |x*w| per output."""
+    N, K = _check_mx(w_q, w_e)
+    x = _c(x, np.uint16)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x has the wrong K")
+    wq, we = _c(w_q, np.uint8), _c(w_e, np.uint8)
+    y = np.empty((M, N), dtype=np.float64)
+    t = np.empty((M, N), dtype=np.float64)
+    _load().oracle_mx_matmul(_ptr(x), _ptr(wq), _ptr(we), M, N, K, _ptr(y), _ptr(t))
+    return y, t

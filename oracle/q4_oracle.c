@@ -46,6 +46,19 @@
  *     2f is the gate row and row 2f+1 the up row of hidden unit f; the
  *     SwiGLU output a_f feeds the down product unrounded.
  *
+ * 4-bit float blocks.  The specialised-runtime spec names a 4-bit float block
+ * format as the performance path after groupwise-int weights (section "Target
+ * package and artifact") but fixes no bits.  The reading taken is the public
+ * microscaling definition with 32-element blocks:
+ *   - an element is e2m1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0
+ *     mantissa; exponent 0 is subnormal (m * 2^-1), otherwise
+ *     (1 + m/2) * 2^(e-1); no infinity or NaN;
+ *   - one E8M0 byte per 32 consecutive k scales the block by 2^(E-127);
+ *     E = 255 is NaN;
+ *   - elements are packed like the int4 codes (k = 2j in the low nibble),
+ *     scales are K/32 bytes per row:
+ *         w[n,k] = e2m1(c[n,k]) * 2^(E[n, k/32] - 127)
+ *
  * Floating point: every fp16 / bf16 value is decoded from its IEEE fields
  * into a double (exact); (c-8)*s is exact in double and in float; products
  * x*w are exact in double; only the k-ordered sum rounds.
@@ -131,7 +144,56 @@ static double weight_at(const uint8_t *wq_row, const uint16_t *ws_row, int64_t k
     return bf16_weights ? bf16_round(w) : w;
 }
 
+/* e2m1 element from its fields. */
+static double e2m1_value(int c) {
+    int sign = (c >> 3) & 1;
+    int e = (c >> 1) & 3;
+    int m = c & 1;
+    double v = (e == 0) ? ldexp((double)m, -1) : ldexp(2.0 + m, e - 2);   /* (1 + m/2) 2^(e-1) */
+    return sign ? -v : v;
+}
+
+/* E8M0 scale byte: 2^(E-127), E = 255 is NaN. */
+static double e8m0_value(uint8_t e) {
+    return e == 255 ? NAN : ldexp(1.0, (int)e - 127);
+}
+
+static double mx_weight_at(const uint8_t *wq_row, const uint8_t *we_row, int64_t k) {
+    return e2m1_value(code_at(wq_row, k)) * e8m0_value(we_row[k / Q4O_BLOCK]);
+}
+
 /* ---- exported ---------------------------------------------------------- */
+
+double oracle_e2m1_value(int c) { return e2m1_value(c & 15); }
+double oracle_e8m0_value(uint8_t e) { return e8m0_value(e); }
+
+/* 4-bit float blocks dequantised to double [N][K] (exact). */
+void oracle_mx_dequant(const uint8_t *wq, const uint8_t *we, int64_t N, int64_t K,
+                       double *out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = mx_weight_at(wq + n * (K / 2), we + n * (K / Q4O_BLOCK), k);
+}
+
+/* y = x . w^T with 4-bit float block weights; y, t: double [M][N]. */
+void oracle_mx_matmul(const uint16_t *x, const uint8_t *wq, const uint8_t *we,
+                      int64_t M, int64_t N, int64_t K, double *y, double *t) {
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            const uint16_t *xr = x + m * K;
+            const uint8_t *wr = wq + n * (K / 2), *er = we + n * (K / Q4O_BLOCK);
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = bf16_value(xr[k]) * mx_weight_at(wr, er, k);
+                acc += p;
+                mag += fabs(p);
+            }
+            y[m * N + n] = acc;
+            t[m * N + n] = mag;
+        }
+}
 
 int oracle_block(void) { return Q4O_BLOCK; }
 

@@ -26,6 +26,12 @@ experts.
 
 Draw order inside one case: codes, scales, x, then (MoE) the router, token
 by token.
+
+4-bit float blocks (``mx_case``): the codes are drawn as above (e2m1
+elements, the library's convention again); each block's E8M0 scale byte is
+drawn uniformly from 118..122 (scales 2^-9 .. 2^-5, the range in which
+blocks of weights of the magnitude above put their largest element near the
+top of the e2m1 range, 6).
 """
 from __future__ import annotations
 
@@ -37,7 +43,7 @@ BLOCK = 32  # elements per quantisation block along K
 
 __all__ = [
     "BLOCK", "DenseCase", "MoECase", "CONFIGS", "dense_case", "moe_case",
-    "f32_to_bf16_bits", "config_case",
+    "f32_to_bf16_bits", "config_case", "MXCase", "mx_case", "MX_CONFIGS",
 ]
 
 
@@ -167,3 +173,28 @@ def config_case(name: str):
     if c["kind"] == "dense":
         return dense_case(c["seed"], c["M"], c["N"], c["K"])
     return moe_case(c["seed"], c["T"], c["topk"], c["E"], c["N"], c["K"])
+
+
+@dataclass
+class MXCase:
+    x: np.ndarray    # uint16 [M][K]   bf16 bits
+    w_q: np.ndarray  # uint8  [N][K/2] packed 4-bit elements
+    w_e: np.ndarray  # uint8  [N][K/32] E8M0 scale bytes
+
+
+def mx_case(seed: int, M: int, N: int, K: int, e_lo: int = 118, e_hi: int = 122) -> MXCase:
+    """4-bit float block weights: uniform element bytes, E8M0 scale bytes
+    uniform in e_lo..e_hi; bf16 x ~ N(0, 1)."""
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.default_rng(seed)
+    w_q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    w_e = rng.integers(e_lo, e_hi + 1, size=(N, K // BLOCK), dtype=np.uint8)
+    x = f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return MXCase(x=x, w_q=w_q, w_e=w_e)
+
+
+# The decode gate+up shape with 4-bit float block weights.
+MX_CONFIGS = {
+    "mx_decode_gate_up": dict(kind="mx", M=1, K=5120, N=34816, seed=6, out="f32"),
+}

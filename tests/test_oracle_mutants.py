@@ -34,6 +34,17 @@ MUTANTS = {
 }
 
 
+# Mutants of the 4-bit float block product, run against tests/test_oracle_mx.py.
+MX_MUTANTS = {
+    "mx_exponent_bias_0": ("ldexp(2.0 + m, e - 2)", "ldexp(2.0 + m, e - 1)"),
+    "mx_sign_bit_0": ("int sign = (c >> 3) & 1;\n    int e = (c >> 1) & 3;\n    int m = c & 1;",
+                      "int sign = c & 1;\n    int e = (c >> 1) & 3;\n    int m = (c >> 3) & 1;"),
+    "mx_subnormal_weight": ("ldexp((double)m, -1)", "ldexp((double)m, 0)"),
+    "mx_scale_bias_128": ("ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 128)"),
+    "mx_scale_block_16": ("we_row[k / Q4O_BLOCK]", "we_row[k / 16]"),
+}
+
+
 # Mutants of the routed FFN, run against tests/test_oracle_ffn.py.
 FFN_MUTANTS = {
     "ffn_gate_up_swapped": ("int64_t rg = e * 2 * F + 2 * f, ru = rg + 1;",
@@ -59,6 +70,12 @@ def _run_suite_on_mutant(old, new, suite, tmp_path):
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                            os.path.join(ROOT, "tests", suite)],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name", sorted(MX_MUTANTS))
+def test_mx_pins_catch_mutant(name, tmp_path):
+    r = _run_suite_on_mutant(*MX_MUTANTS[name], "test_oracle_mx.py", tmp_path)
+    assert r.returncode != 0, f"mutant {name} passed every 4-bit float pin:\n{r.stdout[-2000:]}"
 
 
 @pytest.mark.parametrize("name", sorted(FFN_MUTANTS))
