@@ -184,14 +184,14 @@ void oracle_mx_matmul(const uint16_t *x, const uint8_t *wq, const uint8_t *we,
         for (int64_t m = 0; m < M; ++m) {
             const uint16_t *xr = x + m * K;
             const uint8_t *wr = wq + n * (K / 2), *er = we + n * (K / Q4O_BLOCK);
-            double acc = 0.0, mag = 0.0;
+            double sum = 0.0, abs_sum = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                double p = bf16_value(xr[k]) * mx_weight_at(wr, er, k);
-                acc += p;
-                mag += fabs(p);
+                double prod = bf16_value(xr[k]) * mx_weight_at(wr, er, k);
+                sum += prod;
+                abs_sum += fabs(prod);
             }
-            y[m * N + n] = acc;
-            t[m * N + n] = mag;
+            y[m * N + n] = sum;
+            t[m * N + n] = abs_sum;
         }
 }
 
