@@ -13,8 +13,9 @@ step streams its 100.27 MB of codes and scales from HBM.
 Printed: one JSON line with value = weight+scale GB/s (whole job), the
 roofline of the dominant kernel (the decode GEMV) from HIP events over the
 timed region, the CPU oracle's rate on the host, and the other workloads
-(batched decode M = 4, prefill M = 512, MoE, and the routed expert FFN
-built around the MoE expert shape) measured the same way as extra context.
+(batched decode M = 4, prefill M = 512, the decode shape with 4-bit float
+block weights, MoE, and the routed expert FFN built around the MoE expert
+shape) measured the same way as extra context.
 """
 from __future__ import annotations
 
@@ -104,6 +105,37 @@ class Dense:
         st = self.fn(*self.args[i % self.copies], stream)
         if st:
             raise RuntimeError(f"q4_matmul_ex failed with status {st}")
+
+
+class MxDense:
+    """The decode gate+up shape with 4-bit float block weights (e2m1
+    elements, one E8M0 byte per 32 k), weights rotated over copies."""
+
+    def __init__(self, torch, q4, copies=None):
+        import synthetic
+        c = synthetic.MX_CONFIGS["mx_decode_gate_up"]
+        self.M, self.N, self.K = c["M"], c["N"], c["K"]
+        d = synthetic.mx_case(c["seed"], self.M, self.N, self.K)
+        dev = "cuda:0"
+        wb = self.N * self.K // 2 + self.N * self.K // 32
+        n = copies or max(2, -(-ROTATE_BYTES // wb) + 1)
+        self.copies = n
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev)
+        wq = torch.from_numpy(d.w_q).to(dev)
+        we = torch.from_numpy(d.w_e).to(dev)
+        self.wq = [wq] + [wq.clone() for _ in range(n - 1)]
+        self.we = [we] + [we.clone() for _ in range(n - 1)]
+        self.y = torch.empty((self.M, self.N), device=dev, dtype=torch.float32)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_mx_matmul
+        self.args = [(P(self.x.data_ptr()), P(self.wq[i].data_ptr()), P(self.we[i].data_ptr()),
+                      P(self.y.data_ptr()), q4.Q4_F32, self.M, self.N, self.K) for i in range(n)]
+        self.wbytes = wb
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_mx_matmul failed with status {st}")
 
 
 class MoE:
@@ -428,6 +460,18 @@ def main():
                                 "weight_GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
             del w
             torch.cuda.empty_cache()
+        progress("mx_decode_gate_up: generating inputs")
+        w = MxDense(torch, q4)
+        progress("mx_decode_gate_up: timing")
+        _, ev = time_steps(torch, w, args.steps // 2, max(10, args.warmup // 2))
+        gbs = w.wbytes / (ev * 1e-3) / 1e9
+        others["mx_decode_gate_up"] = {"M": w.M, "N": w.N, "K": w.K,
+                                       "format": "e2m1 elements, E8M0 scale per 32",
+                                       "avg_launch_us": round(ev * 1e3, 2),
+                                       "weight_GB/s": round(gbs, 1),
+                                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del w
+        torch.cuda.empty_cache()
         progress("moe: generating inputs")
         w = MoE(torch, q4)
         progress("moe: timing")

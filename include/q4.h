@@ -69,7 +69,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 4
+#define Q4_ABI_VERSION 5
 
 /* Status codes. */
 #define Q4_OK            0
@@ -210,6 +210,27 @@ Q4_API int32_t q4_moe_ffn(const void *x, const void *w13_q, const void *w13_s,
                           const int32_t *topk_ids, const float *topk_w, float *y,
                           int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
                           void *workspace, size_t workspace_bytes, q4_stream_t stream);
+
+/* y = x . dequant(W)^T with 4-bit float block weights (ABI version 5): the
+ * 4-bit float block format that "spec: specialized model runtimes" (section
+ * "Target package and artifact") plans after groupwise-int weights, read as
+ * the public microscaling definition with 32-element blocks:
+ *   w[n][k] = e2m1(c[n][k]) * 2^(E[n][k/32] - 127)
+ * where an element c is bit 3 sign, bits 2..1 exponent (bias 1; 0 is
+ * subnormal: m * 2^-1), bit 0 mantissa, values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ * E is an E8M0 byte, E = 255 is NaN.
+ *   x    bf16  [M][K] device
+ *   w_q  uint8 [N][K/2] device, elements packed as the int4 codes (k = 2j in
+ *        the low nibble of byte j)
+ *   w_e  uint8 [N][K/32] device, E8M0 scale bytes
+ *   y    [M][N] device, fp32 (Q4_F32) or bf16 (Q4_BF16)
+ * Decode shapes only: 1 <= M <= 8 (M = 0 or N = 0 is a no-op, M > 8 is
+ * Q4_ERR_SHAPE); K a positive multiple of 32.  Every weight enters exactly;
+ * sums are fp32.  x, w_q, w_e and y must be 16-byte aligned.  Checks and
+ * error behaviour as for q4_matmul. */
+Q4_API int32_t q4_mx_matmul(const void *x, const void *w_q, const void *w_e,
+                            void *y, int32_t y_dtype,
+                            int64_t M, int64_t N, int64_t K, q4_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,11 +20,13 @@ of the C ABI in ``include/q4.h``:
     q4_moe_ffn_workspace_bytes(T, topk, E, H, F) -> int
     q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None,
                workspace=None, stream=None) -> y
+    q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=torch.float32, stream=None) -> y
 
 Tensor conventions (all CUDA/HIP device tensors, contiguous):
     x    torch.bfloat16 [M][K]       (or int16/uint16 holding bf16 bits)
     w_q  torch.uint8    [N][K/2]     (MoE: [E][N][K/2])
     w_s  torch.float16  [N][K/32]    (or int16/uint16 holding fp16 bits)
+    w_e  torch.uint8    [N][K/32]    (4-bit float blocks: E8M0 scale bytes)
 A non-zero status from the library raises ``Q4Error``.  If ``libq4.so`` is
 missing the import fails: there is no fallback implementation.
 """
@@ -36,7 +38,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 4
+Q4_ABI_VERSION = 5
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -54,7 +56,7 @@ Q4_PATH_SMALL = 2
 __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
-    "q4_moe_matmul", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn",
+    "q4_moe_matmul", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
 ]
 
 
@@ -94,6 +96,8 @@ def _open():
     L.q4_moe_ffn.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t,
                              P]
     L.q4_moe_ffn.restype = I32
+    L.q4_mx_matmul.argtypes = [P, P, P, P, I32, I64, I64, I64, P]
+    L.q4_mx_matmul.restype = I32
     if L.q4_abi_version() != Q4_ABI_VERSION:
         raise ImportError(f"libq4 ABI version {L.q4_abi_version()} != {Q4_ABI_VERSION}")
     return L
@@ -181,6 +185,31 @@ def q4_matmul(x, w_q, w_s, out=None, out_dtype=None, stream=None):
                        M, N, K, _stream_handle(stream, x.device))
     if st != Q4_OK:
         raise Q4Error(st, "q4_matmul")
+    return out
+
+
+def q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=None, stream=None):
+    """y[M][N] = x[M][K] . W^T with 4-bit float block weights: w = e2m1(code)
+    * 2^(E - 127), one E8M0 byte E per 32 k (fp32 or bf16 output, M <= 8)."""
+    torch = _torch()
+    _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _check_dev(w_q, "w_q", (torch.uint8,), 2)
+    _check_dev(w_e, "w_e", (torch.uint8,), 2)
+    M, K = x.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] * 2 != K or tuple(w_e.shape) != (N, K // 32):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_q {tuple(w_q.shape)}, "
+                         f"w_e {tuple(w_e.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    else:
+        _check_dev(out, "out", (torch.float32, torch.bfloat16), 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    st = lib.q4_mx_matmul(_ptr(x), _ptr(w_q), _ptr(w_e), _ptr(out), _out_code(out.dtype),
+                          M, N, K, _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_mx_matmul")
     return out
 
 

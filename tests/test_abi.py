@@ -49,7 +49,7 @@ def test_header_declares_the_abi():
     assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
                          "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
                          "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_ffn_workspace_bytes",
-                         "q4_moe_ffn"}
+                         "q4_moe_ffn", "q4_mx_matmul"}
 
 
 def test_every_declared_symbol_is_exported():
@@ -188,6 +188,33 @@ def test_matmul_without_gpu_is_device_error():
     need = q4.q4_matmul_workspace_bytes(2, 32, 17408)
     assert _mmx(L, A, need) == q4.Q4_ERR_DEVICE
     assert _mmx(L, 0, 0) == q4.Q4_ERR_DEVICE
+
+
+def _mx(L, x=A, wq=A, we=A, y=A, dt=0, M=1, N=64, K=256):
+    P = ctypes.c_void_p
+    L.q4_mx_matmul.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                               ctypes.c_int64, P]
+    L.q4_mx_matmul.restype = ctypes.c_int32
+    return L.q4_mx_matmul(P(x), P(wq), P(we), P(y), dt, M, N, K, P(0))
+
+
+def test_mx_matmul_argument_errors():
+    q4, L = _lib()
+    assert _mx(L, dt=2) == q4.Q4_ERR_DTYPE
+    assert _mx(L, K=0) == q4.Q4_ERR_SHAPE
+    assert _mx(L, K=48) == q4.Q4_ERR_SHAPE
+    assert _mx(L, N=-1) == q4.Q4_ERR_SHAPE
+    assert _mx(L, M=-1) == q4.Q4_ERR_SHAPE
+    assert _mx(L, M=9) == q4.Q4_ERR_SHAPE            # decode shapes only
+    assert _mx(L, dt=7, M=9) == q4.Q4_ERR_DTYPE       # dtype before shape
+    assert _mx(L, x=0, wq=0, we=0, y=0, M=0) == q4.Q4_OK
+    assert _mx(L, x=0, wq=0, we=0, y=0, N=0) == q4.Q4_OK
+    for kw in ("x", "wq", "we", "y"):
+        assert _mx(L, **{kw: 0}) == q4.Q4_ERR_NULL, kw
+        assert _mx(L, **{kw: MIS}) == q4.Q4_ERR_ALIGN, kw
+    if not _gpu_present():
+        assert _mx(L) == q4.Q4_ERR_DEVICE
+        assert _mx(L, M=8, dt=1) == q4.Q4_ERR_DEVICE
 
 
 def test_dequantize_argument_errors():

@@ -1,0 +1,94 @@
+"""GPU parity of the 4-bit float block product (q4_mx_matmul, through the C
+ABI) with the oracle: e2m1 elements, one E8M0 scale per 32 k.  Every weight
+enters exactly, so the bar is the matmul tolerance |y - y_ref| <= 1e-3 *
+sum_k |x_k w_k| per output (plus half a bf16 ulp of y_ref for bf16 outputs)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from helpers import RTOL, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+import quantized_q4_block_amd as q4  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def _mx(x, w_q, w_e, out_dtype=torch.float32):
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV)
+    y = q4.q4_mx_matmul(xd, torch.from_numpy(np.ascontiguousarray(w_q)).to(DEV),
+                        torch.from_numpy(np.ascontiguousarray(w_e)).to(DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def _check(c, what, out_dtype=torch.float32):
+    y = _mx(c.x, c.w_q, c.w_e, out_dtype)
+    y_ref, t = oracle.mx_matmul(c.x, c.w_q, c.w_e)
+    extra = 0.0 if out_dtype == torch.float32 else 2.0 ** -9 * np.abs(y_ref)
+    assert_parity(y, y_ref, t, RTOL, extra=extra, what=what)
+
+
+# M from 1 to 8; N with ragged task tails; K of one block to several stages,
+# with leftover stages split between the half-waves (<= 32 blocks) or not
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 64), (65, 2048 + 32 * 5), (300, 4096 + 32 * 40),
+                                 (131, 5120), (96, 17408)])
+def test_mx_parity_shapes(M, N, K):
+    c = synthetic.mx_case(9000 + 13 * M + N + K, M, N, K)
+    _check(c, f"mx M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_mx_bf16_output(M):
+    c = synthetic.mx_case(9100 + M, M, 200, 3072)
+    _check(c, f"mx bf16 M={M}", out_dtype=torch.bfloat16)
+
+
+def test_mx_full_decode_gate_up():
+    cfg = synthetic.MX_CONFIGS["mx_decode_gate_up"]
+    c = synthetic.mx_case(cfg["seed"], cfg["M"], cfg["N"], cfg["K"])
+    _check(c, "mx_decode_gate_up")
+
+
+def test_mx_scale_extremes_and_nan():
+    """E8M0 bytes 0 (2^-127, an fp32 subnormal), 254 and 255 (NaN)."""
+    c = synthetic.mx_case(9200, 2, 64, 512)
+    w_e = c.w_e.copy()
+    w_e[0::3, :] = 0
+    w_e[1::3, 0] = 254
+    xs = c.x.copy()
+    xs[:] = 0x3C00                     # 2^-7: keeps the 2^127 blocks finite
+    y = _mx(xs, c.w_q, w_e)
+    y_ref, t = oracle.mx_matmul(xs, c.w_q, w_e)
+    assert_parity(y, y_ref, t, RTOL, what="E8M0 extremes")
+    # a NaN scale poisons its row only (the other blocks keep ordinary scales)
+    w_e = c.w_e.copy()
+    w_e[5, 2] = 255
+    y = _mx(c.x, c.w_q, w_e)
+    assert np.all(np.isnan(y[:, 5]))
+    others = np.delete(np.arange(64), 5)
+    assert np.all(np.isfinite(y[:, others]))
+
+
+def test_mx_exact_zeros_and_closed_form():
+    K, N = 1024, 40
+    x = np.full((3, K), 0x3FC0, dtype=np.uint16)            # 1.5
+    w_q = np.full((N, K // 2), 0x08, dtype=np.uint8)        # +0, -0
+    w_e = np.full((N, K // 32), 127, dtype=np.uint8)
+    assert np.all(_mx(x, w_q, w_e) == 0)
+    w_q[:] = 0x77                                           # 6.0 everywhere
+    w_e[:] = 125                                            # 2^-2
+    assert np.all(_mx(x, w_q, w_e) == K * 1.5 * 6.0 * 0.25)
+
+
+def test_mx_deterministic():
+    c = synthetic.mx_case(9300, 1, 4096, 5120)
+    a = _mx(c.x, c.w_q, c.w_e)
+    b = _mx(c.x, c.w_q, c.w_e)
+    assert np.array_equal(a, b)
