@@ -165,6 +165,50 @@ __device__ __forceinline__ void block_rows_f32(const CodeUnpacker& unpack, const
   }
 }
 
+// 4-bit float blocks: acc[r][m] += s[r] * sum over one block of
+// x[m] * e2m1(c[r]), fp32 activations xv[m][k], k = 0..31 within the block,
+// s[r] the block's power of two as fp32.  Each byte of elements becomes two
+// exact fp32 values with one v_cvt_scalef32_pk_f32_fp4 (scale 1; the low
+// nibble is the first value).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+template <int M, int RR>
+__device__ __forceinline__ void mx_block_rows_f32(const uint4 (&c)[RR], const float (&s)[RR],
+                                                  const float (&xv)[M][32], float (&acc)[RR][M]) {
+#pragma unroll
+  for (int r = 0; r < RR; ++r) {
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t d = i == 0 ? c[r].x : i == 1 ? c[r].y : i == 2 ? c[r].z : c[r].w;
+      f32x2v w[4];
+      w[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+      w[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+      w[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+      w[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          part[m] = __builtin_fmaf(w[b][0], xv[m][8 * i + 2 * b], part[m]);
+          part[m] = __builtin_fmaf(w[b][1], xv[m][8 * i + 2 * b + 1], part[m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(s[r], part[m], acc[r][m]);
+  }
+}
+
+// E8M0 scale byte -> fp32 2^(E-127) (E = 0 is the fp32 subnormal 2^-127,
+// E = 255 is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  const uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23);
+  return __uint_as_float(bits);
+}
+
 // Leftover-stage epilogue (not split): contributions t, computed from raw
 // loads, are added only by lanes that own a leftover block.
 template <int M, int R>
@@ -323,29 +367,36 @@ struct XStagerF32 {
 // bounds); the caller discards their results.
 enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2 };
 
-template <int R, int FULL, int TAIL>
+// SC: how a block scale is held -- _Float16 (the int4 codes' fp16 scales) or
+// uint8_t (the E8M0 bytes of 4-bit float blocks).
+template <int R, int FULL, int TAIL, typename SC = _Float16>
 struct UpfrontLoads {
   static constexpr int TR = TAIL == kSplitTail ? R / 2 : (TAIL == kWideTail ? R : 0);
   uint4 c[FULL > 0 ? FULL : 1][R];
-  _Float16 s[FULL > 0 ? FULL : 1][R];
+  SC s[FULL > 0 ? FULL : 1][R];
   uint4 ct[TR > 0 ? TR : 1];
-  _Float16 st[TR > 0 ? TR : 1];
+  SC st[TR > 0 ? TR : 1];
 };
+
+__device__ __forceinline__ void load_scale(const uint16_t* p, _Float16& s) {
+  s = __builtin_bit_cast(_Float16, *p);
+}
+__device__ __forceinline__ void load_scale(const uint8_t* p, uint8_t& s) { s = *p; }
 
 // cbase / sbase: codes and scales of the task's first row at the first
 // block of the row piece; row_bytes / row_sc: distance between rows (bytes,
 // scales); room = rows that exist past the first (>= 0); rem = leftover
 // blocks of the piece.
-template <int R, int FULL, int TAIL>
-__device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL>& b,
+template <int R, int FULL, int TAIL, typename SC, typename SP>
+__device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL, SC>& b,
                                              const uint8_t* __restrict__ cbase,
-                                             const uint16_t* __restrict__ sbase,
+                                             const SP* __restrict__ sbase,
                                              uint32_t row_bytes, uint32_t row_sc, int room,
                                              int rem, int lane) {
-  auto load = [&](int row, uint32_t blk, uint4& c, _Float16& s) {
+  auto load = [&](int row, uint32_t blk, uint4& c, SC& s) {
     row = row < room ? row : room;
     c = *reinterpret_cast<const uint4*>(cbase + (uint32_t)row * row_bytes + blk * 16);
-    s = __builtin_bit_cast(_Float16, sbase[(uint32_t)row * row_sc + blk]);
+    load_scale(sbase + (uint32_t)row * row_sc + blk, s);
   };
 #pragma unroll
   for (int st = 0; st < FULL; ++st)
@@ -403,11 +454,13 @@ __host__ __device__ __forceinline__ int row_leftover(int64_t K) {
 }
 
 // Totals (wave-uniform) of the task loaded into b; xs is the LDS activation
-// table (fp32 layout above).
-template <int M, int R, int FULL, int TAIL>
-__device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL>& b,
+// table (fp32 layout above).  SC = uint8_t: 4-bit float blocks (e2m1
+// elements, E8M0 scales); else the int4 codes with fp16 scales.
+template <int M, int R, int FULL, int TAIL, typename SC = _Float16>
+__device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL, SC>& b,
                                                 const float4* xs, int rem, int lane,
                                                 float (&out)[R][M]) {
+  constexpr bool kMx = std::is_same<SC, uint8_t>::value;
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   const CodeUnpacker unpack;
   float acc[R][M];
@@ -429,7 +482,14 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
         xv[m][4 * q + 2] = v.z;
         xv[m][4 * q + 3] = v.w;
       }
-    block_rows_f32<M, RR>(unpack, c, s, xv, a);
+    if constexpr (kMx) {
+      float sf[RR];
+#pragma unroll
+      for (int r = 0; r < RR; ++r) sf[r] = e8m0_to_f32(s[r]);
+      mx_block_rows_f32<M, RR>(c, sf, xv, a);
+    } else {
+      block_rows_f32<M, RR>(unpack, c, s, xv, a);
+    }
   };
 #pragma unroll
   for (int st = 0; st < FULL; ++st) rows(st, lane, b.c[st], b.s[st], acc);
@@ -456,10 +516,25 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
     // past K) and gets scale 0, so it adds exactly zero whatever its
     // (clamped, real) codes and scale are.
     const bool ok = lane < rem;
-    _Float16 sc[R];
+    if constexpr (kMx) {
+      // E8M0 has no zero: take the lane's contribution away by selection
+      // (its clamped real scale may be NaN)
+      float t[R][M];
 #pragma unroll
-    for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (_Float16)0.0f;
-    rows(FULL, lane, b.ct, sc, acc);
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) t[r][m] = 0.0f;
+      rows(FULL, lane, b.ct, b.st, t);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] += ok ? t[r][m] : 0.0f;
+    } else {
+      _Float16 sc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (_Float16)0.0f;
+      rows(FULL, lane, b.ct, sc, acc);
+    }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)

@@ -10,8 +10,14 @@
 //
 // Work split as in the int4 matrix-vector kernel (q4_gemv.h): a task is R
 // rows per wavefront, lane l owns the blocks l, l+64, ... of every row, and a
-// leftover stage of at most 32 blocks is split between the half-waves.
-// Activations are read as bf16 through L1/L2, one stage ahead of the math.
+// leftover stage of at most 32 blocks is split between the half-waves.  Two
+// kernels, as for the int4 codes:
+//  * mx_lds_kernel (M <= 4, rows of at most 4 stages): 2 rows per wavefront,
+//    8 wavefronts per workgroup; every code and scale load of a task is
+//    issued up front and the workgroup stages the activations as fp32 in LDS
+//    while they are in flight;
+//  * mx_gemv_kernel (otherwise): activations read as bf16 through L1/L2, one
+//    stage ahead of the math.
 //
 // Arithmetic per byte of elements: one v_cvt_scalef32_pk_f32_fp4 (scale 1)
 // gives the two elements as exact fp32 values (at most 2 significant bits),
@@ -24,14 +30,6 @@
 namespace q4 {
 
 namespace {
-
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-
-// E8M0 byte -> fp32 2^(E-127) (E = 0 is the fp32 subnormal 2^-127; E = 255 NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  const uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23);
-  return __uint_as_float(bits);
-}
 
 // acc[r][m] += 2^(E_r - 127) * sum over one block of x[m] * e2m1(c[r]).
 template <int M, int RR>
@@ -188,9 +186,70 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_gemv_kernel(
     }
 }
 
+// Rows of FULL whole stages plus a leftover stage of kind TAIL, activations
+// staged in LDS (the int4 decode kernel's scheme with E8M0 scale bytes).
+template <int M, int FULL, int TAIL>
+__global__ __launch_bounds__(kLdsWaves * 64) void mx_lds_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ we, void* __restrict__ y, int y_bf16, int64_t N, int64_t K,
+    int rem) {
+  constexpr int R = kLdsRows;
+  constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
+  __shared__ float4 xs[M * S * 8 * kWave];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = ((int64_t)blockIdx.x * kLdsWaves + wave) * R;
+  const bool live = n0 < N;
+  const int64_t nl = live ? n0 : N - 1;
+  const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
+  const uint32_t row_bytes = (uint32_t)(K / 2), row_sc = (uint32_t)(K / kBlock);
+  XStager<M, S, kLdsWaves * 64> xst;
+  xst.load(x, K, K);
+  UpfrontLoads<R, FULL, TAIL, uint8_t> b;
+  upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes, we + nl * (int64_t)row_sc,
+                              row_bytes, row_sc, room, rem, lane);
+  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
+  xst.pin();
+  xst.store_f32(xs);
+  __syncthreads();
+  // a wavefront past the last row computes on clamped rows and stores nothing
+  float out[R][M];
+  upfront_compute<M, R, FULL, TAIL, uint8_t>(b, xs, rem, lane, out);
+  if (!live || lane != 0) return;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (n0 + r >= N) break;
+      if (y_bf16)
+        static_cast<uint16_t*>(y)[m * N + n0 + r] = to_bf16(out[r][m]);
+      else
+        static_cast<float*>(y)[m * N + n0 + r] = out[r][m];
+    }
+}
+
 template <int M>
 hipError_t launch_mx_m(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
                        bool y_bf16, int64_t N, int64_t K, hipStream_t stream) {
+  if constexpr (M <= 4) {
+    if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= 64 * 1024) {
+      const int rem = row_leftover(K);
+      const int64_t tasks = (N + kLdsRows - 1) / kLdsRows;
+      const int64_t grid = (tasks + kLdsWaves - 1) / kLdsWaves;
+      if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+      return dispatch_row_geometry(K, [&](auto full, auto tail) {
+        constexpr int FULL = decltype(full)::value, TAIL = decltype(tail)::value;
+        constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
+        if constexpr ((int64_t)M * S * 8 * kWave * 16 > 64 * 1024) {
+          return hipErrorInvalidValue;   // never chosen (checked above)
+        } else {
+          mx_lds_kernel<M, FULL, TAIL><<<dim3((unsigned)grid), dim3(kLdsWaves * 64), 0, stream>>>(
+              x, wq, we, y, y_bf16 ? 1 : 0, N, K, rem);
+          return hipGetLastError();
+        }
+      });
+    }
+  }
   constexpr int R = MxRows<M>::R;
   const int64_t tasks = (N + R - 1) / R;
   const int64_t grid = (tasks + kMxWaves - 1) / kMxWaves;
