@@ -368,7 +368,8 @@ def summarize_trace(run_dir):
                 continue
             with open(os.path.join(dirpath, fn), newline="") as f:
                 for row in csv.DictReader(f):
-                    name = row["Kernel_Name"].replace("void ", "").split("(")[0]
+                    name = row["Kernel_Name"].replace("void ", "")
+                    name = name.replace("(anonymous namespace)::", "").split("(")[0]
                     d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
                     durs.setdefault(name, []).append(d)
     out = {}

@@ -88,12 +88,12 @@ def test_summarize_trace_percentiles(tmp_path):
         for i in range(1, 11):
             w.writerow({"Kernel_Name": "void q4::a<1>(int)", "Start_Timestamp": 1000 * i,
                         "End_Timestamp": 1000 * i + 1000 * i})
-        w.writerow({"Kernel_Name": "q4::b(float*)", "Start_Timestamp": 0,
-                    "End_Timestamp": 100000})
+        w.writerow({"Kernel_Name": "void q4::(anonymous namespace)::b<2>(float*)",
+                    "Start_Timestamp": 0, "End_Timestamp": 100000})
     s = b.summarize_trace(str(tmp_path / "trace"))
-    assert list(s) == ["q4::b", "q4::a<1>"]          # by total time
+    assert list(s) == ["q4::b<2>", "q4::a<1>"]       # by total time
     a = s["q4::a<1>"]
     assert a["calls"] == 10 and a["mean_us"] == 5.5 and a["median_us"] == 5.5
     assert a["p10_us"] == 1.9 and a["p90_us"] == 9.1
     assert a["min_us"] == 1.0 and a["max_us"] == 10.0
-    assert s["q4::b"]["calls"] == 1 and s["q4::b"]["median_us"] == 100.0
+    assert s["q4::b<2>"]["calls"] == 1 and s["q4::b<2>"]["median_us"] == 100.0
