@@ -224,10 +224,12 @@ Q4_API int32_t q4_moe_ffn(const void *x, const void *w13_q, const void *w13_s,
  *        the low nibble of byte j)
  *   w_e  uint8 [N][K/32] device, E8M0 scale bytes
  *   y    [M][N] device, fp32 (Q4_F32) or bf16 (Q4_BF16)
- * Decode shapes only: 1 <= M <= 8 (M = 0 or N = 0 is a no-op, M > 8 is
- * Q4_ERR_SHAPE); K a positive multiple of 32.  Every weight enters exactly;
- * sums are fp32.  x, w_q, w_e and y must be 16-byte aligned.  Checks and
- * error behaviour as for q4_matmul. */
+ * M <= 2 takes the matrix-vector kernel; 3 <= M <= 65535 * 32 the few-row
+ * matrix-core kernel (e2m1 values are exact in bf16), in slabs of 32 rows.
+ * M = 0 or N = 0 is a no-op; a larger M is Q4_ERR_SHAPE; K must be a
+ * positive multiple of 32.  Every weight enters exactly; sums are fp32.  x,
+ * w_q, w_e and y must be 16-byte aligned.  Checks and error behaviour as for
+ * q4_matmul. */
 Q4_API int32_t q4_mx_matmul(const void *x, const void *w_q, const void *w_e,
                             void *y, int32_t y_dtype,
                             int64_t M, int64_t N, int64_t K, q4_stream_t stream);

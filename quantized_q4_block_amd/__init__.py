@@ -190,7 +190,7 @@ def q4_matmul(x, w_q, w_s, out=None, out_dtype=None, stream=None):
 
 def q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=None, stream=None):
     """y[M][N] = x[M][K] . W^T with 4-bit float block weights: w = e2m1(code)
-    * 2^(E - 127), one E8M0 byte E per 32 k (fp32 or bf16 output, M <= 8)."""
+    * 2^(E - 127), one E8M0 byte E per 32 k (fp32 or bf16 output)."""
     torch = _torch()
     _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
     _check_dev(w_q, "w_q", (torch.uint8,), 2)

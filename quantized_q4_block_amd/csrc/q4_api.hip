@@ -152,7 +152,8 @@ Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, voi
                             int32_t y_dtype, int64_t M, int64_t N, int64_t K,
                             q4_stream_t stream) {
   if (y_dtype != Q4_F32 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
-  if (M < 0 || M > 8) return Q4_ERR_SHAPE;
+  // from 3 rows on, slabs of 32 activation rows in the grid's y dimension
+  if (M < 0 || M > int64_t(65535) * 32) return Q4_ERR_SHAPE;
   if (int32_t s = check_weights(N, K)) return s;
   int64_t mk, mn;
   if (!mul_ok(M, K, &mk) || !mul_ok(M, N, &mn)) return Q4_ERR_SHAPE;
@@ -160,10 +161,13 @@ Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, voi
   if (!x || !w_q || !w_e || !y) return Q4_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_e) || !aligned16(y)) return Q4_ERR_ALIGN;
   if (int32_t s = check_device()) return s;
-  return launched(q4::launch_mx_gemv(static_cast<const uint16_t*>(x),
-                                     static_cast<const uint8_t*>(w_q),
-                                     static_cast<const uint8_t*>(w_e), y, y_dtype == Q4_BF16, M,
-                                     N, K, static_cast<hipStream_t>(stream)));
+  const auto* xp = static_cast<const uint16_t*>(x);
+  const auto* wp = static_cast<const uint8_t*>(w_q);
+  const auto* ep = static_cast<const uint8_t*>(w_e);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = y_dtype == Q4_BF16;
+  if (M <= kGemvMaxRows) return launched(q4::launch_mx_gemv(xp, wp, ep, y, bf16, M, N, K, st));
+  return launched(q4::launch_small_mx(xp, wp, ep, y, bf16, M, N, K, st));
 }
 
 Q4_API int32_t q4_dequantize(const void* w_q, const void* w_s, void* w_out, int32_t out_dtype,

@@ -78,6 +78,16 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
+// 4-bit float blocks (e2m1 elements, one E8M0 scale byte per 32 k).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// E8M0 scale byte -> fp32 2^(E-127) (E = 0 is the fp32 subnormal 2^-127,
+// E = 255 is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  const uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23);
+  return __uint_as_float(bits);
+}
+
 // Sum over the 64 lanes of a wavefront; every lane gets the total.  The
 // butterfly order is fixed, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -170,8 +170,6 @@ __device__ __forceinline__ void block_rows_f32(const CodeUnpacker& unpack, const
 // s[r] the block's power of two as fp32.  Each byte of elements becomes two
 // exact fp32 values with one v_cvt_scalef32_pk_f32_fp4 (scale 1; the low
 // nibble is the first value).
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-
 template <int M, int RR>
 __device__ __forceinline__ void mx_block_rows_f32(const uint4 (&c)[RR], const float (&s)[RR],
                                                   const float (&xv)[M][32], float (&acc)[RR][M]) {
@@ -200,13 +198,6 @@ __device__ __forceinline__ void mx_block_rows_f32(const uint4 (&c)[RR], const fl
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(s[r], part[m], acc[r][m]);
   }
-}
-
-// E8M0 scale byte -> fp32 2^(E-127) (E = 0 is the fp32 subnormal 2^-127,
-// E = 255 is NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  const uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23);
-  return __uint_as_float(bits);
 }
 
 // Leftover-stage epilogue (not split): contributions t, computed from raw

@@ -27,10 +27,15 @@ int64_t gemv_split_slices(int64_t M, int64_t K);
 hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                         bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
-// 4-bit float block weights (e2m1 elements, E8M0 scales), 1 <= M <= 8:
-// fused dequant + matrix-vector product, exact weights.
+// 4-bit float block weights (e2m1 elements, E8M0 scales), M <= 2: fused
+// dequant + matrix-vector product, exact weights.
 hipError_t launch_mx_gemv(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
                           bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// 4-bit float block weights, M >= 3 (at most 65535 slabs of 32): the few-row
+// matrix-core kernel with e2m1 elements in bf16 and E8M0 block scales.
+hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
+                           bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // Many rows: dequant to bf16 in LDS + bf16 MFMA tiles (weights rounded to bf16).
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,

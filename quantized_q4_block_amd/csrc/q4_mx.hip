@@ -1,5 +1,6 @@
 // q4_mx.hip -- 4-bit float block weights (e2m1 elements, one E8M0 scale per
-// 32 k): fused dequant + matrix-vector product for decode (1 <= M <= 8).
+// 32 k): fused dequant + matrix-vector product for decode (M <= 2; from 3
+// rows on q4_small.hip's matrix-core kernel takes the format).
 //
 // The specialised-runtime spec ("spec: specialized model runtimes", section
 // "Target package and artifact") plans a 4-bit float block format after the
@@ -16,8 +17,8 @@
 //    8 wavefronts per workgroup; every code and scale load of a task is
 //    issued up front and the workgroup stages the activations as fp32 in LDS
 //    while they are in flight;
-//  * mx_gemv_kernel (otherwise): activations read as bf16 through L1/L2, one
-//    stage ahead of the math.
+//  * mx_gemv_kernel (longer rows): activations read as bf16 through L1/L2,
+//    one stage ahead of the math.
 //
 // Arithmetic per byte of elements: one v_cvt_scalef32_pk_f32_fp4 (scale 1)
 // gives the two elements as exact fp32 values (at most 2 significant bits),
@@ -266,12 +267,6 @@ hipError_t launch_mx_gemv(const uint16_t* x, const uint8_t* wq, const uint8_t* w
   switch (M) {
     case 1: return launch_mx_m<1>(x, wq, we, y, y_bf16, N, K, stream);
     case 2: return launch_mx_m<2>(x, wq, we, y, y_bf16, N, K, stream);
-    case 3: return launch_mx_m<3>(x, wq, we, y, y_bf16, N, K, stream);
-    case 4: return launch_mx_m<4>(x, wq, we, y, y_bf16, N, K, stream);
-    case 5: return launch_mx_m<5>(x, wq, we, y, y_bf16, N, K, stream);
-    case 6: return launch_mx_m<6>(x, wq, we, y, y_bf16, N, K, stream);
-    case 7: return launch_mx_m<7>(x, wq, we, y, y_bf16, N, K, stream);
-    case 8: return launch_mx_m<8>(x, wq, we, y, y_bf16, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -29,11 +29,20 @@
 // 4 x 4 transpose across the lane groups (v_permlane16_swap and
 // v_permlane32_swap) then gives lane (r, g) dword g of blocks b0 .. b0 + 3.
 //
+// 4-bit float blocks (MX = true: e2m1 elements, E8M0 scale bytes) take the
+// same kernel: e2m1 values are exact in bf16 too (at most 2 significant bits),
+// so each byte of elements becomes two exact fp32 values with
+// v_cvt_scalef32_pk_f32_fp4 (scale 1) and one v_cvt_pk_bf16_f32, and the
+// block's 2^(E-127) is applied in fp32 where the int4 path applies its fp16
+// scale.
+//
 // Work split: a workgroup of kWaves wavefronts owns kNg * 16 weight rows and
 // one slab of 16 * MG activation rows; its wavefronts take consecutive
 // stretches of the row's 4-block groups, each keeping two groups of loads in
 // flight, and their partial sums are added in wavefront order through LDS
 // (deterministic).
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -60,6 +69,20 @@ __device__ __forceinline__ bf16x8v codes_to_bf16(uint32_t d, const CodeUnpacker&
   return __builtin_bit_cast(bf16x8v, o);
 }
 
+// bf16 elements of the 8 e2m1 values of d, in k order (exact).
+__device__ __forceinline__ bf16x8v fp4_to_bf16(uint32_t d) {
+  const f32x2v w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+  const f32x2v w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+  const f32x2v w2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+  const f32x2v w3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+  u32x4 o;
+  o[0] = pack_bf16x2(w0[0], w0[1]);
+  o[1] = pack_bf16x2(w1[0], w1[1]);
+  o[2] = pack_bf16x2(w2[0], w2[1]);
+  o[3] = pack_bf16x2(w3[0], w3[1]);
+  return __builtin_bit_cast(bf16x8v, o);
+}
+
 // Before: register j of lane group g (16 lanes) holds E[g][j].
 // After:  register j of lane group g holds E[j][g].
 __device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
@@ -76,12 +99,16 @@ __device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
 }  // namespace
 
 // SCALE4: K/32 is a multiple of 4, so a row's 4 scales of a group are one
-// aligned 8-byte load.
-template <int MG, bool SCALE4>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void small_kernel(
+// aligned load (8 bytes of fp16, or 4 E8M0 bytes).
+// MX: 4-bit float blocks (scales are E8M0 bytes); else int4 codes with fp16
+// scales.
+template <int MG, bool SCALE4, bool MX>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 4 : 2))) void small_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
-    const uint16_t* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
+    const void* __restrict__ wsv, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
     int64_t K, int64_t groups_per_wave) {
+  using ScaleT = typename std::conditional<MX, uint8_t, uint16_t>::type;
+  const ScaleT* ws = static_cast<const ScaleT*>(wsv);
   __shared__ f32x4v red[kWaves][kNg][MG][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -91,7 +118,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MG);
   // Rows past N (M) read row N-1 (M-1); their outputs are not stored.
   const uint8_t* wrow[kNg];
-  const uint16_t* srow[kNg];
+  const ScaleT* srow[kNg];
 #pragma unroll
   for (int ng = 0; ng < kNg; ++ng) {
     const int64_t n = n0 + ng * 16 + r;
@@ -131,7 +158,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       codes[d][ng][1] = v[1];
       codes[d][ng][2] = v[2];
       codes[d][ng][3] = v[3];
-      if constexpr (SCALE4) {
+      if constexpr (MX) {
+        if constexpr (SCALE4) {
+          const uint32_t s = *reinterpret_cast<const uint32_t*>(srow[ng] + b0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) scale[d][ng][j] = e8m0_to_f32((s >> (8 * j)) & 0xFFu);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            scale[d][ng][j] = e8m0_to_f32(srow[ng][b0 + j < bpr ? b0 + j : bpr - 1]);
+        }
+      } else if constexpr (SCALE4) {
         const u32x2 s = *reinterpret_cast<const u32x2*>(srow[ng] + b0);
         scale[d][ng][0] = fp16_to_f32((uint16_t)(s[0] & 0xFFFFu));
         scale[d][ng][1] = fp16_to_f32((uint16_t)(s[0] >> 16));
@@ -155,7 +192,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     constexpr int d = decltype(slot)::value;
 #pragma unroll
     for (int ng = 0; ng < kNg; ++ng) {
-      const bf16x8v w = codes_to_bf16(codes[d][ng][j], unpack);
+      const bf16x8v w = MX ? fp4_to_bf16(codes[d][ng][j]) : codes_to_bf16(codes[d][ng][j], unpack);
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) {
         const f32x4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[d][j][mg], w, zero, 0, 0, 0);
@@ -218,8 +255,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 
 namespace {
 
-template <int MG>
-hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
+template <int MG, bool MX>
+hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const void* ws, void* y,
                      bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t bpr = K / 32, groups = (bpr + 3) / 4;
   int64_t gpw = (groups + kWaves - 1) / kWaves;
@@ -228,11 +265,11 @@ hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, v
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)gy);
   if (bpr % 4 == 0)
-    small_kernel<MG, true><<<grid, dim3(kWaves * 64), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0,
-                                                                    M, N, K, gpw);
+    small_kernel<MG, true, MX><<<grid, dim3(kWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw);
   else
-    small_kernel<MG, false><<<grid, dim3(kWaves * 64), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0,
-                                                                     M, N, K, gpw);
+    small_kernel<MG, false, MX><<<grid, dim3(kWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw);
   return hipGetLastError();
 }
 
@@ -240,8 +277,14 @@ hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, v
 
 hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                         bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (M <= 16) return launch_mg<1>(x, wq, ws, y, y_bf16, M, N, K, stream);
-  return launch_mg<2>(x, wq, ws, y, y_bf16, M, N, K, stream);
+  if (M <= 16) return launch_mg<1, false>(x, wq, ws, y, y_bf16, M, N, K, stream);
+  return launch_mg<2, false>(x, wq, ws, y, y_bf16, M, N, K, stream);
+}
+
+hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
+                           bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M <= 16) return launch_mg<1, true>(x, wq, we, y, y_bf16, M, N, K, stream);
+  return launch_mg<2, true>(x, wq, we, y, y_bf16, M, N, K, stream);
 }
 
 }  // namespace q4

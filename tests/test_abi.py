@@ -205,8 +205,8 @@ def test_mx_matmul_argument_errors():
     assert _mx(L, K=48) == q4.Q4_ERR_SHAPE
     assert _mx(L, N=-1) == q4.Q4_ERR_SHAPE
     assert _mx(L, M=-1) == q4.Q4_ERR_SHAPE
-    assert _mx(L, M=9) == q4.Q4_ERR_SHAPE            # decode shapes only
-    assert _mx(L, dt=7, M=9) == q4.Q4_ERR_DTYPE       # dtype before shape
+    assert _mx(L, M=65535 * 32 + 1) == q4.Q4_ERR_SHAPE   # past the slab limit
+    assert _mx(L, dt=7, M=-1) == q4.Q4_ERR_DTYPE      # dtype before shape
     assert _mx(L, x=0, wq=0, we=0, y=0, M=0) == q4.Q4_OK
     assert _mx(L, x=0, wq=0, we=0, y=0, N=0) == q4.Q4_OK
     for kw in ("x", "wq", "we", "y"):
@@ -214,7 +214,7 @@ def test_mx_matmul_argument_errors():
         assert _mx(L, **{kw: MIS}) == q4.Q4_ERR_ALIGN, kw
     if not _gpu_present():
         assert _mx(L) == q4.Q4_ERR_DEVICE
-        assert _mx(L, M=8, dt=1) == q4.Q4_ERR_DEVICE
+        assert _mx(L, M=64, dt=1) == q4.Q4_ERR_DEVICE
 
 
 def test_dequantize_argument_errors():

@@ -44,7 +44,15 @@ def test_mx_parity_shapes(M, N, K):
     _check(c, f"mx M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 5])
+# from 3 rows on: the few-row matrix-core kernel, one or more slabs of 32 rows
+@pytest.mark.parametrize("M", [3, 5, 16, 17, 33, 70])
+@pytest.mark.parametrize("N,K", [(40, 96), (130, 2048 + 32 * 3), (512, 5120)])
+def test_mx_few_rows(M, N, K):
+    c = synthetic.mx_case(9400 + M + N + K, M, N, K)
+    _check(c, f"mx few-row M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 5, 40])
 def test_mx_bf16_output(M):
     c = synthetic.mx_case(9100 + M, M, 200, 3072)
     _check(c, f"mx bf16 M={M}", out_dtype=torch.bfloat16)
@@ -59,6 +67,11 @@ def test_mx_full_decode_gate_up():
 def test_mx_scale_extremes_and_nan():
     """E8M0 bytes 0 (2^-127, an fp32 subnormal), 254 and 255 (NaN)."""
     c = synthetic.mx_case(9200, 2, 64, 512)
+    _extremes(c)
+    _extremes(synthetic.mx_case(9201, 7, 64, 512))        # few-row path
+
+
+def _extremes(c):
     w_e = c.w_e.copy()
     w_e[0::3, :] = 0
     w_e[1::3, 0] = 254
