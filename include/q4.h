@@ -224,8 +224,11 @@ Q4_API int32_t q4_moe_ffn(const void *x, const void *w13_q, const void *w13_s,
  *        the low nibble of byte j)
  *   w_e  uint8 [N][K/32] device, E8M0 scale bytes
  *   y    [M][N] device, fp32 (Q4_F32) or bf16 (Q4_BF16)
- * M <= 2 takes the matrix-vector kernel; 3 <= M <= 65535 * 32 the few-row
- * matrix-core kernel (e2m1 values are exact in bf16), in slabs of 32 rows.
+ * M <= 2 takes the matrix-vector kernel.  Where q4_matmul_path(M, N, K) is
+ * Q4_PATH_MFMA and K is a multiple of 64, the tiled matrix-core kernel runs,
+ * with e2m1 * 2^(E - 129) exact in bf16 and the fp32 sums times 4; otherwise
+ * (3 <= M <= 65535 * 32) the few-row matrix-core kernel, in slabs of 32 rows
+ * (e2m1 values exact in bf16, scales applied in fp32).
  * M = 0 or N = 0 is a no-op; a larger M is Q4_ERR_SHAPE; K must be a
  * positive multiple of 32.  Every weight enters exactly; sums are fp32.  x,
  * w_q, w_e and y must be 16-byte aligned.  Checks and error behaviour as for

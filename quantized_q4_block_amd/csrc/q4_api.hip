@@ -167,6 +167,9 @@ Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = y_dtype == Q4_BF16;
   if (M <= kGemvMaxRows) return launched(q4::launch_mx_gemv(xp, wp, ep, y, bf16, M, N, K, st));
+  // the tiled kernel stages 64 k per step; other K stay on the few-row slabs
+  if (q4_matmul_path(M, N, K) == Q4_PATH_MFMA && K % 64 == 0)
+    return launched(q4::launch_gemm_mx(xp, wp, ep, y, bf16, M, N, K, st));
   return launched(q4::launch_small_mx(xp, wp, ep, y, bf16, M, N, K, st));
 }
 

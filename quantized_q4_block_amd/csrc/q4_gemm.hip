@@ -23,6 +23,8 @@
 // padded by 8 bf16 so the 128-bit fragment reads of 8 consecutive rows fall
 // in distinct banks.  Workgroups are numbered so that the workgroups sharing
 // one weight tile land on the same XCD (same L2).
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -201,12 +203,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+//
+// MX: 4-bit float blocks (e2m1 elements, one E8M0 byte E per 32 k).  The tile
+// holds e2m1 * 2^(E-129) in bf16, exact for every E < 255 (at most 1.5*2^127,
+// at least 2^-130, a bf16 subnormal), and the accumulators are multiplied by 4
+// before the store, an exact power-of-two step.  For E >= 2 the scaled fp4 ->
+// bf16 conversion does it in one instruction; that instruction reads its
+// scale as a power of two from the fp32 exponent field, so 2^-129 and 2^-128
+// (fp32 subnormals) would come out as 2^-127, and those two E take an fp32
+// multiply instead.
+template <bool MX>
 __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __restrict__ x,
                                                 const uint8_t* __restrict__ wq,
-                                                const uint16_t* __restrict__ ws,
+                                                const void* __restrict__ wsv,
                                                 void* __restrict__ y, int y_bf16,
                                                 int64_t M, int64_t N, int64_t K,
                                                 int tiles_m, int tiles_n) {
+  using ScaleT = typename std::conditional<MX, uint8_t, uint16_t>::type;
+  const ScaleT* __restrict__ ws = static_cast<const ScaleT*>(wsv);
   __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * 64];
   const int total = tiles_m * tiles_n;
@@ -246,17 +260,50 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
   const int64_t bn = n0 + srow;
   const bool b_ok = bn < N;
   const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
-  const uint16_t* s_src = ws + (b_ok ? bn : 0) * bpr;
+  const ScaleT* s_src = ws + (b_ok ? bn : 0) * bpr;
   const CodeUnpacker unpack;
   uint4 b_codes;
   float b_scale;
+  uint32_t b_e;
   auto load_b = [&](int64_t k0) __attribute__((always_inline)) {
     const int64_t blk = k0 / 32 + shalf;
     b_codes = *reinterpret_cast<const uint4*>(b_src + blk * 16);
-    b_scale = b_ok ? fp16_to_f32(s_src[blk]) : 0.0f;
+    if constexpr (MX) b_e = s_src[blk];   // columns past N are never stored
+    else b_scale = b_ok ? fp16_to_f32(s_src[blk]) : 0.0f;
   };
   auto store_b = [&]() __attribute__((always_inline)) {
     const uint32_t dw[4] = {b_codes.x, b_codes.y, b_codes.z, b_codes.w};
+    if constexpr (MX) {
+      // byte j of a dword holds elements 2j (low nibble) and 2j + 1
+      if (b_e >= 2) {
+        const float s = __uint_as_float(b_e == 255 ? 0x7FC00000u : (b_e - 2) << 23);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 o;
+          o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw[i], s, 0));
+          o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw[i], s, 1));
+          o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw[i], s, 2));
+          o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw[i], s, 3));
+          *reinterpret_cast<u32x4*>(&Bs[swz(srow, shalf * 4 + i) * 8]) = o;
+        }
+      } else {
+        const float s = __uint_as_float(0x00100000u << b_e);   // 2^-129 or 2^-128
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dw[i], 1.0f, 0);
+          const f32x2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dw[i], 1.0f, 1);
+          const f32x2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dw[i], 1.0f, 2);
+          const f32x2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dw[i], 1.0f, 3);
+          u32x4 o;
+          o[0] = pack_bf16x2(v0[0] * s, v0[1] * s);
+          o[1] = pack_bf16x2(v1[0] * s, v1[1] * s);
+          o[2] = pack_bf16x2(v2[0] * s, v2[1] * s);
+          o[3] = pack_bf16x2(v3[0] * s, v3[1] * s);
+          *reinterpret_cast<u32x4*>(&Bs[swz(srow, shalf * 4 + i) * 8]) = o;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2v p[4];
@@ -312,6 +359,12 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
     __builtin_amdgcn_s_waitcnt(0);   // next activation tile landed in LDS
     __syncthreads();
   }
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] *= 4.0f;
+  }
   const int col = lane & 31, rbase = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -336,11 +389,21 @@ hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
   const int64_t tn = (N + BN - 1) / BN;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (K % BK == 0)
-    gemm_dma_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+    gemm_dma_kernel<false><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
   else
     gemm_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
+                          bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t tm = (M + BM - 1) / BM;
+  const int64_t tn = (N + BN - 1) / BN;
+  if (tm * tn > 0x7FFFFFFF || K % BK != 0) return hipErrorInvalidValue;
+  gemm_dma_kernel<true><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
+      x, wq, we, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
   return hipGetLastError();
 }
 

@@ -37,6 +37,11 @@ hipError_t launch_mx_gemv(const uint16_t* x, const uint8_t* wq, const uint8_t* w
 hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
                            bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// 4-bit float block weights, many rows, K a multiple of 64: e2m1 * 2^(E-129)
+// exact in bf16 in LDS + bf16 MFMA tiles, accumulators times 4; exact weights.
+hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
+                          bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // Many rows: dequant to bf16 in LDS + bf16 MFMA tiles (weights rounded to bf16).
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);

@@ -194,7 +194,8 @@ def mx_case(seed: int, M: int, N: int, K: int, e_lo: int = 118, e_hi: int = 122)
     return MXCase(x=x, w_q=w_q, w_e=w_e)
 
 
-# The decode gate+up shape with 4-bit float block weights.
+# The decode gate+up and prefill shapes with 4-bit float block weights.
 MX_CONFIGS = {
     "mx_decode_gate_up": dict(kind="mx", M=1, K=5120, N=34816, seed=6, out="f32"),
+    "mx_prefill":        dict(kind="mx", M=512, K=5120, N=34816, seed=7, out="bf16"),
 }

@@ -58,6 +58,32 @@ def test_mx_bf16_output(M):
     _check(c, f"mx bf16 M={M}", out_dtype=torch.bfloat16)
 
 
+# many rows with K a multiple of 64: the tiled matrix-core kernel (128 x 128
+# tiles, ragged in M and N); K = 96 and 2080 keep the few-row slabs
+@pytest.mark.parametrize("M,N,K", [(129, 130, 64), (200, 300, 2048 + 64), (256, 256, 5120),
+                                   (1000, 72, 1024), (150, 100, 96), (300, 50, 2080)])
+def test_mx_tiled(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    c = synthetic.mx_case(9500 + M + N + K, M, N, K)
+    _check(c, f"mx tiled M={M} N={N} K={K}")
+    _check(c, f"mx tiled bf16 M={M} N={N} K={K}", out_dtype=torch.bfloat16)
+
+
+def test_mx_full_prefill_sampled():
+    """The prefill shape (512 x 34816 x 5120, bf16 out) on the tiled kernel;
+    the oracle takes 40 sampled rows against 384 sampled columns."""
+    cfg = synthetic.MX_CONFIGS["mx_prefill"]
+    c = synthetic.mx_case(cfg["seed"], cfg["M"], cfg["N"], cfg["K"])
+    y = _mx(c.x, c.w_q, c.w_e, torch.bfloat16)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(77)
+    ms = np.unique(np.concatenate([rng.integers(0, cfg["M"], 38), [0, cfg["M"] - 1]]))
+    ns = np.unique(np.concatenate([rng.integers(0, cfg["N"], 382), [0, cfg["N"] - 1]]))
+    y_ref, t = oracle.mx_matmul(c.x[ms], c.w_q[ns], c.w_e[ns])
+    assert_parity(y[np.ix_(ms, ns)], y_ref, t, RTOL, extra=2.0 ** -9 * np.abs(y_ref),
+                  what="mx_prefill sampled")
+
+
 def test_mx_full_decode_gate_up():
     cfg = synthetic.MX_CONFIGS["mx_decode_gate_up"]
     c = synthetic.mx_case(cfg["seed"], cfg["M"], cfg["N"], cfg["K"])
@@ -69,6 +95,7 @@ def test_mx_scale_extremes_and_nan():
     c = synthetic.mx_case(9200, 2, 64, 512)
     _extremes(c)
     _extremes(synthetic.mx_case(9201, 7, 64, 512))        # few-row path
+    _extremes(synthetic.mx_case(9202, 200, 64, 512))      # tiled path
 
 
 def _extremes(c):
@@ -85,7 +112,7 @@ def _extremes(c):
     w_e[5, 2] = 255
     y = _mx(c.x, c.w_q, w_e)
     assert np.all(np.isnan(y[:, 5]))
-    others = np.delete(np.arange(64), 5)
+    others = np.delete(np.arange(w_e.shape[0]), 5)
     assert np.all(np.isfinite(y[:, others]))
 
 
