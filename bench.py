@@ -108,12 +108,12 @@ class Dense:
 
 
 class MxDense:
-    """The decode gate+up shape with 4-bit float block weights (e2m1
-    elements, one E8M0 byte per 32 k), weights rotated over copies."""
+    """A dense shape with 4-bit float block weights (e2m1 elements, one E8M0
+    byte per 32 k), weights rotated over copies."""
 
-    def __init__(self, torch, q4, copies=None):
+    def __init__(self, torch, q4, name="mx_decode_gate_up", copies=None):
         import synthetic
-        c = synthetic.MX_CONFIGS["mx_decode_gate_up"]
+        c = synthetic.MX_CONFIGS[name]
         self.M, self.N, self.K = c["M"], c["N"], c["K"]
         d = synthetic.mx_case(c["seed"], self.M, self.N, self.K)
         dev = "cuda:0"
@@ -125,12 +125,16 @@ class MxDense:
         we = torch.from_numpy(d.w_e).to(dev)
         self.wq = [wq] + [wq.clone() for _ in range(n - 1)]
         self.we = [we] + [we.clone() for _ in range(n - 1)]
-        self.y = torch.empty((self.M, self.N), device=dev, dtype=torch.float32)
+        bf16 = c["out"] == "bf16"
+        self.y = torch.empty((self.M, self.N), device=dev,
+                             dtype=torch.bfloat16 if bf16 else torch.float32)
         P = ctypes.c_void_p
         self.fn = q4.lib.q4_mx_matmul
         self.args = [(P(self.x.data_ptr()), P(self.wq[i].data_ptr()), P(self.we[i].data_ptr()),
-                      P(self.y.data_ptr()), q4.Q4_F32, self.M, self.N, self.K) for i in range(n)]
+                      P(self.y.data_ptr()), q4.Q4_BF16 if bf16 else q4.Q4_F32,
+                      self.M, self.N, self.K) for i in range(n)]
         self.wbytes = wb
+        self.flops = 2.0 * self.M * self.N * self.K
 
     def step(self, i, stream):
         st = self.fn(*self.args[i % self.copies], stream)
@@ -471,6 +475,17 @@ def main():
                                        "avg_launch_us": round(ev * 1e3, 2),
                                        "weight_GB/s": round(gbs, 1),
                                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del w
+        torch.cuda.empty_cache()
+        progress("mx_prefill: generating inputs")
+        w = MxDense(torch, q4, "mx_prefill")
+        progress("mx_prefill: timing")
+        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+        tf = w.flops / (ev * 1e-3) / 1e12
+        others["mx_prefill"] = {"M": w.M, "N": w.N, "K": w.K,
+                                "format": "e2m1 elements, E8M0 scale per 32",
+                                "avg_launch_us": round(ev * 1e3, 2), "TFLOP/s": round(tf, 2),
+                                "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
         del w
         torch.cuda.empty_cache()
         progress("moe: generating inputs")

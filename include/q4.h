@@ -124,9 +124,12 @@ Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
                          int64_t M, int64_t N, int64_t K, q4_stream_t stream);
 
 /* Device workspace (bytes) that lets q4_matmul_ex cut long rows into
- * slices (Q4_PATH_GEMV shapes with K above 8192 or activations too large
- * for one workgroup's LDS): slices * M * N fp32 partial sums.  0 when the call
- * needs none, or for sizes q4_matmul would reject. */
+ * slices: slices * M * N fp32 partial sums.  Q4_PATH_GEMV shapes are cut when
+ * K is above 8192 or the activations are too large for one workgroup's LDS;
+ * Q4_PATH_MFMA shapes with K a multiple of 64 when their grid has fewer than
+ * 512 tiles of 128 x 128 outputs (at most 768 / tiles and 64 slices, each of
+ * at least 8 steps of 64 k).  0 when the call needs none, or for sizes
+ * q4_matmul would reject. */
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* q4_matmul with an optional workspace.  workspace == NULL: exactly

@@ -105,8 +105,15 @@ Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K) {
 
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 0;
-  if (q4_matmul_path(M, N, K) != Q4_PATH_GEMV) return 0;
-  const int64_t slices = q4::gemv_split_slices(M, K);
+  const int32_t path = q4_matmul_path(M, N, K);
+  if (path == Q4_PATH_SMALL) return 0;
+  int64_t slices;   // 0: the call never cuts its rows
+  if (path == Q4_PATH_GEMV) {
+    slices = q4::gemv_split_slices(M, K);
+  } else {
+    slices = q4::gemm_split_slices(M, N, K);
+    if (slices == 1) slices = 0;
+  }
   int64_t mn, total;
   if (slices == 0 || !mul_ok(M, N, &mn) || !mul_ok(mn, slices * 4, &total)) return 0;
   return (size_t)total;
@@ -138,7 +145,7 @@ Q4_API int32_t q4_matmul_ex(const void* x, const void* w_q, const void* w_s, voi
   switch (q4_matmul_path(M, N, K)) {
     case Q4_PATH_GEMV: return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, partial, st));
     case Q4_PATH_SMALL: return launched(q4::launch_small(xp, wp, sp, y, bf16, M, N, K, st));
-    default: return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, st));
+    default: return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, partial, st));
   }
 }
 

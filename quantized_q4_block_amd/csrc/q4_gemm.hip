@@ -218,14 +218,20 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
                                                 const void* __restrict__ wsv,
                                                 void* __restrict__ y, int y_bf16,
                                                 int64_t M, int64_t N, int64_t K,
-                                                int tiles_m, int tiles_n) {
+                                                int tiles_m, int tiles_n, int kt_slice,
+                                                float* __restrict__ partial) {
   using ScaleT = typename std::conditional<MX, uint8_t, uint16_t>::type;
-  const ScaleT* __restrict__ ws = static_cast<const ScaleT*>(wsv);
   __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * 64];
   const int total = tiles_m * tiles_n;
-  int c = blockIdx.x;
+  // workgroup b: K slice b / total (its kt_slice K steps), tile b % total
+  const int slice = (int)(blockIdx.x / (unsigned)total);
+  int c = (int)blockIdx.x - slice * total;
   if (total % 8 == 0) c = (c % 8) * (total / 8) + c / 8;
+  const int64_t kbeg = (int64_t)slice * kt_slice * 64;
+  const int64_t nk = K / 64 - kbeg / 64 < kt_slice ? K / 64 - kbeg / 64 : kt_slice;
+  if (nk <= 0) return;   // the launcher makes no empty slice
+  const ScaleT* __restrict__ ws = static_cast<const ScaleT*>(wsv) + kbeg / 32;
   const int tile_n = c / tiles_m, tile_m = c % tiles_m;
   const int64_t m0 = (int64_t)tile_m * 128, n0 = (int64_t)tile_n * 128;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
     const int p = (wave * 4 + j) * 64 + lane;
     const int r = p >> 3, cl = (p & 7) ^ ((r >> 1) & 7);
     const int64_t m = m0 + r < M ? m0 + r : M - 1;
-    a_src[j] = x + m * K + cl * 8;
+    a_src[j] = x + m * K + kbeg + cl * 8;
   }
   auto dma = [&](int buf, int64_t k0) __attribute__((always_inline)) {
 #pragma unroll
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
   const int shalf = sl & 1;
   const int64_t bn = n0 + srow;
   const bool b_ok = bn < N;
-  const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
+  const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2) + kbeg / 2;
   const ScaleT* s_src = ws + (b_ok ? bn : 0) * bpr;
   const CodeUnpacker unpack;
   uint4 b_codes;
@@ -323,7 +329,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  const int64_t nk = K / 64;
   dma(0, 0);
   load_b(0);
   store_b();
@@ -366,6 +371,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
       for (int j = 0; j < 2; ++j) acc[i][j] *= 4.0f;
   }
   const int col = lane & 31, rbase = (lane >> 5) * 4;
+  float* const part = partial ? partial + (int64_t)slice * M * N : nullptr;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -376,22 +382,85 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
       for (int v = 0; v < 16; ++v) {
         const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v / 4) + rbase + (v % 4);
         if (m < M) {
-          if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(acc[i][j][v]);
+          if (part) part[m * N + n] = acc[i][j][v];
+          else if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(acc[i][j][v]);
           else static_cast<float*>(y)[m * N + n] = acc[i][j][v];
         }
       }
     }
 }
 
+// y[i] = sum over slices s = 0 .. slices-1, in order, of partial[s][i]; four
+// consecutive outputs per thread (16-byte loads when MN is a multiple of 4).
+__global__ __launch_bounds__(256) void gemm_combine_kernel(const float* __restrict__ partial,
+                                                           void* __restrict__ y, int y_bf16,
+                                                           int64_t MN, int slices) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  if (MN % 4 == 0) {
+    f32x4v acc = *reinterpret_cast<const f32x4v*>(partial + i);
+    for (int s = 1; s < slices; ++s) acc += *reinterpret_cast<const f32x4v*>(partial + s * MN + i);
+    if (y_bf16) {
+      uint2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + i) = o;
+    } else {
+      *reinterpret_cast<f32x4v*>(static_cast<float*>(y) + i) = acc;
+    }
+    return;
+  }
+  for (int64_t e = i; e < i + 4 && e < MN; ++e) {
+    float acc = partial[e];
+    for (int s = 1; s < slices; ++s) acc += partial[s * MN + e];
+    if (y_bf16) static_cast<uint16_t*>(y)[e] = to_bf16(acc);
+    else static_cast<float*>(y)[e] = acc;
+  }
+}
+
+// Workgroup slots the tiled kernel has on the chip (256 CUs, 3 workgroups
+// each); a grid with fewer tiles than 2/3 of that is cut along K into slices
+// (at least 8 K steps each) when the caller gives a workspace.
+#ifndef Q4_GEMM_SPLIT_SLOTS
+#define Q4_GEMM_SPLIT_SLOTS 768
+#endif
+
+int64_t gemm_split_slices(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K % BK != 0) return 1;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles * 3 >= int64_t(Q4_GEMM_SPLIT_SLOTS) * 2) return 1;
+  int64_t s = int64_t(Q4_GEMM_SPLIT_SLOTS) / tiles;
+  const int64_t by_k = K / BK / 8;
+  if (s > by_k) s = by_k;
+  if (s > 64) s = 64;
+  if (s < 2) return 1;
+  // ceil(kt / s) K steps per slice; as many slices as that needs, so that
+  // none is empty
+  const int64_t kt = K / BK, per = (kt + s - 1) / s;
+  return (kt + per - 1) / per;
+}
+
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                       hipStream_t stream) {
   const int64_t tm = (M + BM - 1) / BM;
   const int64_t tn = (N + BN - 1) / BN;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (K % BK == 0)
-    gemm_dma_kernel<false><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
-  else
+  if (K % BK == 0) {
+    const int64_t slices = partial ? gemm_split_slices(M, N, K) : 1;
+    const int64_t kt = K / BK;
+    const int64_t kt_slice = (kt + slices - 1) / slices;
+    if (tm * tn * slices > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemm_dma_kernel<false><<<dim3((unsigned)(tm * tn * slices)), dim3(kThreads), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn, (int)kt_slice,
+        slices > 1 ? partial : nullptr);
+    if (slices > 1) {
+      // every slice has at least one K step: (slices - 1) * kt_slice < kt
+      const int64_t MN = M * N;
+      const int64_t grid = (MN + 1023) / 1024;
+      if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+      gemm_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+          partial, y, y_bf16 ? 1 : 0, MN, (int)slices);
+    }
+  } else
     gemm_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
   return hipGetLastError();
@@ -403,7 +472,7 @@ hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* w
   const int64_t tn = (N + BN - 1) / BN;
   if (tm * tn > 0x7FFFFFFF || K % BK != 0) return hipErrorInvalidValue;
   gemm_dma_kernel<true><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-      x, wq, we, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
+      x, wq, we, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn, (int)(K / BK), nullptr);
   return hipGetLastError();
 }
 

@@ -43,8 +43,14 @@ hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* w
                           bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // Many rows: dequant to bf16 in LDS + bf16 MFMA tiles (weights rounded to bf16).
+// partial: NULL, or fp32 scratch of gemm_split_slices(M, N, K) * M * N floats
+// that lets a grid of few tiles be cut along K (K a multiple of 64).
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                       bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                       bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                       hipStream_t stream);
+
+// K slices of the tiled kernel when scratch is given (1: never cut).
+int64_t gemm_split_slices(int64_t M, int64_t N, int64_t K);
 
 // Expert-routed rows; workspace laid out by moe_workspace_layout.
 struct MoeLayout {

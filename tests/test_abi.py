@@ -145,6 +145,15 @@ def test_matmul_workspace_bytes():
     # shapes need none
     assert q4.q4_matmul_workspace_bytes(1, 34816, 5120) == 0
     assert q4.q4_matmul_workspace_bytes(512, 34816, 5120) == 0
+    # tiled path: grids of 512 tiles or more are never cut along K; fewer
+    # tiles take up to 768 / tiles slices of at least 8 K steps, none empty
+    assert q4.q4_matmul_workspace_bytes(512, 5120, 17408) == 4 * 512 * 5120 * 4
+    assert q4.q4_matmul_workspace_bytes(1024, 5120, 17408) == 2 * 1024 * 5120 * 4
+    assert q4.q4_matmul_workspace_bytes(2048, 5120, 17408) == 0
+    assert q4.q4_matmul_workspace_bytes(129, 130, 64) == 0                 # one K step
+    assert q4.q4_matmul_workspace_bytes(129, 130, 64 * 16) == 2 * 129 * 130 * 4
+    assert q4.q4_matmul_workspace_bytes(200, 128, 64 * 520) == 58 * 200 * 128 * 4
+    assert q4.q4_matmul_workspace_bytes(300, 77, 96) == 0                  # K % 64 != 0
     for M in (3, 4, 5, 32):
         assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == 0
     assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 0

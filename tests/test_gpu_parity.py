@@ -221,6 +221,47 @@ def test_mfma_bf16_output(M, N, K):
     _check_dense(d, BF16, what=f"mfma bf16 M={M}")
 
 
+# K slices on the tiled path: q4_matmul_ex with a workspace cuts grids of
+# fewer than 512 tiles along K (2 to 64 slices of at least 8 K steps, the
+# last one ragged), then adds the fp32 slice sums in order.  M * N = 33153
+# and 23100 take the combine kernel's scalar and 16-byte forms.
+@pytest.mark.parametrize("M,N,K", [(129, 257, 1024), (256, 384, 2048 + 64 * 3),
+                                   (300, 77, 64 * 37), (512, 640, 5120), (200, 128, 64 * 520)])
+def test_mfma_split_parity(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_workspace_bytes(M, N, K) >= 2 * M * N * 4
+    d = synthetic.dense_case(4100 + M + N, M, N, K)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=True)
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"mfma split M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"mfma split bf16 M={M}")
+    y0 = matmul_ex(d.x, d.w_q, d.w_s, F32, workspace=None)
+    assert_parity(y0, y_ref, t, RTOL, what=f"mfma unsplit M={M} N={N} K={K}")
+
+
+def test_prefill_down_split_sampled_and_deterministic():
+    """The prefill FFN's down projection (512 x 5120 x 17408: 160 tiles) with
+    a workspace, against sampled outputs of the oracle; junk workspace
+    contents do not matter and two calls agree bit for bit."""
+    M, N, K = 512, 5120, 17408
+    d = synthetic.dense_case(4200, M, N, K)
+    x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
+    need = q4.q4_matmul_workspace_bytes(M, N, K)
+    assert need == 4 * M * N * 4
+    work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)
+    y1 = q4.q4_matmul_ex(x, wq, ws, out_dtype=BF16, workspace=work)
+    y2 = q4.q4_matmul_ex(x, wq, ws, out_dtype=BF16, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y = host(y1)
+    rng = np.random.default_rng(98)
+    ms = np.concatenate([rng.integers(0, M, 2000), [0, M - 1]])
+    ns = np.concatenate([rng.integers(0, N, 2000), [N - 1, 0]])
+    y_ref, t = oracle.matmul_sampled(d.x, d.w_q, d.w_s, ms, ns, bf16_weights=True)
+    assert_parity(y[ms, ns], y_ref, t, RTOL, bf16_half_ulp(y_ref), what="prefill down split")
+
+
 # ------------------------------------------------- exact special cases
 
 
