@@ -69,7 +69,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 5
+#define Q4_ABI_VERSION 6
 
 /* Status codes. */
 #define Q4_OK            0
@@ -239,6 +239,26 @@ Q4_API int32_t q4_moe_ffn(const void *x, const void *w13_q, const void *w13_s,
 Q4_API int32_t q4_mx_matmul(const void *x, const void *w_q, const void *w_e,
                             void *y, int32_t y_dtype,
                             int64_t M, int64_t N, int64_t K, q4_stream_t stream);
+
+/* Device workspace (bytes) that lets q4_mx_matmul_ex cut the tiled path's
+ * grid along K (ABI version 6): slices * M * N fp32 partial sums, with the
+ * slices q4_matmul_workspace_bytes gives a Q4_PATH_MFMA shape (grids of fewer
+ * than 512 tiles, K a multiple of 64).  0 when the call needs none, or for
+ * sizes q4_mx_matmul would reject. */
+Q4_API size_t q4_mx_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* q4_mx_matmul with an optional workspace (ABI version 6).  workspace ==
+ * NULL: exactly q4_mx_matmul.  Otherwise the same contract as q4_matmul_ex's:
+ * 16-byte aligned, at least q4_mx_matmul_workspace_bytes(M, N, K) bytes
+ * (else Q4_ERR_WORKSPACE, after the tensor NULL and alignment checks),
+ * contents on entry do not matter, not shared by calls that may overlap.
+ * The slices' fp32 sums are added in slice order: the same result on every
+ * run, which can differ from the unsplit call's in the last bits. */
+Q4_API int32_t q4_mx_matmul_ex(const void *x, const void *w_q, const void *w_e,
+                               void *y, int32_t y_dtype,
+                               int64_t M, int64_t N, int64_t K,
+                               void *workspace, size_t workspace_bytes,
+                               q4_stream_t stream);
 
 #ifdef __cplusplus
 }

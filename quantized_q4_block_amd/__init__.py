@@ -21,6 +21,9 @@ of the C ABI in ``include/q4.h``:
     q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None,
                workspace=None, stream=None) -> y
     q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=torch.float32, stream=None) -> y
+    q4_mx_matmul_workspace_bytes(M, N, K)   -> int
+    q4_mx_matmul_ex(x, w_q, w_e, out=None, out_dtype=torch.float32, workspace="auto",
+                    stream=None) -> y
 
 Tensor conventions (all CUDA/HIP device tensors, contiguous):
     x    torch.bfloat16 [M][K]       (or int16/uint16 holding bf16 bits)
@@ -38,7 +41,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 5
+Q4_ABI_VERSION = 6
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -57,6 +60,7 @@ __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
     "q4_moe_matmul", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
+    "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
 ]
 
 
@@ -98,6 +102,10 @@ def _open():
     L.q4_moe_ffn.restype = I32
     L.q4_mx_matmul.argtypes = [P, P, P, P, I32, I64, I64, I64, P]
     L.q4_mx_matmul.restype = I32
+    L.q4_mx_matmul_workspace_bytes.argtypes = [I64, I64, I64]
+    L.q4_mx_matmul_workspace_bytes.restype = ctypes.c_size_t
+    L.q4_mx_matmul_ex.argtypes = [P, P, P, P, I32, I64, I64, I64, P, ctypes.c_size_t, P]
+    L.q4_mx_matmul_ex.restype = I32
     if L.q4_abi_version() != Q4_ABI_VERSION:
         raise ImportError(f"libq4 ABI version {L.q4_abi_version()} != {Q4_ABI_VERSION}")
     return L
@@ -188,9 +196,7 @@ def q4_matmul(x, w_q, w_s, out=None, out_dtype=None, stream=None):
     return out
 
 
-def q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=None, stream=None):
-    """y[M][N] = x[M][K] . W^T with 4-bit float block weights: w = e2m1(code)
-    * 2^(E - 127), one E8M0 byte E per 32 k (fp32 or bf16 output)."""
+def _mx_args(x, w_q, w_e, out, out_dtype):
     torch = _torch()
     _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
     _check_dev(w_q, "w_q", (torch.uint8,), 2)
@@ -206,10 +212,39 @@ def q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=None, stream=None):
         _check_dev(out, "out", (torch.float32, torch.bfloat16), 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
+    return M, N, K, out
+
+
+def q4_mx_matmul(x, w_q, w_e, out=None, out_dtype=None, stream=None):
+    """y[M][N] = x[M][K] . W^T with 4-bit float block weights: w = e2m1(code)
+    * 2^(E - 127), one E8M0 byte E per 32 k (fp32 or bf16 output)."""
+    M, N, K, out = _mx_args(x, w_q, w_e, out, out_dtype)
     st = lib.q4_mx_matmul(_ptr(x), _ptr(w_q), _ptr(w_e), _ptr(out), _out_code(out.dtype),
                           M, N, K, _stream_handle(stream, x.device))
     if st != Q4_OK:
         raise Q4Error(st, "q4_mx_matmul")
+    return out
+
+
+def q4_mx_matmul_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q4_mx_matmul_workspace_bytes(int(M), int(N), int(K)))
+
+
+def q4_mx_matmul_ex(x, w_q, w_e, out=None, out_dtype=None, workspace="auto", stream=None):
+    """q4_mx_matmul with a workspace: "auto" allocates what the call can use
+    (a torch tensor), None passes none, a uint8 device tensor is passed as is."""
+    torch = _torch()
+    M, N, K, out = _mx_args(x, w_q, w_e, out, out_dtype)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        need = q4_mx_matmul_workspace_bytes(M, N, K)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.q4_mx_matmul_ex(_ptr(x), _ptr(w_q), _ptr(w_e), _ptr(out), _out_code(out.dtype),
+                             M, N, K, _ptr(workspace), nbytes, _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_mx_matmul_ex")
     return out
 
 

@@ -155,9 +155,24 @@ Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* 
   return q4_matmul_ex(x, w_q, w_s, y, y_dtype, M, N, K, nullptr, 0, stream);
 }
 
-Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, void* y,
-                            int32_t y_dtype, int64_t M, int64_t N, int64_t K,
-                            q4_stream_t stream) {
+// Tiled-path K slices of q4_mx_matmul_ex (0: the call never cuts K).
+static int64_t mx_split_slices(int64_t M, int64_t N, int64_t K) {
+  if (M <= kGemvMaxRows || K % 64 != 0 || q4_matmul_path(M, N, K) != Q4_PATH_MFMA) return 0;
+  const int64_t s = q4::gemm_split_slices(M, N, K);
+  return s > 1 ? s : 0;
+}
+
+Q4_API size_t q4_mx_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 0;
+  const int64_t slices = mx_split_slices(M, N, K);
+  int64_t mn, total;
+  if (slices == 0 || !mul_ok(M, N, &mn) || !mul_ok(mn, slices * 4, &total)) return 0;
+  return (size_t)total;
+}
+
+Q4_API int32_t q4_mx_matmul_ex(const void* x, const void* w_q, const void* w_e, void* y,
+                               int32_t y_dtype, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, q4_stream_t stream) {
   if (y_dtype != Q4_F32 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
   // from 3 rows on, slabs of 32 activation rows in the grid's y dimension
   if (M < 0 || M > int64_t(65535) * 32) return Q4_ERR_SHAPE;
@@ -167,6 +182,12 @@ Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, voi
   if (M == 0 || N == 0) return Q4_OK;
   if (!x || !w_q || !w_e || !y) return Q4_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_e) || !aligned16(y)) return Q4_ERR_ALIGN;
+  float* partial = nullptr;
+  if (workspace) {
+    const size_t need = q4_mx_matmul_workspace_bytes(M, N, K);
+    if (!aligned16(workspace) || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+    if (need > 0) partial = static_cast<float*>(workspace);
+  }
   if (int32_t s = check_device()) return s;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint8_t*>(w_q);
@@ -176,8 +197,14 @@ Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, voi
   if (M <= kGemvMaxRows) return launched(q4::launch_mx_gemv(xp, wp, ep, y, bf16, M, N, K, st));
   // the tiled kernel stages 64 k per step; other K stay on the few-row slabs
   if (q4_matmul_path(M, N, K) == Q4_PATH_MFMA && K % 64 == 0)
-    return launched(q4::launch_gemm_mx(xp, wp, ep, y, bf16, M, N, K, st));
+    return launched(q4::launch_gemm_mx(xp, wp, ep, y, bf16, M, N, K, partial, st));
   return launched(q4::launch_small_mx(xp, wp, ep, y, bf16, M, N, K, st));
+}
+
+Q4_API int32_t q4_mx_matmul(const void* x, const void* w_q, const void* w_e, void* y,
+                            int32_t y_dtype, int64_t M, int64_t N, int64_t K,
+                            q4_stream_t stream) {
+  return q4_mx_matmul_ex(x, w_q, w_e, y, y_dtype, M, N, K, nullptr, 0, stream);
 }
 
 Q4_API int32_t q4_dequantize(const void* w_q, const void* w_s, void* w_out, int32_t out_dtype,

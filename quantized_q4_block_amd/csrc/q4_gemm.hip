@@ -467,12 +467,27 @@ hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
 }
 
 hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
-                          bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                          bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                          hipStream_t stream) {
   const int64_t tm = (M + BM - 1) / BM;
   const int64_t tn = (N + BN - 1) / BN;
   if (tm * tn > 0x7FFFFFFF || K % BK != 0) return hipErrorInvalidValue;
-  gemm_dma_kernel<true><<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
-      x, wq, we, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn, (int)(K / BK), nullptr);
+  const int64_t slices = partial ? gemm_split_slices(M, N, K) : 1;
+  const int64_t kt = K / BK;
+  const int64_t kt_slice = (kt + slices - 1) / slices;
+  if (tm * tn * slices > 0x7FFFFFFF) return hipErrorInvalidValue;
+  gemm_dma_kernel<true><<<dim3((unsigned)(tm * tn * slices)), dim3(kThreads), 0, stream>>>(
+      x, wq, we, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn, (int)kt_slice,
+      slices > 1 ? partial : nullptr);
+  if (slices > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t MN = M * N;
+    const int64_t grid = (MN + 1023) / 1024;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemm_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+        partial, y, y_bf16 ? 1 : 0, MN, (int)slices);
+  }
   return hipGetLastError();
 }
 

@@ -39,8 +39,10 @@ hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* 
 
 // 4-bit float block weights, many rows, K a multiple of 64: e2m1 * 2^(E-129)
 // exact in bf16 in LDS + bf16 MFMA tiles, accumulators times 4; exact weights.
+// partial: as for launch_gemm (K slices of gemm_split_slices(M, N, K)).
 hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
-                          bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                          bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                          hipStream_t stream);
 
 // Many rows: dequant to bf16 in LDS + bf16 MFMA tiles (weights rounded to bf16).
 // partial: NULL, or fp32 scratch of gemm_split_slices(M, N, K) * M * N floats

@@ -49,7 +49,8 @@ def test_header_declares_the_abi():
     assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
                          "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
                          "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_ffn_workspace_bytes",
-                         "q4_moe_ffn", "q4_mx_matmul"}
+                         "q4_moe_ffn", "q4_mx_matmul", "q4_mx_matmul_workspace_bytes",
+                         "q4_mx_matmul_ex"}
 
 
 def test_every_declared_symbol_is_exported():
@@ -224,6 +225,40 @@ def test_mx_matmul_argument_errors():
     if not _gpu_present():
         assert _mx(L) == q4.Q4_ERR_DEVICE
         assert _mx(L, M=64, dt=1) == q4.Q4_ERR_DEVICE
+
+
+def test_mx_matmul_ex_workspace():
+    """Workspace sizes of the 4-bit float product: the tiled path's K slices
+    only (grids of fewer than 512 tiles, K a multiple of 64); its checks as
+    q4_matmul_ex's."""
+    q4, L = _lib()
+    assert q4.q4_mx_matmul_workspace_bytes(512, 5120, 17408) == 4 * 512 * 5120 * 4
+    assert q4.q4_mx_matmul_workspace_bytes(200, 300, 2112) == 4 * 200 * 300 * 4
+    assert q4.q4_mx_matmul_workspace_bytes(512, 34816, 5120) == 0      # 1088 tiles
+    assert q4.q4_mx_matmul_workspace_bytes(200, 300, 2080) == 0        # K % 64 != 0
+    assert q4.q4_mx_matmul_workspace_bytes(16, 5120, 17408) == 0       # few-row path
+    assert q4.q4_mx_matmul_workspace_bytes(1, 5120, 17408) == 0        # matrix-vector
+    assert q4.q4_mx_matmul_workspace_bytes(-1, 64, 256) == 0
+    assert q4.q4_mx_matmul_workspace_bytes(200, 300, 48) == 0
+    P = ctypes.c_void_p
+    L.q4_mx_matmul_ex.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int64, P, ctypes.c_size_t, P]
+    L.q4_mx_matmul_ex.restype = ctypes.c_int32
+
+    def mxx(ws_ptr, ws_bytes, x=A, M=512, N=5120, K=17408, dt=0):
+        return L.q4_mx_matmul_ex(P(x), P(A), P(A), P(A), dt, M, N, K, P(ws_ptr), ws_bytes, None)
+
+    need = q4.q4_mx_matmul_workspace_bytes(512, 5120, 17408)
+    assert mxx(A, need - 1) == q4.Q4_ERR_WORKSPACE
+    assert mxx(MIS, need) == q4.Q4_ERR_WORKSPACE
+    assert mxx(A, 0, x=0) == q4.Q4_ERR_NULL
+    assert mxx(A, 0, x=MIS) == q4.Q4_ERR_ALIGN
+    assert mxx(A, 0, dt=5) == q4.Q4_ERR_DTYPE
+    assert mxx(A, 0, K=40) == q4.Q4_ERR_SHAPE
+    assert mxx(0, 0, M=0) == q4.Q4_OK
+    if not _gpu_present():
+        assert mxx(A, need) == q4.Q4_ERR_DEVICE
+        assert mxx(0, 0) == q4.Q4_ERR_DEVICE
 
 
 def test_dequantize_argument_errors():

@@ -84,6 +84,53 @@ def test_mx_full_prefill_sampled():
                   what="mx_prefill sampled")
 
 
+def _mx_ex(x, w_q, w_e, out_dtype=torch.float32, workspace="auto"):
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV)
+    y = q4.q4_mx_matmul_ex(xd, torch.from_numpy(np.ascontiguousarray(w_q)).to(DEV),
+                           torch.from_numpy(np.ascontiguousarray(w_e)).to(DEV),
+                           out_dtype=out_dtype, workspace=workspace)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+# K slices of the tiled path through q4_mx_matmul_ex (2 to 58 slices, ragged
+# last slice; M * N = 60000 and 33153 take the combine kernel's 16-byte and
+# scalar forms)
+@pytest.mark.parametrize("M,N,K", [(200, 300, 2048 + 64), (129, 257, 1024), (200, 128, 64 * 520)])
+def test_mx_tiled_split(M, N, K):
+    assert q4.q4_mx_matmul_workspace_bytes(M, N, K) >= 2 * M * N * 4
+    c = synthetic.mx_case(9600 + M + N, M, N, K)
+    y_ref, t = oracle.mx_matmul(c.x, c.w_q, c.w_e)
+    y = _mx_ex(c.x, c.w_q, c.w_e)
+    assert_parity(y, y_ref, t, RTOL, what=f"mx split M={M} N={N} K={K}")
+    yb = _mx_ex(c.x, c.w_q, c.w_e, torch.bfloat16)
+    assert_parity(yb, y_ref, t, RTOL, extra=2.0 ** -9 * np.abs(y_ref), what=f"mx split bf16 M={M}")
+    y0 = _mx_ex(c.x, c.w_q, c.w_e, workspace=None)
+    assert_parity(y0, y_ref, t, RTOL, what=f"mx unsplit M={M} N={N} K={K}")
+
+
+def test_mx_split_down_projection_sampled_and_deterministic():
+    """512 x 5120 x 17408 (160 tiles, 4 slices) with junk workspace contents:
+    two calls agree bit for bit; sampled rows and columns against the oracle."""
+    M, N, K = 512, 5120, 17408
+    c = synthetic.mx_case(9700, M, N, K)
+    x = torch.from_numpy(c.x.view(np.int16)).to(DEV)
+    wq, we = torch.from_numpy(c.w_q).to(DEV), torch.from_numpy(c.w_e).to(DEV)
+    need = q4.q4_mx_matmul_workspace_bytes(M, N, K)
+    work = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    y1 = q4.q4_mx_matmul_ex(x, wq, we, out_dtype=torch.bfloat16, workspace=work)
+    y2 = q4.q4_mx_matmul_ex(x, wq, we, out_dtype=torch.bfloat16, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y = y1.float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(78)
+    ms = np.unique(np.concatenate([rng.integers(0, M, 30), [0, M - 1]]))
+    ns = np.unique(np.concatenate([rng.integers(0, N, 200), [0, N - 1]]))
+    y_ref, t = oracle.mx_matmul(c.x[ms], c.w_q[ns], c.w_e[ns])
+    assert_parity(y[np.ix_(ms, ns)], y_ref, t, RTOL, extra=2.0 ** -9 * np.abs(y_ref),
+                  what="mx down split sampled")
+
+
 def test_mx_full_decode_gate_up():
     cfg = synthetic.MX_CONFIGS["mx_decode_gate_up"]
     c = synthetic.mx_case(cfg["seed"], cfg["M"], cfg["N"], cfg["K"])
