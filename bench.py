@@ -387,6 +387,31 @@ def summarize_trace(run_dir):
     return out
 
 
+def summarize_counters(run_dir):
+    """Per-kernel dispatch count and mean value per dispatch of every counter
+    in the counter_collection.csv files a rocprofv3 --pmc run wrote under
+    run_dir (kernel names shortened as in summarize_trace)."""
+    import csv
+    vals = {}
+    for dirpath, _, files in os.walk(run_dir):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(dirpath, fn), newline="") as f:
+                for row in csv.DictReader(f):
+                    name = row["Kernel_Name"].replace("void ", "")
+                    name = name.replace("(anonymous namespace)::", "").split("(")[0]
+                    per = vals.setdefault(name, {})
+                    per.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    out = {}
+    for name, per in vals.items():
+        rec = {"dispatches": max(len(v) for v in per.values())}
+        for c, v in sorted(per.items()):
+            rec[c] = round(float(np.mean(v)), 1)
+        out[name] = rec
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -399,6 +424,9 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print per-kernel duration statistics (mean, p10, median, p90) of a "
                          "rocprofv3 --kernel-trace run of this script (no GPU needed)")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="print each kernel's mean counter values per dispatch from a "
+                         "rocprofv3 --pmc run of this script (no GPU needed)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script with --calibrate-copy-mib 256 into the decode kernel's "
@@ -407,6 +435,9 @@ def main():
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
         return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], 256,
                       "gemv_decode_gate_up", "gemv_lds_kernel", weight_bytes(34816, 5120),
@@ -414,7 +445,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the decode and prefill paths would shard the weight rows; see DESIGN.md)",
+              "(the decode and prefill paths would shard the weight rows by output feature)",
               file=sys.stderr)
         sys.exit(2)
 
