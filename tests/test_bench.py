@@ -97,3 +97,23 @@ def test_summarize_trace_percentiles(tmp_path):
     assert a["p10_us"] == 1.9 and a["p90_us"] == 9.1
     assert a["min_us"] == 1.0 and a["max_us"] == 10.0
     assert s["q4::b<2>"]["calls"] == 1 and s["q4::b<2>"]["median_us"] == 100.0
+
+
+def test_summarize_counters_means(tmp_path):
+    b = _bench()
+    d = tmp_path / "pmc" / "host"
+    d.mkdir(parents=True)
+    with open(d / "9_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        # kernel a: two dispatches of two counters; kernel b: one dispatch
+        for v in (10.0, 30.0):
+            w.writerow({"Kernel_Name": "void q4::a<1>(int)", "Counter_Name": "SQ_WAVES",
+                        "Counter_Value": v})
+            w.writerow({"Kernel_Name": "void q4::a<1>(int)", "Counter_Name": "FETCH_SIZE",
+                        "Counter_Value": 2 * v})
+        w.writerow({"Kernel_Name": "void q4::(anonymous namespace)::b<2>(float*)",
+                    "Counter_Name": "SQ_WAVES", "Counter_Value": 7})
+    s = b.summarize_counters(str(tmp_path / "pmc"))
+    assert s["q4::a<1>"] == {"dispatches": 2, "FETCH_SIZE": 40.0, "SQ_WAVES": 20.0}
+    assert s["q4::b<2>"] == {"dispatches": 1, "SQ_WAVES": 7.0}
