@@ -271,8 +271,12 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[S * 8 * kWave];
   const int slot = blockIdx.y;
-  if (slot >= *num_active) return;                 // whole workgroup
+  // the active count and this slot's expert in one round trip (grid.y is the
+  // length of the active list, so the read is in bounds)
+  const int na = *num_active;
   const int32_t e = active[slot];
+  asm volatile("" :: "s"(e), "s"(na));
+  if (slot >= na) return;                          // whole workgroup
   const int32_t start = offsets[e];
   const int32_t cnt = counts[e];
   const int lane = threadIdx.x & 63;
@@ -283,7 +287,8 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   const int room = (int)((N - 1 - nl) < R ? (N - 1 - nl) : R);
   const uint8_t* wq_e = wq + (int64_t)e * N * (K / 2);
   const uint16_t* ws_e = ws + (int64_t)e * N * (K / kBlock);
-  // the first pair's activation loads go out before the weight loads
+  // the weight loads go out as soon as the expert is known; the first pair's
+  // activation loads follow once its index has come back from the bucket
   using Stager = typename std::conditional<MODE == kRowsDown, XStagerF32<S, kLdsWaves * 64>,
                                            XStager<1, S, kLdsWaves * 64>>::type;
   Stager xst;
@@ -293,12 +298,13 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
     else
       xst.load(static_cast<const uint16_t*>(xv) + (int64_t)(pp / topk) * K, K, K);
   };
-  int32_t p = order[start];   // an active expert has at least one pair
-  stage(p);
   const uint32_t row_bytes = (uint32_t)(K / 2), row_sc = (uint32_t)(K / kBlock);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq_e + nl * (int64_t)row_bytes, ws_e + nl * (int64_t)row_sc,
                               row_bytes, row_sc, room, rem, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  int32_t p = order[start];   // an active expert has at least one pair
+  stage(p);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.pin();
   for (int32_t i = 0; i < cnt; ++i) {
