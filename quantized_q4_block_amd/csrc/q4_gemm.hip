@@ -340,6 +340,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
     const int64_t kn = (kt + 1 < nk ? kt + 1 : kt) * 64;
     dma(cur ^ 1, kn);
     load_b(kn);
+    // 4-bit float staging is light (4 conversions per 8 weights): raising
+    // the wave's priority for its MFMA stretch interleaves the workgroups of
+    // a CU better; the int4 staging (21 instructions per 8 weights) is slower
+    // with it, so only the MX form does this
+    if constexpr (MX) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8v af[2], bfr[2];
@@ -359,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(const uint16_t* __re
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    if constexpr (MX) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     store_b();
     __builtin_amdgcn_s_waitcnt(0);   // next activation tile landed in LDS
