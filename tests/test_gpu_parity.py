@@ -500,3 +500,23 @@ def test_non_default_stream():
     s.synchronize()
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     assert_parity(host(y), y_ref, t, RTOL, what="stream")
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 300, 17408), (300, 200, 64 * 40)])
+def test_split_calls_on_a_non_default_stream(M, N, K):
+    """The cut calls (matrix-vector slices, tiled K slices) put their product
+    and their combine kernel on the caller's stream; the workspace is
+    allocated on that stream too."""
+    d = synthetic.dense_case(7400 + M, M, N, K)
+    need = q4.q4_matmul_workspace_bytes(M, N, K)
+    assert need > 0
+    s = torch.cuda.Stream()
+    x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)
+        y = q4.q4_matmul_ex(x, wq, ws, workspace=work, stream=s)
+    s.synchronize()
+    mfma = q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=mfma)
+    assert_parity(host(y), y_ref, t, RTOL, what=f"split on a stream M={M}")
