@@ -289,13 +289,33 @@ def summarize_pmc(fetch_dir, write_dir, copy_mib, kernel_tag, kernel_match, algo
     print(json.dumps(rec, indent=1))
 
 
-def time_steps(torch, work, steps, warmup):
+# After a few seconds without GPU work (input generation on the host) the
+# chip needs several milliseconds of load before its clocks are back up: the
+# MoE call measured 51 us in its first 200 launches and 44 us from then on.
+CLOCK_WARM_MS = 60.0
+
+
+def time_steps(torch, work, steps, warmup, warm_ms=0.0):
     """Host-timed steps (synchronised on both sides) and HIP-event time over
-    the same region on the launch stream."""
+    the same region on the launch stream.  `warmup` untimed steps first, and
+    before them, if warm_ms > 0, untimed steps until the GPU has run this
+    work for warm_ms."""
     stream = torch.cuda.current_stream()
     h = ctypes.c_void_p(stream.cuda_stream)
-    for i in range(warmup):
-        work.step(i, h)
+    done, i = 0.0, 0
+    while done < warm_ms:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for _ in range(20):
+            work.step(i, h)
+            i += 1
+        w1.record(stream)
+        torch.cuda.synchronize()
+        done += w0.elapsed_time(w1)
+    for j in range(warmup):
+        work.step(i + j, h)
+    warmup += i
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -416,7 +436,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    # 3000 decode launches (about 60 ms) bring the clocks up after the input
+    # generation: 20.5 us per launch after 200 warmup launches, 19.4-19.8 after 3000
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -485,7 +507,7 @@ def main():
             progress(f"{name}: generating inputs")
             w = Dense(torch, q4, name)
             progress(f"{name}: timing")
-            _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+            _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10), CLOCK_WARM_MS)
             if name == "prefill":
                 tf = w.flops / (ev * 1e-3) / 1e12
                 others[name] = {"M": w.M, "N": w.N, "K": w.K, "avg_launch_us": round(ev * 1e3, 2),
@@ -499,7 +521,7 @@ def main():
         progress("mx_decode_gate_up: generating inputs")
         w = MxDense(torch, q4)
         progress("mx_decode_gate_up: timing")
-        _, ev = time_steps(torch, w, args.steps // 2, max(10, args.warmup // 2))
+        _, ev = time_steps(torch, w, args.steps // 2, max(10, args.warmup // 2), CLOCK_WARM_MS)
         gbs = w.wbytes / (ev * 1e-3) / 1e9
         others["mx_decode_gate_up"] = {"M": w.M, "N": w.N, "K": w.K,
                                        "format": "e2m1 elements, E8M0 scale per 32",
@@ -511,7 +533,7 @@ def main():
         progress("mx_prefill: generating inputs")
         w = MxDense(torch, q4, "mx_prefill")
         progress("mx_prefill: timing")
-        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10), CLOCK_WARM_MS)
         tf = w.flops / (ev * 1e-3) / 1e12
         others["mx_prefill"] = {"M": w.M, "N": w.N, "K": w.K,
                                 "format": "e2m1 elements, E8M0 scale per 32",
@@ -522,7 +544,7 @@ def main():
         progress("moe: generating inputs")
         w = MoE(torch, q4)
         progress("moe: timing")
-        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10), CLOCK_WARM_MS)
         gbs = w.wbytes / (ev * 1e-3) / 1e9
         others["moe"] = {"T": w.T, "topk": w.topk, "E": w.E, "N": w.N, "K": w.K,
                          "touched_experts": w.touched, "avg_call_us": round(ev * 1e3, 2),
@@ -533,7 +555,7 @@ def main():
         progress("moe_ffn: generating inputs")
         w = MoeFfn(torch, q4)
         progress("moe_ffn: timing")
-        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10))
+        _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10), CLOCK_WARM_MS)
         gbs = w.wbytes / (ev * 1e-3) / 1e9
         others["moe_ffn"] = {"T": w.T, "topk": w.topk, "E": w.E, "H": w.H, "F": w.F,
                              "touched_experts": w.touched, "avg_call_us": round(ev * 1e3, 2),
