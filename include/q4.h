@@ -69,7 +69,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 6
+#define Q4_ABI_VERSION 7
 
 /* Status codes. */
 #define Q4_OK            0
@@ -110,6 +110,15 @@ Q4_API const char *q4_status_str(int32_t status);
  * Host-only: enqueues nothing. */
 Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K);
 
+/* Path q4_matmul_ex takes (ABI version 7): with_workspace == 0 as
+ * q4_matmul_path; otherwise, for a workspace of at least
+ * q4_matmul_workspace_bytes(M, N, K) bytes, shapes with 33 <= M <= 128 that
+ * q4_matmul_path sends to Q4_PATH_SMALL take Q4_PATH_MFMA (the tiled kernel
+ * cut along K, weights rounded to bf16) when K is a multiple of 64, N * K is
+ * at least 2^24 and the grid of 128 x 128 tiles is small enough to be cut.  q4_mx_matmul_ex follows
+ * the same rule (its tiled weights are exact).  Host-only. */
+Q4_API int32_t q4_matmul_path_ex(int64_t M, int64_t N, int64_t K, int32_t with_workspace);
+
 /* y = x * dequant(W)^T.
  *   x       bf16  [M][K]    device
  *   w_q     uint8 [N][K/2]  device
@@ -126,10 +135,10 @@ Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
 /* Device workspace (bytes) that lets q4_matmul_ex cut long rows into
  * slices: slices * M * N fp32 partial sums.  Q4_PATH_GEMV shapes are cut when
  * K is above 8192 or the activations are too large for one workgroup's LDS;
- * Q4_PATH_MFMA shapes with K a multiple of 64 when their grid has fewer than
- * 512 tiles of 128 x 128 outputs (at most 768 / tiles and 64 slices, each of
- * at least 8 steps of 64 k).  0 when the call needs none, or for sizes
- * q4_matmul would reject. */
+ * tiled shapes (q4_matmul_path_ex(M, N, K, 1) == Q4_PATH_MFMA) with K a
+ * multiple of 64 when their grid has fewer than 512 tiles of 128 x 128
+ * outputs (at most 768 / tiles and 64 slices, each of at least 8 steps of
+ * 64 k).  0 when the call needs none, or for sizes q4_matmul would reject. */
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* q4_matmul with an optional workspace.  workspace == NULL: exactly

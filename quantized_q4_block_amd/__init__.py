@@ -9,6 +9,7 @@ of the C ABI in ``include/q4.h``:
     q4_abi_version()                        -> int
     q4_status_str(status)                   -> str
     q4_matmul_path(M, N, K)                 -> Q4_PATH_GEMV | Q4_PATH_SMALL | Q4_PATH_MFMA
+    q4_matmul_path_ex(M, N, K, with_workspace) -> the path q4_matmul_ex takes
     q4_matmul(x, w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> y
     q4_matmul_workspace_bytes(M, N, K)      -> int
     q4_matmul_ex(x, w_q, w_s, out=None, out_dtype=torch.float32, workspace="auto",
@@ -41,7 +42,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 6
+Q4_ABI_VERSION = 7
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -57,7 +58,8 @@ Q4_PATH_MFMA = 1
 Q4_PATH_SMALL = 2
 
 __all__ = [
-    "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
+    "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul_path_ex",
+    "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
     "q4_moe_matmul", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
     "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
@@ -83,6 +85,8 @@ def _open():
     L.q4_status_str.restype = ctypes.c_char_p
     L.q4_matmul_path.argtypes = [I64, I64, I64]
     L.q4_matmul_path.restype = I32
+    L.q4_matmul_path_ex.argtypes = [I64, I64, I64, I32]
+    L.q4_matmul_path_ex.restype = I32
     L.q4_matmul.argtypes = [P, P, P, P, I32, I64, I64, I64, P]
     L.q4_matmul.restype = I32
     L.q4_matmul_workspace_bytes.argtypes = [I64, I64, I64]
@@ -124,6 +128,10 @@ def q4_status_str(status: int) -> str:
 
 def q4_matmul_path(M: int, N: int, K: int) -> int:
     return int(lib.q4_matmul_path(int(M), int(N), int(K)))
+
+
+def q4_matmul_path_ex(M: int, N: int, K: int, with_workspace: bool) -> int:
+    return int(lib.q4_matmul_path_ex(int(M), int(N), int(K), 1 if with_workspace else 0))
 
 
 # ---------------------------------------------------------------- tensors

@@ -46,7 +46,8 @@ def _gpu_present() -> bool:
 
 def test_header_declares_the_abi():
     syms = _declared_symbols()
-    assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul",
+    assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul_path_ex",
+                         "q4_matmul",
                          "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
                          "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_ffn_workspace_bytes",
                          "q4_moe_ffn", "q4_mx_matmul", "q4_mx_matmul_workspace_bytes",
@@ -103,6 +104,17 @@ def test_path_dispatch():
     assert q4.q4_matmul_path(129, 5120, 17408) == q4.Q4_PATH_MFMA
     assert q4.q4_matmul_path(512, 34816, 5120) == q4.Q4_PATH_MFMA
     assert q4.q4_matmul_path(1 << 20, 64, 64) == q4.Q4_PATH_MFMA
+    # with a workspace: 33..128 rows on large weights leave the slabs for the
+    # tiled kernel cut along K; small matrices, K % 64 != 0 and <= 32 rows stay
+    assert q4.q4_matmul_path_ex(64, 5120, 17408, False) == q4.Q4_PATH_SMALL
+    assert q4.q4_matmul_path_ex(64, 5120, 17408, True) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path_ex(33, 5120, 5120, True) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path_ex(128, 1024, 4096, True) == q4.Q4_PATH_SMALL    # 2^22 weights
+    assert q4.q4_matmul_path_ex(64, 5120, 17408 + 32, True) == q4.Q4_PATH_SMALL
+    assert q4.q4_matmul_path_ex(32, 5120, 17408, True) == q4.Q4_PATH_SMALL
+    assert q4.q4_matmul_path_ex(1, 5120, 17408, True) == q4.Q4_PATH_GEMV
+    assert q4.q4_matmul_path_ex(512, 34816, 5120, True) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path_ex(-1, 64, 64, True) == -1
     for bad in ((-1, 8, 32), (4, -1, 32), (4, 8, 0), (4, 8, 48)):
         assert q4.q4_matmul_path(*bad) == -1
 
@@ -151,6 +163,8 @@ def test_matmul_workspace_bytes():
     assert q4.q4_matmul_workspace_bytes(512, 5120, 17408) == 4 * 512 * 5120 * 4
     assert q4.q4_matmul_workspace_bytes(1024, 5120, 17408) == 2 * 1024 * 5120 * 4
     assert q4.q4_matmul_workspace_bytes(2048, 5120, 17408) == 0
+    assert q4.q4_matmul_workspace_bytes(64, 5120, 17408) == 19 * 64 * 5120 * 4    # 40 tiles
+    assert q4.q4_matmul_workspace_bytes(64, 1024, 4096) == 0                      # slabs
     assert q4.q4_matmul_workspace_bytes(129, 130, 64) == 0                 # one K step
     assert q4.q4_matmul_workspace_bytes(129, 130, 64 * 16) == 2 * 129 * 130 * 4
     assert q4.q4_matmul_workspace_bytes(200, 128, 64 * 520) == 58 * 200 * 128 * 4

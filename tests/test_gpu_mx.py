@@ -109,6 +109,19 @@ def test_mx_tiled_split(M, N, K):
     assert_parity(y0, y_ref, t, RTOL, what=f"mx unsplit M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 4096 + 64 * 3), (128, 2048, 8192)])
+def test_mx_slab_shapes_with_a_workspace(M, N, K):
+    """33..128 rows on large weights: the tiled kernel cut along K with a
+    workspace, the few-row slabs without; both exact."""
+    assert q4.q4_matmul_path_ex(M, N, K, True) == q4.Q4_PATH_MFMA
+    assert q4.q4_mx_matmul_workspace_bytes(M, N, K) > 0
+    c = synthetic.mx_case(9800 + M, M, N, K)
+    y_ref, t = oracle.mx_matmul(c.x, c.w_q, c.w_e)
+    assert_parity(_mx_ex(c.x, c.w_q, c.w_e), y_ref, t, RTOL, what=f"mx slab shape tiled M={M}")
+    assert_parity(_mx_ex(c.x, c.w_q, c.w_e, workspace=None), y_ref, t, RTOL,
+                  what=f"mx slab shape slabs M={M}")
+
+
 def test_mx_split_down_projection_sampled_and_deterministic():
     """512 x 5120 x 17408 (160 tiles, 4 slices) with junk workspace contents:
     two calls agree bit for bit; sampled rows and columns against the oracle."""

@@ -240,6 +240,24 @@ def test_mfma_split_parity(M, N, K):
     assert_parity(y0, y_ref, t, RTOL, what=f"mfma unsplit M={M} N={N} K={K}")
 
 
+# With a workspace, 33..128 rows on weight matrices of at least 2^24 entries
+# leave the few-row slabs for the tiled kernel cut along K (weights rounded
+# to bf16 there); without one the same shapes stay on the slabs (exact).
+@pytest.mark.parametrize("M,N,K", [(33, 4096, 4096 + 64 * 3), (100, 5120, 5120), (128, 2048, 8192)])
+def test_slab_shapes_with_a_workspace(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_SMALL
+    assert q4.q4_matmul_path_ex(M, N, K, True) == q4.Q4_PATH_MFMA
+    d = synthetic.dense_case(4300 + M, M, N, K)
+    y_ref_b, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=True)
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref_b, t, RTOL, what=f"slab shape tiled M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref_b, t, RTOL, bf16_half_ulp(y_ref_b), what=f"slab shape tiled bf16 M={M}")
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    y0 = matmul_ex(d.x, d.w_q, d.w_s, F32, workspace=None)
+    assert_parity(y0, y_ref, t, RTOL, what=f"slab shape slabs M={M} N={N} K={K}")
+
+
 def test_prefill_down_split_sampled_and_deterministic():
     """The prefill FFN's down projection (512 x 5120 x 17408: 160 tiles) with
     a workspace, against sampled outputs of the oracle; junk workspace
