@@ -98,8 +98,8 @@ Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return -1;
   if (M <= kGemvMaxRows) return Q4_PATH_GEMV;
   if (M <= kSmallMaxRows) return Q4_PATH_SMALL;
-  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  if (M <= kSmallSlabMaxRows && tiles < kTiledMinTiles) return Q4_PATH_SMALL;
+  // at most 128 rows: one row of 128 x 128 tiles
+  if (M <= kSmallSlabMaxRows && (N + 127) / 128 < kTiledMinTiles) return Q4_PATH_SMALL;
   return Q4_PATH_MFMA;
 }
 
@@ -111,7 +111,9 @@ Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K) {
 constexpr int64_t kSlabsToTiledMinWeights = int64_t(1) << 24;
 
 static bool slabs_to_tiled(int64_t M, int64_t N, int64_t K) {
-  return M > kSmallMaxRows && K % 64 == 0 && N * K >= kSlabsToTiledMinWeights &&
+  // N * K >= 2^24 without forming the product (sizes are not checked here)
+  return M > kSmallMaxRows && K % 64 == 0 && N > 0 &&
+         K >= (kSlabsToTiledMinWeights + N - 1) / N &&
          q4_matmul_path(M, N, K) == Q4_PATH_SMALL && q4::gemm_split_slices(M, N, K) > 1;
 }
 

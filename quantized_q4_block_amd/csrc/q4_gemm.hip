@@ -431,7 +431,9 @@ __global__ __launch_bounds__(256) void gemm_combine_kernel(const float* __restri
 
 int64_t gemm_split_slices(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K % BK != 0) return 1;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  if (tm >= 512 || tn >= 512) return 1;   // never cut; keeps the product in range
+  const int64_t tiles = tm * tn;
   if (tiles * 3 >= int64_t(Q4_GEMM_SPLIT_SLOTS) * 2) return 1;
   int64_t s = int64_t(Q4_GEMM_SPLIT_SLOTS) / tiles;
   const int64_t by_k = K / BK / 8;

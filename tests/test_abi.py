@@ -115,6 +115,11 @@ def test_path_dispatch():
     assert q4.q4_matmul_path_ex(1, 5120, 17408, True) == q4.Q4_PATH_GEMV
     assert q4.q4_matmul_path_ex(512, 34816, 5120, True) == q4.Q4_PATH_MFMA
     assert q4.q4_matmul_path_ex(-1, 64, 64, True) == -1
+    # sizes far past any device: answers without overflowing a product
+    assert q4.q4_matmul_path(1 << 40, 1 << 40, 64) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_path_ex(100, 1 << 40, 1 << 40, True) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_workspace_bytes(1 << 40, 1 << 40, 64) == 0
+    assert q4.q4_matmul_workspace_bytes(100, 1 << 40, 1 << 30) == 0
     for bad in ((-1, 8, 32), (4, -1, 32), (4, 8, 0), (4, 8, 48)):
         assert q4.q4_matmul_path(*bad) == -1
 
