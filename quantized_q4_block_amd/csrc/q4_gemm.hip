@@ -422,6 +422,19 @@ __global__ __launch_bounds__(256) void gemm_combine_kernel(const float* __restri
   }
 }
 
+// The fp32 slice sums of a cut call into y, enqueued after the product on
+// the same stream.
+static hipError_t launch_combine(const float* partial, void* y, bool y_bf16, int64_t MN,
+                                 int64_t slices, hipStream_t stream) {
+  const hipError_t e = hipGetLastError();   // the product's launch
+  if (e != hipSuccess) return e;
+  const int64_t grid = (MN + 1023) / 1024;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  gemm_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(partial, y, y_bf16 ? 1 : 0,
+                                                                      MN, (int)slices);
+  return hipGetLastError();
+}
+
 // Workgroup slots the tiled kernel has on the chip (256 CUs, 3 workgroups
 // each); a grid with fewer tiles than 2/3 of that is cut along K into slices
 // (at least 8 K steps each) when the caller gives a workspace.
@@ -460,14 +473,8 @@ hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
     gemm_dma_kernel<false><<<dim3((unsigned)(tm * tn * slices)), dim3(kThreads), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn, (int)kt_slice,
         slices > 1 ? partial : nullptr);
-    if (slices > 1) {
-      // every slice has at least one K step: (slices - 1) * kt_slice < kt
-      const int64_t MN = M * N;
-      const int64_t grid = (MN + 1023) / 1024;
-      if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-      gemm_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
-          partial, y, y_bf16 ? 1 : 0, MN, (int)slices);
-    }
+    // every slice has at least one K step: (slices - 1) * kt_slice < kt
+    if (slices > 1) return launch_combine(partial, y, y_bf16, M * N, slices, stream);
   } else
     gemm_kernel<<<dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn);
@@ -487,15 +494,7 @@ hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* w
   gemm_dma_kernel<true><<<dim3((unsigned)(tm * tn * slices)), dim3(kThreads), 0, stream>>>(
       x, wq, we, y, y_bf16 ? 1 : 0, M, N, K, (int)tm, (int)tn, (int)kt_slice,
       slices > 1 ? partial : nullptr);
-  if (slices > 1) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t MN = M * N;
-    const int64_t grid = (MN + 1023) / 1024;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_combine_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
-        partial, y, y_bf16 ? 1 : 0, MN, (int)slices);
-  }
+  if (slices > 1) return launch_combine(partial, y, y_bf16, M * N, slices, stream);
   return hipGetLastError();
 }
 
