@@ -25,24 +25,27 @@
  *   y    fp32 or bf16 [M][N]
  * K must be a positive multiple of 32.
  *
- * Numerics.  Products and sums are fp32.  The matrix-vector path and the
- * few-row matrix-core path (Q4_PATH_GEMV, Q4_PATH_SMALL) use every weight
- * (c-8)*s exactly: each 32-element block's sum of x * (c - 8) is formed
- * first (exact products) and its scale applied once in fp32.  The tiled
- * matrix-core path (Q4_PATH_MFMA) rounds every weight to bf16
- * (nearest-even) and the bf16 matrix cores accumulate in fp32.
- * q4_matmul_path tells which path a shape takes.  bf16 outputs are rounded
- * nearest-even from the fp32 result.  Results are bit-identical from run to
- * run (no floating-point atomics).
+ * Numerics.  Products and sums are fp32 and every weight (c-8)*s enters
+ * exactly, on every path: each 32-element block's sum of x * (c - 8) is
+ * formed first (exact products; on the matrix-core paths the small integers
+ * c - 8 are exact bf16 operands) and the block's scale is applied to it once
+ * in fp32.  q4_matmul_path tells which kernel a shape takes.  bf16 outputs
+ * are rounded nearest-even from the fp32 result.  Results are bit-identical
+ * from run to run (no floating-point atomics).
  *
  * Conventions of every call:
  *   - All checks run on the host before anything is enqueued; on any error
  *     nothing is launched and no output is written.
- *   - Check order: dtype, shape, zero-size no-op, NULL, alignment, device,
- *     launch.  M == 0 or N == 0 (T == 0 for MoE) returns Q4_OK and touches
+ *   - Check order: dtype, shape, zero-size no-op, NULL, alignment,
+ *     workspace, device, pending HIP error, launch.  M == 0 or N == 0 (T == 0 for MoE) returns Q4_OK and touches
  *     nothing (pointers may then be NULL).
  *   - Alignment: every tensor pointer must be 16-byte aligned (the kernels
  *     use 128-bit loads and stores).
+ *   - HIP error state: a HIP error already pending when a call is made (from
+ *     the caller's own earlier work) is left in place, and the call returns
+ *     Q4_ERR_PENDING without launching anything.  An error raised by this
+ *     call's own launches is reported as Q4_ERR_LAUNCH and consumed, so no
+ *     HIP error state leaves a call.
  *   - Device: the current HIP device must be a gfx950 GPU, else
  *     Q4_ERR_DEVICE.
  *   - The call returns once the work is enqueued on `stream` (a hipStream_t;
@@ -69,7 +72,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 7
+#define Q4_ABI_VERSION 8
 
 /* Status codes. */
 #define Q4_OK            0
@@ -80,6 +83,8 @@ extern "C" {
 #define Q4_ERR_WORKSPACE 5  /* workspace NULL (MoE), misaligned or too small */
 #define Q4_ERR_DEVICE    6  /* no current HIP device, or it is not gfx950 */
 #define Q4_ERR_LAUNCH    7  /* the HIP runtime reported an error at enqueue */
+#define Q4_ERR_PENDING   8  /* a HIP error from before the call was pending: left
+                               in place, nothing launched (ABI version 8) */
 
 /* Output dtypes. */
 #define Q4_F32  0
@@ -87,7 +92,8 @@ extern "C" {
 
 /* Paths chosen by q4_matmul. */
 #define Q4_PATH_GEMV  0     /* fused dequant + matrix-vector, exact weights */
-#define Q4_PATH_MFMA  1     /* dequant to bf16 in LDS + bf16 matrix-core tiles */
+#define Q4_PATH_MFMA  1     /* exact (c - 8) tiles in LDS + bf16 matrix-core
+                               tiles, fp32 block scales: exact weights */
 #define Q4_PATH_SMALL 2     /* exact (c - 8) on bf16 matrix cores, fp32 block
                                scales: exact weights */
 
@@ -114,7 +120,7 @@ Q4_API int32_t q4_matmul_path(int64_t M, int64_t N, int64_t K);
  * q4_matmul_path; otherwise, for a workspace of at least
  * q4_matmul_workspace_bytes(M, N, K) bytes, shapes with 33 <= M <= 128 that
  * q4_matmul_path sends to Q4_PATH_SMALL take Q4_PATH_MFMA (the tiled kernel
- * cut along K, weights rounded to bf16) when K is a multiple of 64, N * K is
+ * cut along K) when K is a multiple of 64, N * K is
  * at least 2^24 and the grid of 128 x 128 tiles is small enough to be cut.  q4_mx_matmul_ex follows
  * the same rule (its tiled weights are exact).  Host-only. */
 Q4_API int32_t q4_matmul_path_ex(int64_t M, int64_t N, int64_t K, int32_t with_workspace);

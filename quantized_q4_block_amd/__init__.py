@@ -42,7 +42,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 7
+Q4_ABI_VERSION = 8
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -51,6 +51,7 @@ Q4_ERR_DTYPE = 4
 Q4_ERR_WORKSPACE = 5
 Q4_ERR_DEVICE = 6
 Q4_ERR_LAUNCH = 7
+Q4_ERR_PENDING = 8
 Q4_F32 = 0
 Q4_BF16 = 1
 Q4_PATH_GEMV = 0

@@ -42,22 +42,18 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// The current device must be gfx950 (cached per device after the first
+// query).  A failed query's error is left as the runtime set it.
 int32_t check_device() {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
-    (void)hipGetLastError();
-    return Q4_ERR_DEVICE;
-  }
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return Q4_ERR_DEVICE;
   if (dev < kMaxDevices) {
     const int known = g_arch[dev].load(std::memory_order_relaxed);
     if (known == 1) return Q4_OK;
     if (known == 2) return Q4_ERR_DEVICE;
   }
   hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return Q4_ERR_DEVICE;
-  }
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q4_ERR_DEVICE;
   const char* a = prop.gcnArchName;
   const bool ok = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
                   a[5] == '0' && (a[6] == '\0' || a[6] == ':');
@@ -72,7 +68,22 @@ int32_t check_weights(int64_t N, int64_t K) {
   return Q4_OK;
 }
 
-int32_t launched(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_LAUNCH; }
+// Run right before anything is enqueued: the device check, then a HIP error
+// already pending from the caller's own work is left in place (not cleared,
+// not taken for this call's) and nothing is launched.
+int32_t ready() {
+  if (int32_t s = check_device()) return s;
+  if (hipPeekAtLastError() != hipSuccess) return Q4_ERR_PENDING;
+  return Q4_OK;
+}
+
+// Status of the launches: the error state was clean when they were enqueued,
+// so an error pending now is theirs; it is consumed here, so no HIP error
+// state leaves the call.
+int32_t launched(hipError_t e) {
+  const hipError_t own = hipGetLastError();
+  return e == hipSuccess && own == hipSuccess ? Q4_OK : Q4_ERR_LAUNCH;
+}
 
 }  // namespace
 
@@ -90,6 +101,7 @@ Q4_API const char* q4_status_str(int32_t status) {
     case Q4_ERR_WORKSPACE: return "workspace missing (MoE), misaligned or too small";
     case Q4_ERR_DEVICE: return "no current HIP device or it is not gfx950";
     case Q4_ERR_LAUNCH: return "HIP runtime error at enqueue";
+    case Q4_ERR_PENDING: return "a HIP error from before the call is pending (left in place; nothing launched)";
     default: return "unknown status";
   }
 }
@@ -156,7 +168,7 @@ Q4_API int32_t q4_matmul_ex(const void* x, const void* w_q, const void* w_s, voi
     if (!aligned16(workspace) || workspace_bytes < need) return Q4_ERR_WORKSPACE;
     if (need > 0) partial = static_cast<float*>(workspace);
   }
-  if (int32_t s = check_device()) return s;
+  if (int32_t s = ready()) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = y_dtype == Q4_BF16;
   const auto* xp = static_cast<const uint16_t*>(x);
@@ -208,7 +220,7 @@ Q4_API int32_t q4_mx_matmul_ex(const void* x, const void* w_q, const void* w_e, 
     if (!aligned16(workspace) || workspace_bytes < need) return Q4_ERR_WORKSPACE;
     if (need > 0) partial = static_cast<float*>(workspace);
   }
-  if (int32_t s = check_device()) return s;
+  if (int32_t s = ready()) return s;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint8_t*>(w_q);
   const auto* ep = static_cast<const uint8_t*>(w_e);
@@ -234,7 +246,7 @@ Q4_API int32_t q4_dequantize(const void* w_q, const void* w_s, void* w_out, int3
   if (N == 0) return Q4_OK;
   if (!w_q || !w_s || !w_out) return Q4_ERR_NULL;
   if (!aligned16(w_q) || !aligned16(w_s) || !aligned16(w_out)) return Q4_ERR_ALIGN;
-  if (int32_t s = check_device()) return s;
+  if (int32_t s = ready()) return s;
   return launched(q4::launch_dequant(static_cast<const uint8_t*>(w_q),
                                      static_cast<const uint16_t*>(w_s), w_out,
                                      out_dtype == Q4_BF16, N, K,
@@ -269,7 +281,7 @@ Q4_API int32_t q4_moe_matmul(const void* x, const void* w_q, const void* w_s,
   const size_t need = q4_moe_workspace_bytes(T, topk, E, N);
   if (need == 0 || !workspace || !aligned16(workspace) || workspace_bytes < need)
     return Q4_ERR_WORKSPACE;
-  if (int32_t s = check_device()) return s;
+  if (int32_t s = ready()) return s;
   return launched(q4::launch_moe(static_cast<const uint16_t*>(x),
                                  static_cast<const uint8_t*>(w_q),
                                  static_cast<const uint16_t*>(w_s), topk_ids, topk_w, y, T, topk,
@@ -307,7 +319,7 @@ Q4_API int32_t q4_moe_ffn(const void* x, const void* w13_q, const void* w13_s, c
   const size_t need = q4_moe_ffn_workspace_bytes(T, topk, E, H, F);
   if (need == 0 || !workspace || !aligned16(workspace) || workspace_bytes < need)
     return Q4_ERR_WORKSPACE;
-  if (int32_t s = check_device()) return s;
+  if (int32_t s = ready()) return s;
   return launched(q4::launch_moe_ffn(
       static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w13_q),
       static_cast<const uint16_t*>(w13_s), static_cast<const uint8_t*>(w2_q),

@@ -56,6 +56,43 @@ struct CodeUnpacker {
   }
 };
 
+// Unpacks codes into exact bf16 (c - 8) values for the matrix cores, in k
+// order: o[i] holds elements 2i (low half) and 2i + 1 (high half).
+//
+// The same magic-exponent fp16 halves as CodeUnpacker (1024 + c for the low
+// nibble of each 16-bit half, 64 + c for the next one) are widened by
+// v_fma_mix_f32, which subtracts the constant in the same instruction:
+// h * 1 - 1032 (or - 72) is c - 8 exactly in fp32.  The multiplier is kept in a
+// register so the compiler cannot fold the multiply away and split the
+// instruction into a conversion and an add.  v_cvt_pk_bf16_f32 then packs two
+// small integers (exact in bf16).  Cost per dword: one shift, four
+// v_and_or_b32, eight v_fma_mix_f32 and four v_cvt_pk_bf16_f32.
+struct ExactBf16Unpacker {
+  uint32_t m_lo, m_hi;
+  float one;
+  __device__ __forceinline__ ExactBf16Unpacker()
+      : m_lo(opaque_vgpr(0x000F000Fu)), m_hi(opaque_vgpr(0x00F000F0u)),
+        one(__uint_as_float(opaque_vgpr(0x3F800000u))) {}
+  __device__ __forceinline__ void operator()(uint32_t d, uint32_t o[4]) const {
+    const uint32_t d8 = d >> 8;
+    const half2v h0 = __builtin_bit_cast(half2v, (d & m_lo) | 0x64006400u);   // e0, e4
+    const half2v h1 = __builtin_bit_cast(half2v, (d & m_hi) | 0x54005400u);   // e1, e5
+    const half2v h2 = __builtin_bit_cast(half2v, (d8 & m_lo) | 0x64006400u);  // e2, e6
+    const half2v h3 = __builtin_bit_cast(half2v, (d8 & m_hi) | 0x54005400u);  // e3, e7
+    const float lo = -1032.0f, hi = -72.0f;
+    o[0] = pack2(__builtin_fmaf((float)h0[0], one, lo), __builtin_fmaf((float)h1[0], one, hi));
+    o[1] = pack2(__builtin_fmaf((float)h2[0], one, lo), __builtin_fmaf((float)h3[0], one, hi));
+    o[2] = pack2(__builtin_fmaf((float)h0[1], one, lo), __builtin_fmaf((float)h1[1], one, hi));
+    o[3] = pack2(__builtin_fmaf((float)h2[1], one, lo), __builtin_fmaf((float)h3[1], one, hi));
+  }
+
+ private:
+  __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+    bf16x2v v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }

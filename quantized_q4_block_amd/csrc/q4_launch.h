@@ -44,7 +44,8 @@ hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* w
                           bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                           hipStream_t stream);
 
-// Many rows: dequant to bf16 in LDS + bf16 MFMA tiles (weights rounded to bf16).
+// Many rows: exact (c - 8) tiles in LDS + bf16 MFMA, fp32 block scales (exact
+// weights); any K that is a multiple of 32.
 // partial: NULL, or fp32 scratch of gemm_split_slices(M, N, K) * M * N floats
 // that lets a grid of few tiles be cut along K (K a multiple of 64).
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,

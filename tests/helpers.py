@@ -68,3 +68,13 @@ def assert_parity(y, y_ref, t, rtol=RTOL, extra=0.0, what=""):
         raise AssertionError(
             f"{what}: {len(bad)} of {ok.size} outputs outside tolerance; first at {i}: "
             f"y={y[i]!r} ref={y_ref[i]!r} bound={t[i]!r}; worst |err|/bound={np.nanmax(ratio):.3e}")
+
+
+def stratified_outputs(M: int, N: int):
+    """One output (m, n) of every column n, with m = (7 n + n // 128) mod M.
+    Within a 128-column tile m walks in steps of 7, so it passes through
+    every 128-row tile; over the whole width it reaches every row (the tests
+    that use it assert both coverages for their shapes)."""
+    ns = np.arange(N, dtype=np.int64)
+    ms = (7 * ns + ns // 128) % M
+    return ms, ns

@@ -71,6 +71,7 @@ def test_constants_match_header():
     d = _defines()
     for name in ("Q4_ABI_VERSION", "Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN",
                  "Q4_ERR_DTYPE", "Q4_ERR_WORKSPACE", "Q4_ERR_DEVICE", "Q4_ERR_LAUNCH",
+                 "Q4_ERR_PENDING",
                  "Q4_F32", "Q4_BF16", "Q4_PATH_GEMV", "Q4_PATH_MFMA", "Q4_PATH_SMALL"):
         assert getattr(q4, name) == d[name], name
     assert L.q4_abi_version() == d["Q4_ABI_VERSION"]
@@ -79,11 +80,11 @@ def test_constants_match_header():
 def test_status_strings():
     q4, L = _lib()
     seen = set()
-    for code in range(0, 8):
+    for code in range(0, 9):
         s = q4.q4_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert q4.q4_status_str(99) == "unknown status"
     assert q4.q4_status_str(-1) == "unknown status"
 

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synthetic
-from helpers import RTOL, assert_parity
+from helpers import RTOL, assert_parity, bf16_half_ulp, stratified_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -69,19 +69,26 @@ def test_mx_tiled(M, N, K):
     _check(c, f"mx tiled bf16 M={M} N={N} K={K}", out_dtype=torch.bfloat16)
 
 
-def test_mx_full_prefill_sampled():
-    """The prefill shape (512 x 34816 x 5120, bf16 out) on the tiled kernel;
-    the oracle takes 40 sampled rows against 384 sampled columns."""
+def test_mx_full_prefill_stratified():
+    """The prefill shape (512 x 34816 x 5120, bf16 out) on the tiled kernel,
+    against the oracle on one output of every column, spread so that every
+    row and every 128 x 128 output tile is hit."""
     cfg = synthetic.MX_CONFIGS["mx_prefill"]
-    c = synthetic.mx_case(cfg["seed"], cfg["M"], cfg["N"], cfg["K"])
+    M, N = cfg["M"], cfg["N"]
+    c = synthetic.mx_case(cfg["seed"], M, N, cfg["K"])
     y = _mx(c.x, c.w_q, c.w_e, torch.bfloat16)
     assert np.isfinite(y).all()
-    rng = np.random.default_rng(77)
-    ms = np.unique(np.concatenate([rng.integers(0, cfg["M"], 38), [0, cfg["M"] - 1]]))
-    ns = np.unique(np.concatenate([rng.integers(0, cfg["N"], 382), [0, cfg["N"] - 1]]))
-    y_ref, t = oracle.mx_matmul(c.x[ms], c.w_q[ns], c.w_e[ns])
-    assert_parity(y[np.ix_(ms, ns)], y_ref, t, RTOL, extra=2.0 ** -9 * np.abs(y_ref),
-                  what="mx_prefill sampled")
+    ms, ns = stratified_outputs(M, N)
+    assert len(set(ms.tolist())) == M
+    assert len(set(zip((ms // 128).tolist(), (ns // 128).tolist()))) == (M // 128) * (N // 128)
+    got = np.empty(N)
+    ref = np.empty(N)
+    bound = np.empty(N)
+    for m in range(M):
+        cols = ns[ms == m]
+        y_ref, t = oracle.mx_matmul(c.x[m:m + 1], c.w_q[cols], c.w_e[cols])
+        got[cols], ref[cols], bound[cols] = y[m, cols], y_ref[0], t[0]
+    assert_parity(got, ref, bound, RTOL, extra=bf16_half_ulp(ref), what="mx_prefill stratified")
 
 
 def _mx_ex(x, w_q, w_e, out_dtype=torch.float32, workspace="auto"):

@@ -6,9 +6,8 @@ All calls go through the C ABI (via the binding).  The bars:
   * matmul: |y - y_ref| <= 1e-3 * sum_k |x_k * w_k| per output, with y_ref
     the oracle's double result; a bf16 output adds half a bf16 ulp of y_ref
     (the rounding of the store itself);
-  * the matrix-core path (M > 8) is compared with the oracle over the
-    bf16-rounded weights it is defined on (same bar), and, at the prefill
-    workload's full size, also with the exact-weight oracle;
+  * every path, the tiled matrix-core one included, is compared with the
+    exact-weight oracle (the weights (c-8)*s unrounded);
   * integer-valued special cases (identity activations, zero codes, closed
     forms) are compared exactly.
 """
@@ -21,7 +20,7 @@ import torch
 import oracle
 import synthetic
 from gpu_util import dev, host, matmul, matmul_ex, moe
-from helpers import RTOL, assert_parity, bf16_half_ulp, load_golden
+from helpers import RTOL, assert_parity, bf16_half_ulp, load_golden, stratified_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +33,7 @@ def _check_dense(d, out_dtype=F32, what=""):
     M, K = d.x.shape
     N = d.w_q.shape[0]
     y = matmul(d.x, d.w_q, d.w_s, out_dtype)
-    # only the tiled path rounds weights to bf16
-    mfma = q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
-    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=mfma)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     extra = bf16_half_ulp(y_ref) if out_dtype == BF16 else 0.0
     assert_parity(y, y_ref, t, RTOL, extra, what=what)
     return y, y_ref, t
@@ -231,7 +228,7 @@ def test_mfma_split_parity(M, N, K):
     assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
     assert q4.q4_matmul_workspace_bytes(M, N, K) >= 2 * M * N * 4
     d = synthetic.dense_case(4100 + M + N, M, N, K)
-    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=True)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     y = matmul_ex(d.x, d.w_q, d.w_s, F32)
     assert_parity(y, y_ref, t, RTOL, what=f"mfma split M={M} N={N} K={K}")
     yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
@@ -241,19 +238,18 @@ def test_mfma_split_parity(M, N, K):
 
 
 # With a workspace, 33..128 rows on weight matrices of at least 2^24 entries
-# leave the few-row slabs for the tiled kernel cut along K (weights rounded
-# to bf16 there); without one the same shapes stay on the slabs (exact).
+# leave the few-row slabs for the tiled kernel cut along K; without one the
+# same shapes stay on the slabs.  Both use exact weights.
 @pytest.mark.parametrize("M,N,K", [(33, 4096, 4096 + 64 * 3), (100, 5120, 5120), (128, 2048, 8192)])
 def test_slab_shapes_with_a_workspace(M, N, K):
     assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_SMALL
     assert q4.q4_matmul_path_ex(M, N, K, True) == q4.Q4_PATH_MFMA
     d = synthetic.dense_case(4300 + M, M, N, K)
-    y_ref_b, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=True)
-    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
-    assert_parity(y, y_ref_b, t, RTOL, what=f"slab shape tiled M={M} N={N} K={K}")
-    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
-    assert_parity(yb, y_ref_b, t, RTOL, bf16_half_ulp(y_ref_b), what=f"slab shape tiled bf16 M={M}")
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"slab shape tiled M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"slab shape tiled bf16 M={M}")
     y0 = matmul_ex(d.x, d.w_q, d.w_s, F32, workspace=None)
     assert_parity(y0, y_ref, t, RTOL, what=f"slab shape slabs M={M} N={N} K={K}")
 
@@ -273,10 +269,8 @@ def test_prefill_down_split_sampled_and_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     y = host(y1)
-    rng = np.random.default_rng(98)
-    ms = np.concatenate([rng.integers(0, M, 2000), [0, M - 1]])
-    ns = np.concatenate([rng.integers(0, N, 2000), [N - 1, 0]])
-    y_ref, t = oracle.matmul_sampled(d.x, d.w_q, d.w_s, ms, ns, bf16_weights=True)
+    ms, ns = stratified_outputs(M, N)
+    y_ref, t = oracle.matmul_sampled(d.x, d.w_q, d.w_s, ms, ns)
     assert_parity(y[ms, ns], y_ref, t, RTOL, bf16_half_ulp(y_ref), what="prefill down split")
 
 
@@ -284,18 +278,20 @@ def test_prefill_down_split_sampled_and_deterministic():
 
 
 def test_identity_activations_give_dequantised_weights():
-    """x = I (K x K): y[m][n] = w[n][m]; bf16-rounded weights on the tiled
-    matrix-core path, exact fp32 weights on the few-row matrix-core path and
-    the matrix-vector path (row slices)."""
+    """x = I (K x K): y[m][n] = w[n][m], the exact fp32 weights, on the tiled
+    matrix-core path (M = 256; in bf16 output, their nearest-even rounding),
+    the few-row matrix-core path and the matrix-vector path (row slices)."""
     K, N = 256, 192
     d = synthetic.dense_case(5000, 1, N, K)
     eye = np.zeros((K, K), dtype=np.uint16)
     eye[np.arange(K), np.arange(K)] = 0x3F80
-    y = matmul(eye, d.w_q, d.w_s)                      # M = 256: MFMA
-    wb = oracle.dequant_bf16_bits(d.w_q, d.w_s)
-    wbf = (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    assert np.array_equal(y, wbf.T)
+    assert q4.q4_matmul_path(K, N, K) == q4.Q4_PATH_MFMA
     wf = oracle.dequant_f32(d.w_q, d.w_s).astype(np.float64)
+    y = matmul(eye, d.w_q, d.w_s)                      # M = 256: tiled
+    assert np.array_equal(y, wf.T)
+    yb = matmul(eye, d.w_q, d.w_s, BF16)
+    wb = oracle.dequant_bf16_bits(d.w_q, d.w_s)
+    assert np.array_equal(yb, (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64).T)
     for m0 in range(0, K, 8):                           # M = 8 slices: few-row path
         ys = matmul(eye[m0:m0 + 8], d.w_q, d.w_s)
         assert np.array_equal(ys, wf[:, m0:m0 + 8].T)
@@ -362,6 +358,53 @@ def test_closed_form_constant(M):
     assert np.all(y == K * 1.5 * 5 * 2.0 ** -4)
 
 
+@pytest.mark.parametrize("M,K", [(129, 512), (256, 5120), (300, 2048 + 32)])
+@pytest.mark.parametrize("code,factor", [(0x99, 1), (0xFF, 7), (0x00, -8)])
+def test_tiled_closed_form_scale_outside_bf16(M, K, code, factor):
+    """Tiled path, x = 1, every code the same, scale fp16 0x3C03 = 1.0029296875
+    (11 significant bits, not a bf16 value): y = K * (c - 8) * 1.0029296875
+    exactly (every partial sum is a small multiple of the scale)."""
+    N = 257
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    x = np.full((M, K), 0x3F80, dtype=np.uint16)
+    w_q = np.full((N, K // 2), code, dtype=np.uint8)
+    w_s = np.full((N, K // 32), 0x3C03, dtype=np.uint16)
+    y = matmul(x, w_q, w_s)
+    assert np.all(y == K * factor * 1.0029296875)
+    y_ref, t = oracle.matmul(x, w_q, w_s)
+    assert_parity(y, y_ref, t, RTOL, what="tiled closed form")
+
+
+@pytest.mark.parametrize("kind", ["wide", "subnormal", "huge", "tiny", "sparse"])
+def test_tiled_activation_ranges_and_sparse_codes(kind):
+    """The tiled path on inputs where rounded weights or scaled activations
+    would break the bar: an activation 2^63 times the rest whose weight is
+    zero, bf16 subnormal activations, both ends of bf16's range, and nearly
+    all codes 8 (sum |x w| tiny next to sum |x|)."""
+    M, N, K = 160, 200, 2048
+    d = synthetic.dense_case(5400, M, N, K)
+    x, w_q = d.x.copy(), d.w_q.copy()
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    if kind == "wide":
+        x[:, 7] = 0x5F00            # ~9.2e18
+        w_q[:, 3] = (w_q[:, 3] & 0x0F) | 0x80   # its weight (k = 7, high nibble) is 0
+    elif kind == "subnormal":
+        x[:, 100] = 0x0003
+        x[::3, 5] = 0x8001
+    elif kind == "huge":
+        x = synthetic.f32_to_bf16_bits(xf * np.float32(2.0 ** 100))
+    elif kind == "tiny":
+        x = synthetic.f32_to_bf16_bits(xf * np.float32(2.0 ** -100))
+    else:
+        rng = np.random.default_rng(8)
+        hit = rng.random(w_q.shape) < 0.01
+        w_q = np.where(hit, d.w_q, 0x88).astype(np.uint8)
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    y = matmul(x, w_q, d.w_s)
+    y_ref, t = oracle.matmul(x, w_q, d.w_s)
+    assert_parity(y, y_ref, t, RTOL, what=f"tiled {kind}")
+
+
 # ------------------------------------------------------ full-size configs
 
 
@@ -386,19 +429,17 @@ def test_batched_down_full_size():
     assert_parity(y, y_ref, t, RTOL, what="batched_down through q4_matmul_ex")
 
 
-def test_prefill_full_size_sampled():
+def test_prefill_full_size_stratified():
+    """The prefill workload (512 x 34816 x 5120, bf16 output) against the
+    exact-weight oracle on one output of every column, spread so that every
+    row and every 128 x 128 output tile is hit."""
     d, y = _full_dense("prefill", BF16)
     M, N = y.shape
-    rng = np.random.default_rng(99)
-    ms = np.concatenate([rng.integers(0, M, 3000), [0, M - 1, M - 1, 0]])
-    ns = np.concatenate([rng.integers(0, N, 3000), [0, N - 1, 0, N - 1]])
-    got = y[ms, ns]
-    extra = None
-    for bw in (True, False):
-        y_ref, t = oracle.matmul_sampled(d.x, d.w_q, d.w_s, ms, ns, bf16_weights=bw)
-        extra = bf16_half_ulp(y_ref)
-        # with the exact weights this is the stated bar 1e-3 * sum |x w|
-        assert_parity(got, y_ref, t, RTOL, extra, what=f"prefill bf16_weights={bw}")
+    ms, ns = stratified_outputs(M, N)
+    assert len(set(ms.tolist())) == M and len(set(ns.tolist())) == N
+    assert len(set(zip((ms // 128).tolist(), (ns // 128).tolist()))) == (M // 128) * (N // 128)
+    y_ref, t = oracle.matmul_sampled(d.x, d.w_q, d.w_s, ms, ns)
+    assert_parity(y[ms, ns], y_ref, t, RTOL, bf16_half_ulp(y_ref), what="prefill")
     assert np.isfinite(y).all()
 
 
@@ -485,8 +526,7 @@ def test_output_guard_bands_untouched(M, out_dtype):
     q4.q4_matmul(dev(d.x), dev(d.w_q), dev(d.w_s), out=y)
     torch.cuda.synchronize()
     assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + M * N:] == 7.0)
-    mfma = q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
-    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=mfma)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     extra = bf16_half_ulp(y_ref) if out_dtype == BF16 else 0.0
     assert_parity(host(y), y_ref, t, RTOL, extra, what="guard")
 
@@ -535,6 +575,5 @@ def test_split_calls_on_a_non_default_stream(M, N, K):
         work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)
         y = q4.q4_matmul_ex(x, wq, ws, workspace=work, stream=s)
     s.synchronize()
-    mfma = q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
-    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s, bf16_weights=mfma)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     assert_parity(host(y), y_ref, t, RTOL, what=f"split on a stream M={M}")
