@@ -149,6 +149,18 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _scratch(torch, nbytes, device, stream):
+    """A temporary workspace for a call enqueued on `stream` (None: the current
+    stream).  It is allocated with that stream current, so the caching
+    allocator gives the block to another allocation only in that stream's
+    order, after the call's kernels, even when the caller's current stream is
+    another one."""
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -248,7 +260,7 @@ def q4_mx_matmul_ex(x, w_q, w_e, out=None, out_dtype=None, workspace="auto", str
         if workspace != "auto":
             raise ValueError('workspace must be "auto", None or a device tensor')
         need = q4_mx_matmul_workspace_bytes(M, N, K)
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+        workspace = _scratch(torch, need, x.device, stream) if need else None
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.q4_mx_matmul_ex(_ptr(x), _ptr(w_q), _ptr(w_e), _ptr(out), _out_code(out.dtype),
                              M, N, K, _ptr(workspace), nbytes, _stream_handle(stream, x.device))
@@ -270,7 +282,7 @@ def q4_matmul_ex(x, w_q, w_s, out=None, out_dtype=None, workspace="auto", stream
         if workspace != "auto":
             raise ValueError('workspace must be "auto", None or a device tensor')
         need = q4_matmul_workspace_bytes(M, N, K)
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+        workspace = _scratch(torch, need, x.device, stream) if need else None
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.q4_matmul_ex(_ptr(x), _ptr(w_q), _ptr(w_s), _ptr(out), _out_code(out.dtype),
                           M, N, K, _ptr(workspace), nbytes, _stream_handle(stream, x.device))
@@ -305,8 +317,7 @@ def q4_moe_workspace_bytes(T: int, topk: int, E: int, N: int) -> int:
     return int(lib.q4_moe_workspace_bytes(int(T), int(topk), int(E), int(N)))
 
 
-def q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None, stream=None):
-    """y[T][N] = sum_j topk_w[t][j] * x[t] . dequant(W[topk_ids[t][j]])^T (fp32)."""
+def _moe_args(x, w_q, w_s, topk_ids, topk_w, out):
     torch = _torch()
     _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
     _check_dev(w_q, "w_q", (torch.uint8,), 3)
@@ -326,9 +337,17 @@ def q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None, strea
         _check_dev(out, "out", (torch.float32,), 2)
         if tuple(out.shape) != (T, N):
             raise ValueError("out has the wrong shape")
+    return T, topk, E, N, K, out
+
+
+def q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None, stream=None):
+    """y[T][N] = sum_j topk_w[t][j] * x[t] . dequant(W[topk_ids[t][j]])^T (fp32).
+    workspace None allocates one (a torch tensor on the stream the call runs on)."""
+    torch = _torch()
+    T, topk, E, N, K, out = _moe_args(x, w_q, w_s, topk_ids, topk_w, out)
     need = q4_moe_workspace_bytes(T, topk, E, N)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(torch, max(need, 1), x.device, stream)
     st = lib.q4_moe_matmul(_ptr(x), _ptr(w_q), _ptr(w_s), _ptr(topk_ids), _ptr(topk_w),
                            _ptr(out), T, topk, E, N, K, _ptr(workspace),
                            workspace.numel() * workspace.element_size(),
@@ -372,7 +391,7 @@ def q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None, workspac
             raise ValueError("out has the wrong shape")
     need = q4_moe_ffn_workspace_bytes(T, topk, E, H, F)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(torch, max(need, 1), x.device, stream)
     st = lib.q4_moe_ffn(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
                         _ptr(topk_ids), _ptr(topk_w), _ptr(out), T, topk, E, H, F,
                         _ptr(workspace), workspace.numel() * workspace.element_size(),

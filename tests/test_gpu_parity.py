@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import synthetic
-from gpu_util import dev, host, matmul, matmul_ex, moe
+from gpu_util import DEV, dev, host, matmul, matmul_ex, moe
 from helpers import RTOL, assert_parity, bf16_half_ulp, load_golden, stratified_outputs
 
 pytestmark = pytest.mark.gpu
@@ -577,3 +577,29 @@ def test_split_calls_on_a_non_default_stream(M, N, K):
     s.synchronize()
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     assert_parity(host(y), y_ref, t, RTOL, what=f"split on a stream M={M}")
+
+
+def test_auto_workspace_on_a_stream_that_is_not_current():
+    """A call given stream=s while another stream is current: the binding's
+    temporary workspace belongs to s, so allocations made on the current
+    stream right after the call (which reuse freed blocks) cannot take it
+    while the call's kernels still run."""
+    M, N, K = 300, 200, 64 * 40
+    d = synthetic.dense_case(7500, M, N, K)
+    m = synthetic.moe_case(7501, 8, 4, 16, 512, 1024)
+    x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
+    mx, mwq, mws, mids, mg = dev(m.x), dev(m.w_q), dev(m.w_s), dev(m.ids), dev(m.gates)
+    assert q4.q4_matmul_workspace_bytes(M, N, K) > 0
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    assert torch.cuda.current_stream() != s
+    y = q4.q4_matmul_ex(x, wq, ws, stream=s)
+    ym = q4.q4_moe_matmul(mx, mwq, mws, mids, mg, stream=s)
+    junk = [torch.full((1 << 20,), 1e30, device=DEV) for _ in range(8)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    assert_parity(host(y), y_ref, t, RTOL, what="matmul_ex on a stream that is not current")
+    y_ref, t = oracle.moe(m.x, m.w_q, m.w_s, m.ids, m.gates)
+    assert_parity(host(ym), y_ref, t, RTOL, what="moe on a stream that is not current")
