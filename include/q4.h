@@ -85,6 +85,8 @@ extern "C" {
 #define Q4_ERR_LAUNCH    7  /* the HIP runtime reported an error at enqueue */
 #define Q4_ERR_PENDING   8  /* a HIP error from before the call was pending: left
                                in place, nothing launched (ABI version 8) */
+#define Q4_ERR_SCRATCH   9  /* needs more than Q4_MOE_NOALLOC_MAX_BYTES of the
+                               built-in scratch (q4_moe_matmul_noalloc) */
 
 /* Output dtypes. */
 #define Q4_F32  0
@@ -197,6 +199,25 @@ Q4_API int32_t q4_moe_matmul(const void *x, const void *w_q, const void *w_s,
                              int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes,
                              q4_stream_t stream);
+
+/* q4_moe_matmul without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops or
+ * harnesses that forbid allocation).  Same arguments, checks and result as
+ * q4_moe_matmul; the workspace is the library's own scratch array, one per
+ * GPU, of Q4_MOE_NOALLOC_MAX_BYTES bytes, held from the first call on that
+ * GPU until the process ends.  A call whose q4_moe_workspace_bytes(T, topk,
+ * E, N) exceeds that returns Q4_ERR_SCRATCH (after the argument checks,
+ * before anything is enqueued).  Every call on one GPU shares its array:
+ * calls that may overlap on one GPU (different streams, different host
+ * threads) race and must be serialised by the caller; calls on one stream
+ * are ordered.  Nothing in the array needs to start at zero (each call
+ * rebuilds what it reads).  Allocates nothing (no hipMalloc, no library
+ * allocation).  ABI version 8. */
+#define Q4_MOE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+Q4_API int32_t q4_moe_matmul_noalloc(const void *x, const void *w_q, const void *w_s,
+                                     const int32_t *topk_ids, const float *topk_w,
+                                     float *y, int64_t T, int64_t topk, int64_t E,
+                                     int64_t N, int64_t K, q4_stream_t stream);
 
 /* Device workspace (bytes) q4_moe_ffn needs for these sizes; 0 if a size is
  * negative or the size overflows. */

@@ -18,6 +18,7 @@ of the C ABI in ``include/q4.h``:
     q4_moe_workspace_bytes(T, topk, E, N)   -> int
     q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None,
                   stream=None) -> y
+    q4_moe_matmul_noalloc(x, w_q, w_s, topk_ids, topk_w, out=None, stream=None) -> y
     q4_moe_ffn_workspace_bytes(T, topk, E, H, F) -> int
     q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None,
                workspace=None, stream=None) -> y
@@ -52,6 +53,8 @@ Q4_ERR_WORKSPACE = 5
 Q4_ERR_DEVICE = 6
 Q4_ERR_LAUNCH = 7
 Q4_ERR_PENDING = 8
+Q4_ERR_SCRATCH = 9
+Q4_MOE_NOALLOC_MAX_BYTES = 8 << 20
 Q4_F32 = 0
 Q4_BF16 = 1
 Q4_PATH_GEMV = 0
@@ -62,7 +65,7 @@ __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul_path_ex",
     "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
-    "q4_moe_matmul", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
+    "q4_moe_matmul", "q4_moe_matmul_noalloc", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
     "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
 ]
 
@@ -100,6 +103,8 @@ def _open():
     L.q4_moe_workspace_bytes.restype = ctypes.c_size_t
     L.q4_moe_matmul.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     L.q4_moe_matmul.restype = I32
+    L.q4_moe_matmul_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
+    L.q4_moe_matmul_noalloc.restype = I32
     L.q4_moe_ffn_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
     L.q4_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
     L.q4_moe_ffn.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t,
@@ -354,6 +359,17 @@ def q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None, strea
                            _stream_handle(stream, x.device))
     if st != Q4_OK:
         raise Q4Error(st, "q4_moe_matmul")
+    return out
+
+
+def q4_moe_matmul_noalloc(x, w_q, w_s, topk_ids, topk_w, out=None, stream=None):
+    """q4_moe_matmul with the library's built-in scratch as its workspace (no
+    device allocation by the library; calls that overlap on one GPU race)."""
+    T, topk, E, N, K, out = _moe_args(x, w_q, w_s, topk_ids, topk_w, out)
+    st = lib.q4_moe_matmul_noalloc(_ptr(x), _ptr(w_q), _ptr(w_s), _ptr(topk_ids), _ptr(topk_w),
+                                   _ptr(out), T, topk, E, N, K, _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_moe_matmul_noalloc")
     return out
 
 

@@ -102,6 +102,7 @@ Q4_API const char* q4_status_str(int32_t status) {
     case Q4_ERR_DEVICE: return "no current HIP device or it is not gfx950";
     case Q4_ERR_LAUNCH: return "HIP runtime error at enqueue";
     case Q4_ERR_PENDING: return "a HIP error from before the call is pending (left in place; nothing launched)";
+    case Q4_ERR_SCRATCH: return "the call needs more than the library's built-in scratch (no-allocation entry point)";
     default: return "unknown status";
   }
 }
@@ -286,6 +287,34 @@ Q4_API int32_t q4_moe_matmul(const void* x, const void* w_q, const void* w_s,
                                  static_cast<const uint8_t*>(w_q),
                                  static_cast<const uint16_t*>(w_s), topk_ids, topk_w, y, T, topk,
                                  E, N, K, workspace, static_cast<hipStream_t>(stream)));
+}
+
+static_assert(Q4_MOE_NOALLOC_MAX_BYTES == q4::kMoeScratchBytes,
+              "the header's scratch limit is the array's size");
+
+Q4_API int32_t q4_moe_matmul_noalloc(const void* x, const void* w_q, const void* w_s,
+                                     const int32_t* topk_ids, const float* topk_w, float* y,
+                                     int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
+                                     q4_stream_t stream) {
+  if (T < 0 || topk < 0 || E < 0) return Q4_ERR_SHAPE;
+  if (int32_t s = check_weights(N, K)) return s;
+  int64_t P, tk, en, enk;
+  if (!mul_ok(T, topk, &P) || !mul_ok(T, K, &tk) || !mul_ok(E, N, &en) || !mul_ok(en, K, &enk))
+    return Q4_ERR_SHAPE;
+  if ((P < E ? P : E) > 65535) return Q4_ERR_SHAPE;
+  if (T == 0 || N == 0) return Q4_OK;
+  if (!y || !x || (topk > 0 && (!topk_ids || !topk_w))) return Q4_ERR_NULL;
+  if (E > 0 && topk > 0 && (!w_q || !w_s)) return Q4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_w && !aligned16(topk_w)) || (w_q && !aligned16(w_q)) || (w_s && !aligned16(w_s)))
+    return Q4_ERR_ALIGN;
+  const size_t need = q4_moe_workspace_bytes(T, topk, E, N);
+  if (need == 0 || need > Q4_MOE_NOALLOC_MAX_BYTES) return Q4_ERR_SCRATCH;
+  if (int32_t s = ready()) return s;
+  return launched(q4::launch_moe_noalloc(
+      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w_q),
+      static_cast<const uint16_t*>(w_s), topk_ids, topk_w, y, T, topk, E, N, K,
+      static_cast<hipStream_t>(stream)));
 }
 
 Q4_API size_t q4_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H,

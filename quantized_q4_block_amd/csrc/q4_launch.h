@@ -66,6 +66,13 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
                       int64_t topk, int64_t E, int64_t N, int64_t K, void* workspace,
                       hipStream_t stream);
 
+// launch_moe with the workspace in the library's per-device scratch array
+// (at most kMoeScratchBytes of it; hipErrorInvalidValue past that).
+constexpr size_t kMoeScratchBytes = size_t(8) << 20;
+hipError_t launch_moe_noalloc(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
+                              const int32_t* ids, const float* gates, float* y, int64_t T,
+                              int64_t topk, int64_t E, int64_t N, int64_t K, hipStream_t stream);
+
 // Routed expert FFN; the MoE layout for N = H followed by the SwiGLU
 // outputs act [T * topk][F] (fp32).  H and F at most 8192 (4 stages).
 struct MoeFfnLayout {

@@ -23,6 +23,8 @@
 //  3. weighted sum: y[t][n] = sum over slots j in order of g[t][j] * partial.
 // Results are bit-identical from run to run: atomics only assign bucket
 // slots (integers), never sum floating point.
+#include <atomic>
+
 #include "q4_device.h"
 #include "q4_gemv.h"
 #include "q4_launch.h"
@@ -448,6 +450,49 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
     if (err != hipSuccess) return err;
   }
   return moe_combine(ids, gates, partial, y, T, topk, E, N, stream);
+}
+
+// ---- the MoE call without a caller-owned workspace --------------------------
+//
+// For callers that cannot allocate device memory: the workspace lives in this
+// file-scope array, one copy per GPU, held until the process ends.  Every call
+// on a GPU shares that GPU's copy (calls that overlap on one GPU race); the
+// prep kernel rebuilds everything the later kernels read on every call, so
+// nothing needs clearing.  In host code the name `scratch` is a host-side
+// stand-in, not a device address: the device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) on
+// its first call and kept per device.
+static __device__ __align__(256) unsigned char scratch[kMoeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t moe_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_moe_noalloc(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
+                              const int32_t* ids, const float* gates, float* y, int64_t T,
+                              int64_t topk, int64_t E, int64_t N, int64_t K, hipStream_t stream) {
+  if (moe_workspace_layout(T, topk, E, N).total > kMoeScratchBytes) return hipErrorInvalidValue;
+  void* p = nullptr;
+  const hipError_t e = moe_scratch_address(&p);
+  if (e != hipSuccess) return e;
+  return launch_moe(x, wq, ws, ids, gates, y, T, topk, E, N, K, p, stream);
 }
 
 MoeFfnLayout moe_ffn_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t H,

@@ -49,7 +49,8 @@ def test_header_declares_the_abi():
     assert set(syms) == {"q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul_path_ex",
                          "q4_matmul",
                          "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
-                         "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_ffn_workspace_bytes",
+                         "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_matmul_noalloc",
+                         "q4_moe_ffn_workspace_bytes",
                          "q4_moe_ffn", "q4_mx_matmul", "q4_mx_matmul_workspace_bytes",
                          "q4_mx_matmul_ex"}
 
@@ -71,7 +72,7 @@ def test_constants_match_header():
     d = _defines()
     for name in ("Q4_ABI_VERSION", "Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN",
                  "Q4_ERR_DTYPE", "Q4_ERR_WORKSPACE", "Q4_ERR_DEVICE", "Q4_ERR_LAUNCH",
-                 "Q4_ERR_PENDING",
+                 "Q4_ERR_PENDING", "Q4_ERR_SCRATCH",
                  "Q4_F32", "Q4_BF16", "Q4_PATH_GEMV", "Q4_PATH_MFMA", "Q4_PATH_SMALL"):
         assert getattr(q4, name) == d[name], name
     assert L.q4_abi_version() == d["Q4_ABI_VERSION"]
@@ -80,11 +81,11 @@ def test_constants_match_header():
 def test_status_strings():
     q4, L = _lib()
     seen = set()
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = q4.q4_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert q4.q4_status_str(99) == "unknown status"
     assert q4.q4_status_str(-1) == "unknown status"
 
