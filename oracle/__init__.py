@@ -85,6 +85,12 @@ def _load():
     lib.oracle_e2m1_value.restype = ctypes.c_double
     lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
     lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_rmsnorm.argtypes = [P, P, ctypes.c_double, I64, I64, P]
+    lib.oracle_bf16_half_ulp.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_half_ulp.restype = ctypes.c_double
+    lib.oracle_rmsnorm_matmul.argtypes = [P, P, ctypes.c_double, P, P, I64, I64, I64, P, P, P]
+    lib.oracle_rmsnorm_matmul_sampled.argtypes = [P, P, ctypes.c_double, P, P, I64, I64, I64,
+                                                  P, P, I64, P, P, P]
     lib.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
     lib.oracle_mx_matmul.argtypes = [P, P, P, I64, I64, I64, P, P]
     _lib = lib
@@ -271,3 +277,66 @@ def mx_matmul(x: np.ndarray, w_q: np.ndarray, w_e: np.ndarray):
     t = np.empty((M, N), dtype=np.float64)
     _load().oracle_mx_matmul(_ptr(x), _ptr(wq), _ptr(we), M, N, K, _ptr(y), _ptr(t))
     return y, t
+
+
+# ---- RMSNorm prologue ------------------------------------------------------
+
+def bf16_half_ulp(v: float) -> float:
+    """Half a bf16 unit in the last place of |v|."""
+    return float(_load().oracle_bf16_half_ulp(float(v)))
+
+
+def _check_norm(x, gamma):
+    x = _c(x, np.uint16)
+    gamma = _c(gamma, np.uint16)
+    if x.ndim != 2 or gamma.shape != (x.shape[1],):
+        raise ValueError("x must be [M][K] and gamma [K]")
+    return x, gamma
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """double [M][K]: x[m,k] * gamma[k] / sqrt(mean_k x[m,k]^2 + eps)."""
+    x, gamma = _check_norm(x, gamma)
+    M, K = x.shape
+    out = np.empty((M, K), dtype=np.float64)
+    _load().oracle_rmsnorm(_ptr(x), _ptr(gamma), float(eps), M, K, _ptr(out))
+    return out
+
+
+def rmsnorm_matmul(x: np.ndarray, gamma: np.ndarray, eps: float, w_q: np.ndarray,
+                   w_s: np.ndarray):
+    """(y, t, u): double [M][N] product of the normalised activations with
+    dequant(W), sum_k |x'*w|, and sum_k hulp(x'_k)*|w_k| (what rounding the
+    normalised activations to bf16 can move y by)."""
+    N, K = _check_w(w_q, w_s)
+    x, gamma = _check_norm(x, gamma)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x has the wrong K")
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    y, t, u = (np.empty((M, N), dtype=np.float64) for _ in range(3))
+    _load().oracle_rmsnorm_matmul(_ptr(x), _ptr(gamma), float(eps), _ptr(wq), _ptr(ws), M, N, K,
+                                  _ptr(y), _ptr(t), _ptr(u))
+    return y, t, u
+
+
+def rmsnorm_matmul_sampled(x: np.ndarray, gamma: np.ndarray, eps: float, w_q: np.ndarray,
+                           w_s: np.ndarray, ms: np.ndarray, ns: np.ndarray):
+    """(y, t, u) of rmsnorm_matmul for the outputs (ms[i], ns[i]) only."""
+    N, K = _check_w(w_q, w_s)
+    x, gamma = _check_norm(x, gamma)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x has the wrong K")
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    if ms.shape != ns.shape or ms.ndim != 1:
+        raise ValueError("ms and ns must be 1-D and equal length")
+    if ms.size and (ms.min() < 0 or ms.max() >= M or ns.min() < 0 or ns.max() >= N):
+        raise ValueError("sample index out of range")
+    wq, ws = _c(w_q, np.uint8), _c(w_s, np.uint16)
+    y, t, u = (np.empty(ms.size, dtype=np.float64) for _ in range(3))
+    _load().oracle_rmsnorm_matmul_sampled(_ptr(x), _ptr(gamma), float(eps), _ptr(wq), _ptr(ws),
+                                          M, N, K, _ptr(ms), _ptr(ns), ms.size, _ptr(y), _ptr(t),
+                                          _ptr(u))
+    return y, t, u

@@ -40,11 +40,24 @@
  *     byte j and k = 2j+1 in the HIGH nibble; rows are K/2 bytes apart;
  *   - scales of row n are K/32 consecutive fp16 values;
  *   - activations are bf16, row-major [M][K];
- *   - the prefill (matrix-core) variant rounds each dequantised weight to
- *     bf16, nearest-even, before the product (oracle option bf16_weights);
+ *   - oracle option bf16_weights rounds each dequantised weight to bf16,
+ *     nearest-even, before the product (a pinned variant of the oracle; the
+ *     product paths use the weights exactly);
  *   - FFN: gate and up weights of an expert are one [2F][H] matrix whose row
  *     2f is the gate row and row 2f+1 the up row of hidden unit f; the
  *     SwiGLU output a_f feeds the down product unrounded.
+ *
+ * RMSNorm prologue.  The specialised-runtime spec's first measured kernel is
+ * "one quantized GEMM plus fused RMSNorm" (section "Feasibility gate"; also
+ * Phase 1 of "Development sequence").  The pages do not define RMSNorm; the
+ * reading taken is the usual one, per activation row m:
+ *         r_m      = 1 / sqrt( (1/K) * sum_k x[m,k]^2 + eps )
+ *         x'[m,k]  = x[m,k] * r_m * gamma[k]          (gamma: bf16 [K])
+ *         y[m,n]   = sum_k x'[m,k] * w[n,k],  t[m,n] = sum_k |x'[m,k] * w[n,k]|
+ *         u[m,n]   = sum_k hulp(x'[m,k]) * |w[n,k]|
+ * where hulp(v) is half a bf16 unit in the last place of v: the normalised
+ * activations are the matmul's activation operand, whose type is bf16, and u
+ * is what their rounding to bf16 can move y by.  Everything in double.
  *
  * 4-bit float blocks.  The specialised-runtime spec names a 4-bit float block
  * format as the performance path after groupwise-int weights (section "Target
@@ -350,4 +363,81 @@ void oracle_moe_ffn(const uint16_t *x, const uint8_t *w13q, const uint16_t *w13s
     }
     free(a);
     free(da);
+}
+
+/* ---- RMSNorm prologue + matmul ------------------------------------------ */
+
+/* Half a bf16 unit in the last place of |v|: 8 significant bits in the
+ * normal range (|v| >= 2^-126), a fixed quantum of 2^-133 below it. */
+static double bf16_half_ulp(double v) {
+    double a = fabs(v);
+    if (a == 0.0 || isnan(a) || isinf(a))
+        return a == 0.0 ? ldexp(1.0, -134) : a;
+    int e;
+    frexp(a, &e);                       /* a = m * 2^e, m in [0.5, 1) */
+    if (e - 1 < -126)
+        return ldexp(1.0, -134);
+    return ldexp(1.0, (e - 1) - 8);     /* ulp 2^(e-1-7), half of it */
+}
+
+/* x' = RMSNorm(x) * gamma as double [M][K]. */
+void oracle_rmsnorm(const uint16_t *x, const uint16_t *gamma, double eps, int64_t M,
+                    int64_t K, double *xn) {
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = bf16_value(x[m * K + k]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            xn[m * K + k] = bf16_value(x[m * K + k]) * r * bf16_value(gamma[k]);
+    }
+}
+
+double oracle_bf16_half_ulp(double v) { return bf16_half_ulp(v); }
+
+/* One output of the normalised product: xn_row is a row of oracle_rmsnorm. */
+static void rms_dot_one(const double *xn_row, const uint8_t *wq_row, const uint16_t *ws_row,
+                        int64_t K, double *y, double *t, double *u) {
+    double acc = 0.0, mag = 0.0, rnd = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double w = weight_at(wq_row, ws_row, k, 0);
+        double p = xn_row[k] * w;
+        acc += p;
+        mag += fabs(p);
+        rnd += bf16_half_ulp(xn_row[k]) * fabs(w);
+    }
+    *y = acc;
+    *t = mag;
+    *u = rnd;
+}
+
+/* y, t, u: double [M][N] (see the header). */
+void oracle_rmsnorm_matmul(const uint16_t *x, const uint16_t *gamma, double eps,
+                           const uint8_t *wq, const uint16_t *ws, int64_t M, int64_t N,
+                           int64_t K, double *y, double *t, double *u) {
+    double *xn = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    oracle_rmsnorm(x, gamma, eps, M, K, xn);
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m)
+            rms_dot_one(xn + m * K, wq + n * (K / 2), ws + n * (K / Q4O_BLOCK), K,
+                        &y[m * N + n], &t[m * N + n], &u[m * N + n]);
+    free(xn);
+}
+
+/* Only the listed outputs (ms[i], ns[i]); y, t, u: double [count]. */
+void oracle_rmsnorm_matmul_sampled(const uint16_t *x, const uint16_t *gamma, double eps,
+                                   const uint8_t *wq, const uint16_t *ws, int64_t M,
+                                   int64_t N, int64_t K, const int64_t *ms, const int64_t *ns,
+                                   int64_t count, double *y, double *t, double *u) {
+    (void)N;
+    double *xn = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    oracle_rmsnorm(x, gamma, eps, M, K, xn);
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i)
+        rms_dot_one(xn + ms[i] * K, wq + ns[i] * (K / 2), ws + ns[i] * (K / Q4O_BLOCK), K,
+                    &y[i], &t[i], &u[i]);
+    free(xn);
 }

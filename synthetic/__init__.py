@@ -27,6 +27,10 @@ experts.
 Draw order inside one case: codes, scales, x, then (MoE) the router, token
 by token.
 
+RMSNorm prologue (``rms_case``): a dense case, then the norm's weights gamma,
+bf16 ``uint16[K]`` drawn as 1 + 0.1 N(0, 1) (learned norm weights sit around
+1); eps is 1e-6.
+
 4-bit float blocks (``mx_case``): the codes are drawn as above (e2m1
 elements, the library's convention again); each block's E8M0 scale byte is
 drawn uniformly from 118..122 (scales 2^-9 .. 2^-5, the range in which
@@ -44,6 +48,7 @@ BLOCK = 32  # elements per quantisation block along K
 __all__ = [
     "BLOCK", "DenseCase", "MoECase", "CONFIGS", "dense_case", "moe_case",
     "f32_to_bf16_bits", "config_case", "MXCase", "mx_case", "MX_CONFIGS",
+    "RMSCase", "rms_case", "RMS_CONFIGS", "RMS_EPS",
 ]
 
 
@@ -198,4 +203,31 @@ def mx_case(seed: int, M: int, N: int, K: int, e_lo: int = 118, e_hi: int = 122)
 MX_CONFIGS = {
     "mx_decode_gate_up": dict(kind="mx", M=1, K=5120, N=34816, seed=6, out="f32"),
     "mx_prefill":        dict(kind="mx", M=512, K=5120, N=34816, seed=7, out="bf16"),
+}
+
+
+@dataclass
+class RMSCase:
+    x: np.ndarray      # uint16 [M][K]    bf16 bits (the un-normalised activations)
+    gamma: np.ndarray  # uint16 [K]       bf16 bits
+    w_q: np.ndarray    # uint8  [N][K/2]
+    w_s: np.ndarray    # uint16 [N][K/32]
+    eps: float
+
+
+RMS_EPS = 1e-6
+
+
+def rms_case(seed: int, M: int, N: int, K: int) -> RMSCase:
+    """A dense case (codes, scales, x) followed by the norm weights."""
+    d = dense_case(seed, M, N, K)
+    rng = np.random.default_rng(seed + 1_000_003)
+    gamma = f32_to_bf16_bits(1.0 + 0.1 * rng.standard_normal(K, dtype=np.float32))
+    return RMSCase(x=d.x, gamma=gamma, w_q=d.w_q, w_s=d.w_s, eps=RMS_EPS)
+
+
+# The decode gate+up and prefill shapes behind an RMSNorm prologue.
+RMS_CONFIGS = {
+    "rms_decode_gate_up": dict(kind="rms", M=1, K=5120, N=34816, seed=8, out="f32"),
+    "rms_prefill":        dict(kind="rms", M=512, K=5120, N=34816, seed=9, out="bf16"),
 }

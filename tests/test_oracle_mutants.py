@@ -59,6 +59,23 @@ FFN_MUTANTS = {
 }
 
 
+# Mutants of the RMSNorm prologue, run against tests/test_oracle_rmsnorm.py.
+RMS_MUTANTS = {
+    "rms_eps_dropped": ("double r = 1.0 / sqrt(ss / (double)K + eps);",
+                        "double r = 1.0 / sqrt(ss / (double)K);"),
+    "rms_sum_not_mean": ("double r = 1.0 / sqrt(ss / (double)K + eps);",
+                         "double r = 1.0 / sqrt(ss + eps);"),
+    "rms_sqrt_dropped": ("double r = 1.0 / sqrt(ss / (double)K + eps);",
+                         "double r = 1.0 / (ss / (double)K + eps);"),
+    "rms_gamma_dropped": ("xn[m * K + k] = bf16_value(x[m * K + k]) * r * bf16_value(gamma[k]);",
+                          "xn[m * K + k] = bf16_value(x[m * K + k]) * r;"),
+    "rms_gamma_index": ("xn[m * K + k] = bf16_value(x[m * K + k]) * r * bf16_value(gamma[k]);",
+                        "xn[m * K + k] = bf16_value(x[m * K + k]) * r * bf16_value(gamma[K - 1 - k]);"),
+    "rms_half_ulp_double": ("return ldexp(1.0, (e - 1) - 8);", "return ldexp(1.0, (e - 1) - 7);"),
+    "rms_abs_dropped": ("        mag += fabs(p);\n        rnd +=", "        mag += p;\n        rnd +="),
+}
+
+
 def _run_suite_on_mutant(old, new, suite, tmp_path):
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not unique"
@@ -98,3 +115,9 @@ def test_pins_catch_mutant(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(RMS_MUTANTS))
+def test_rms_pins_catch_mutant(name, tmp_path):
+    r = _run_suite_on_mutant(*RMS_MUTANTS[name], "test_oracle_rmsnorm.py", tmp_path)
+    assert r.returncode != 0, f"mutant {name} passed every RMSNorm pin:\n{r.stdout[-2000:]}"
