@@ -24,9 +24,10 @@ MUTANTS = {
     "fp16_exponent_bias": ("e - 25);", "e - 24);"),
     "fp16_subnormal_quantum": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "bf16_exponent_bias": ("e - 134);", "e - 133);"),
-    "output_transposed": ("&y[m * N + n], &t[m * N + n]", "&y[n * M + m], &t[n * M + m]"),
-    "sum_sign": ("acc += p;", "acc -= p;"),
-    "abs_dropped": ("mag += fabs(p);", "mag += p;"),
+    "output_transposed": ("K, bf16_weights,\n                    &y[m * N + n], &t[m * N + n]",
+                          "K, bf16_weights,\n                    &y[n * M + m], &t[n * M + m]"),
+    "sum_sign": ("acc += p;\n        mag += fabs(p);\n    }", "acc -= p;\n        mag += fabs(p);\n    }"),
+    "abs_dropped": ("mag += fabs(p);\n    }", "mag += p;\n    }"),
     "bf16_round_truncates": ("r = ldexp(rint(ldexp(a, 8 - e)), e - 8);",
                              "r = ldexp(floor(ldexp(a, 8 - e)), e - 8);"),
     "moe_gate_dropped": ("acc += g * d;", "acc += d;"),
