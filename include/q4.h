@@ -164,6 +164,42 @@ Q4_API int32_t q4_matmul_ex(const void *x, const void *w_q, const void *w_s,
                             void *workspace, size_t workspace_bytes,
                             q4_stream_t stream);
 
+/* Device workspace (bytes) q4_rmsnorm_matmul needs for these sizes (ABI
+ * version 8): 0 when the fused matrix-vector form serves the shape (M <= 2,
+ * K up to 8192) or a size is invalid; otherwise the normalised activations,
+ * M * K bf16 rounded up to 256 bytes, followed by
+ * q4_matmul_workspace_bytes(M, N, K) bytes that let the product cut K (a
+ * workspace of only the first part is accepted; the product then runs
+ * uncut).  Host-only. */
+Q4_API size_t q4_rmsnorm_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* y = RMSNorm(x) . dequant(W)^T: the quantised matmul behind an RMSNorm
+ * prologue, the first measured kernel of "spec: specialized model runtimes"
+ * ("Feasibility gate": one quantized GEMM plus fused RMSNorm; "Development
+ * sequence", Phase 1).  The pages do not define RMSNorm; this library takes,
+ * per activation row m,
+ *     x'[m][k] = x[m][k] * gamma[k] / sqrt(mean_k x[m][k]^2 + eps)
+ * with the sum of squares in double.
+ *   x, w_q, w_s, y, y_dtype, M, N, K   as for q4_matmul
+ *   gamma   bf16 [K] device, the norm weights
+ *   eps     >= 0 and finite (else Q4_ERR_SHAPE)
+ *   workspace, workspace_bytes   device scratch of at least the first part
+ *           of q4_rmsnorm_matmul_workspace_bytes(M, N, K) when that is
+ *           non-zero (else Q4_ERR_WORKSPACE, after the NULL and alignment
+ *           checks); contents on entry do not matter; may be NULL when 0.
+ * M <= 2 with K up to 8192: one matrix-vector kernel whose activation
+ * staging applies the norm (x' in fp32).  Otherwise the normalised
+ * activations are written to the workspace as bf16 (nearest-even; the matrix
+ * cores' operand type) and the product takes the q4_matmul_ex path on them;
+ * that rounding can move y by at most sum_k hulp(x'[m][k]) * |w[n][k]|,
+ * hulp = half a bf16 unit in the last place.  Weights enter exactly.
+ * Returns Q4_OK or an error code. */
+Q4_API int32_t q4_rmsnorm_matmul(const void *x, const void *gamma, float eps,
+                                 const void *w_q, const void *w_s, void *y,
+                                 int32_t y_dtype, int64_t M, int64_t N, int64_t K,
+                                 void *workspace, size_t workspace_bytes,
+                                 q4_stream_t stream);
+
 /* Dequantise W to fp32 ((c-8)*s, exact) or bf16 (that value rounded
  * nearest-even): w_out [N][K] device, out_dtype Q4_F32 or Q4_BF16.  Same
  * conventions as q4_matmul (N == 0 is a no-op). */

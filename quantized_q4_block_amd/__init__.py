@@ -15,6 +15,9 @@ of the C ABI in ``include/q4.h``:
     q4_matmul_ex(x, w_q, w_s, out=None, out_dtype=torch.float32, workspace="auto",
                  stream=None) -> y
     q4_dequantize(w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> w
+    q4_rmsnorm_matmul_workspace_bytes(M, N, K) -> int
+    q4_rmsnorm_matmul(x, gamma, eps, w_q, w_s, out=None, out_dtype=torch.float32,
+                      workspace="auto", stream=None) -> y
     q4_moe_workspace_bytes(T, topk, E, N)   -> int
     q4_moe_matmul(x, w_q, w_s, topk_ids, topk_w, out=None, workspace=None,
                   stream=None) -> y
@@ -65,6 +68,7 @@ __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul_path_ex",
     "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
+    "q4_rmsnorm_matmul_workspace_bytes", "q4_rmsnorm_matmul",
     "q4_moe_matmul", "q4_moe_matmul_noalloc", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
     "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
 ]
@@ -97,6 +101,11 @@ def _open():
     L.q4_matmul_workspace_bytes.restype = ctypes.c_size_t
     L.q4_matmul_ex.argtypes = [P, P, P, P, I32, I64, I64, I64, P, ctypes.c_size_t, P]
     L.q4_matmul_ex.restype = I32
+    L.q4_rmsnorm_matmul_workspace_bytes.argtypes = [I64, I64, I64]
+    L.q4_rmsnorm_matmul_workspace_bytes.restype = ctypes.c_size_t
+    L.q4_rmsnorm_matmul.argtypes = [P, P, ctypes.c_float, P, P, P, I32, I64, I64, I64, P,
+                                    ctypes.c_size_t, P]
+    L.q4_rmsnorm_matmul.restype = I32
     L.q4_dequantize.argtypes = [P, P, P, I32, I64, I64, P]
     L.q4_dequantize.restype = I32
     L.q4_moe_workspace_bytes.argtypes = [I64, I64, I64, I64]
@@ -293,6 +302,35 @@ def q4_matmul_ex(x, w_q, w_s, out=None, out_dtype=None, workspace="auto", stream
                           M, N, K, _ptr(workspace), nbytes, _stream_handle(stream, x.device))
     if st != Q4_OK:
         raise Q4Error(st, "q4_matmul_ex")
+    return out
+
+
+def q4_rmsnorm_matmul_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q4_rmsnorm_matmul_workspace_bytes(int(M), int(N), int(K)))
+
+
+def q4_rmsnorm_matmul(x, gamma, eps, w_q, w_s, out=None, out_dtype=None, workspace="auto",
+                      stream=None):
+    """y = RMSNorm(x) . dequant(W)^T with RMSNorm(x)[m,k] = x[m,k] * gamma[k] /
+    sqrt(mean_k x[m,k]^2 + eps).  workspace: "auto" allocates what the call
+    can use (a torch tensor on the call's stream), None passes none, a uint8
+    device tensor is passed as is."""
+    torch = _torch()
+    M, N, K, out = _matmul_args(x, w_q, w_s, out, out_dtype)
+    _check_dev(gamma, "gamma", (torch.bfloat16, torch.int16, torch.uint16), 1)
+    if gamma.shape[0] != K:
+        raise ValueError("gamma must be [K]")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        need = q4_rmsnorm_matmul_workspace_bytes(M, N, K)
+        workspace = _scratch(torch, need, x.device, stream) if need else None
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.q4_rmsnorm_matmul(_ptr(x), _ptr(gamma), float(eps), _ptr(w_q), _ptr(w_s), _ptr(out),
+                               _out_code(out.dtype), M, N, K, _ptr(workspace), nbytes,
+                               _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_rmsnorm_matmul")
     return out
 
 

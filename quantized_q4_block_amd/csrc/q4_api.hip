@@ -188,6 +188,38 @@ Q4_API int32_t q4_matmul(const void* x, const void* w_q, const void* w_s, void* 
   return q4_matmul_ex(x, w_q, w_s, y, y_dtype, M, N, K, nullptr, 0, stream);
 }
 
+Q4_API size_t q4_rmsnorm_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 0;
+  int64_t mk;
+  if (!mul_ok(M, K, &mk) || mk > (int64_t(1) << 40)) return 0;
+  if (M == 0 || N == 0 || q4::gemv_norm_fits(M, K)) return 0;
+  return q4::rmsnorm_act_bytes(M, K) + q4_matmul_workspace_bytes(M, N, K);
+}
+
+Q4_API int32_t q4_rmsnorm_matmul(const void* x, const void* gamma, float eps, const void* w_q,
+                                 const void* w_s, void* y, int32_t y_dtype, int64_t M,
+                                 int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                 q4_stream_t stream) {
+  if (y_dtype != Q4_F32 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+  if (M < 0 || !(eps >= 0.0f) || eps > 3.4e38f) return Q4_ERR_SHAPE;
+  if (int32_t s = check_weights(N, K)) return s;
+  int64_t mk, mn;
+  if (!mul_ok(M, K, &mk) || !mul_ok(M, N, &mn) || mk > (int64_t(1) << 40)) return Q4_ERR_SHAPE;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!x || !gamma || !w_q || !w_s || !y) return Q4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(y))
+    return Q4_ERR_ALIGN;
+  if (!q4::gemv_norm_fits(M, K)) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < q4::rmsnorm_act_bytes(M, K))
+      return Q4_ERR_WORKSPACE;
+  }
+  if (int32_t s = ready()) return s;
+  return launched(q4::launch_rmsnorm_matmul(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma), eps,
+      static_cast<const uint8_t*>(w_q), static_cast<const uint16_t*>(w_s), y, y_dtype == Q4_BF16,
+      M, N, K, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
 // Tiled-path K slices of q4_mx_matmul_ex (0: the call never cuts K).
 static int64_t mx_split_slices(int64_t M, int64_t N, int64_t K) {
   if (M <= kGemvMaxRows || K % 64 != 0 || q4_matmul_path_ex(M, N, K, 1) != Q4_PATH_MFMA) return 0;

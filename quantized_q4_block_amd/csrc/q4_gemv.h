@@ -303,6 +303,47 @@ struct XStager {
                                                bf16_lo(d[m][i].w), bf16_hi(d[m][i].w));
       }
   }
+  // This thread's share of sum_k x[m][k]^2, in double (each square is exact
+  // there, and the sum cannot overflow for any bf16 input).
+  __device__ __forceinline__ void sum_squares(double (&ss)[M]) const {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      ss[m] = 0.0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint32_t w[4] = {d[m][i].x, d[m][i].y, d[m][i].z, d[m][i].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const double a = bf16_lo(w[h]), b = bf16_hi(w[h]);
+          ss[m] = __builtin_fma(a, a, ss[m]);
+          ss[m] = __builtin_fma(b, b, ss[m]);
+        }
+      }
+    }
+  }
+  // store_f32 of x[m][k] * g[k] * r[m] (g: a one-row stager loaded at the
+  // same positions), each product in fp32.
+  __device__ __forceinline__ void store_f32_scaled(float4* __restrict__ xs,
+                                                   const XStager<1, S, THREADS>& g,
+                                                   const float (&r)[M]) const {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = i * THREADS + (int)threadIdx.x;
+        if (kRowChunks % THREADS != 0 && c >= kRowChunks) break;
+        const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
+        float4* row = xs + m * (2 * kRowChunks) + st * 8 * kWave + l;
+        const uint4 v = d[m][i], gv = g.d[0][i];
+        const float rm = r[m];
+        row[(2 * q) * kWave] =
+            make_float4(bf16_lo(v.x) * bf16_lo(gv.x) * rm, bf16_hi(v.x) * bf16_hi(gv.x) * rm,
+                        bf16_lo(v.y) * bf16_lo(gv.y) * rm, bf16_hi(v.y) * bf16_hi(gv.y) * rm);
+        row[(2 * q + 1) * kWave] =
+            make_float4(bf16_lo(v.z) * bf16_lo(gv.z) * rm, bf16_hi(v.z) * bf16_hi(gv.z) * rm,
+                        bf16_lo(v.w) * bf16_lo(gv.w) * rm, bf16_hi(v.w) * bf16_hi(gv.w) * rm);
+      }
+  }
 };
 
 // The same staging for one activation row that is already fp32 (the routed

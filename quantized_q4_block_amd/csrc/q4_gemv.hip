@@ -57,11 +57,21 @@ __device__ __forceinline__ void store_rows(void* __restrict__ y, int y_bf16, int
 // plus a partial one (TAIL = kWideTail; lanes past the slice's end add
 // zero) and writes the fp32 partial sums of slice s to partial[s][M][N],
 // which gemv_combine_kernel then adds in slice order.
-template <int M, int FULL, int TAIL>
+//
+// NORM: the RMSNorm prologue fused into the staging (whole rows only): the
+// workgroup also loads the norm weights gamma at its activations' positions
+// and stages x * gamma (exact in fp32) instead of x; each wavefront sums the
+// squares of its chunks of every activation row in double and leaves the sum
+// in LDS before the staging barrier; after it every wavefront adds the eight
+// sums in the same fixed order, forms r = 1 / sqrt(sum / K + eps) and
+// multiplies its outputs by r, since y = r * sum_k (x gamma)_k w_k.  Every
+// workgroup computes the same r; the prologue adds no barrier.
+template <int M, int FULL, int TAIL, bool NORM = false>
 __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t N, int64_t K,
-    int rem, int64_t ld_blocks, int slice0, int slice_blocks, float* __restrict__ partial) {
+    int rem, int64_t ld_blocks, int slice0, int slice_blocks, float* __restrict__ partial,
+    const uint16_t* __restrict__ gamma = nullptr, float eps = 0.0f) {
   constexpr int R = kLdsRows;
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[M * S * 8 * kWave];
@@ -84,19 +94,48 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
   // into LDS while the weights are in flight
   XStager<M, S, kLdsWaves * 64> xst;
   xst.load(x + blk0 * kBlock, K, ld_blocks * kBlock);
+  XStager<1, S, kLdsWaves * 64> gst;
+  if constexpr (NORM) gst.load(gamma, K, 0);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes + blk0 * 16,
                               ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
                               lane);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.pin();
-  xst.store_f32(xs);
+  __shared__ double red[NORM ? M : 1][kLdsWaves];
+  if constexpr (NORM) {
+    gst.pin();
+    double ss[M];
+    xst.sum_squares(ss);
+    float one[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss[m] += __shfl_xor(ss[m], off, kWave);
+      if (lane == 0) red[m][wave] = ss[m];
+      one[m] = 1.0f;
+    }
+    xst.store_f32_scaled(xs, gst, one);
+  } else {
+    xst.store_f32(xs);
+  }
   __syncthreads();
   // a wavefront past the last row computes on clamped rows and stores
   // nothing (an early exit would let the compiler sink its loads past the
   // barrier)
   float out[R][M];
   upfront_compute<M, R, FULL, TAIL>(b, xs, rem, lane, out);
+  if constexpr (NORM) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < kLdsWaves; ++w) t += red[m][w];
+      const float r = (float)(1.0 / __builtin_sqrt(t / (double)K + (double)eps));
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) out[rr][m] *= r;
+    }
+  }
   if (!live) return;
   if (partial)
     store_rows<M, R>(partial + (int64_t)slice * M * N, 0, N, n0, out);
@@ -230,6 +269,37 @@ static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t*
         x, wq, ws, y, yb, N, K, 0);
   }
   return hipGetLastError();
+}
+
+// RMSNorm fused into the LDS kernel (M <= 2, whole rows of at most
+// kLdsMaxStages stages whose activations fit the LDS).
+bool gemv_norm_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= 2 && x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit;
+}
+
+template <int M>
+static hipError_t launch_norm_m(const uint16_t* x, const uint16_t* gamma, float eps,
+                                const uint8_t* wq, const uint16_t* ws, void* y, bool y_bf16,
+                                int64_t N, int64_t K, hipStream_t stream) {
+  const int rem = row_leftover(K);
+  const int64_t bpr = K / kBlock;
+  return dispatch_row_geometry(K, [&](auto full, auto tail) {
+    constexpr int FULL = decltype(full)::value, TAIL = decltype(tail)::value;
+    const int64_t tasks = (N + kLdsRows - 1) / kLdsRows;
+    const int64_t grid = (tasks + kLdsWaves - 1) / kLdsWaves;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemv_lds_kernel<M, FULL, TAIL, true><<<dim3((unsigned)grid), dim3(kLdsWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, N, K, rem, bpr, 0, 0, nullptr, gamma, eps);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* gamma, float eps,
+                            const uint8_t* wq, const uint16_t* ws, void* y, bool y_bf16,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (!gemv_norm_fits(M, K)) return hipErrorInvalidValue;
+  if (M == 1) return launch_norm_m<1>(x, gamma, eps, wq, ws, y, y_bf16, N, K, stream);
+  return launch_norm_m<2>(x, gamma, eps, wq, ws, y, y_bf16, N, K, stream);
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,

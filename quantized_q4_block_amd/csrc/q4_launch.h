@@ -22,6 +22,23 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
 // given (0: never cut).
 int64_t gemv_split_slices(int64_t M, int64_t K);
 
+// The RMSNorm prologue fused into the matrix-vector kernel: M <= 2, whole
+// rows that fit its LDS staging (gemv_norm_fits).
+bool gemv_norm_fits(int64_t M, int64_t K);
+hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* gamma, float eps,
+                            const uint8_t* wq, const uint16_t* ws, void* y, bool y_bf16,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// RMSNorm prologue + product: the fused matrix-vector kernel where it fits,
+// else the normalised activations (bf16) into the first rmsnorm_act_bytes
+// of the workspace and the q4_matmul_ex paths on them (K slices when the
+// rest of the workspace holds q4_matmul_workspace_bytes).
+size_t rmsnorm_act_bytes(int64_t M, int64_t K);
+hipError_t launch_rmsnorm_matmul(const uint16_t* x, const uint16_t* gamma, float eps,
+                                 const uint8_t* wq, const uint16_t* ws, void* y, bool y_bf16,
+                                 int64_t M, int64_t N, int64_t K, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 // Few rows (3 <= M, at most 65535 slabs of 32): exact (c - 8) on the bf16
 // matrix cores, block scales applied in fp32; exact weights.
 hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
