@@ -91,6 +91,7 @@ def _load():
     lib.oracle_rmsnorm_matmul.argtypes = [P, P, ctypes.c_double, P, P, I64, I64, I64, P, P, P]
     lib.oracle_rmsnorm_matmul_sampled.argtypes = [P, P, ctypes.c_double, P, P, I64, I64, I64,
                                                   P, P, I64, P, P, P]
+    lib.oracle_quantize.argtypes = [P, I64, I64, P, P]
     lib.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
     lib.oracle_mx_matmul.argtypes = [P, P, P, I64, I64, I64, P, P]
     _lib = lib
@@ -340,3 +341,19 @@ def rmsnorm_matmul_sampled(x: np.ndarray, gamma: np.ndarray, eps: float, w_q: np
                                           M, N, K, _ptr(ms), _ptr(ns), ms.size, _ptr(y), _ptr(t),
                                           _ptr(u))
     return y, t, u
+
+
+# ---- quantiser --------------------------------------------------------------
+
+def quantize(w: np.ndarray):
+    """(w_q, w_s): bf16 weights [N][K] (bit patterns) in this format -- per
+    32-element block s = fp16(m / -8) with m the largest-magnitude element,
+    codes clamp(rint(w / s) + 8, 0, 15) (fp32 quotient)."""
+    w = _c(w, np.uint16)
+    if w.ndim != 2 or w.shape[1] % BLOCK:
+        raise ValueError("w must be [N][K] with K a multiple of 32")
+    N, K = w.shape
+    wq = np.zeros((N, K // 2), dtype=np.uint8)
+    ws = np.zeros((N, K // BLOCK), dtype=np.uint16)
+    _load().oracle_quantize(_ptr(w), N, K, _ptr(wq), _ptr(ws))
+    return wq, ws

@@ -59,6 +59,17 @@
  * activations are the matmul's activation operand, whose type is bf16, and u
  * is what their rounding to bf16 can move y by.  Everything in double.
  *
+ * Quantiser (bf16 weights -> this format).  The spec's build flow converts
+ * model weights into the runtime's profile before qualifying it (section
+ * "Target package and artifact": Convert, then Qualify) but fixes no method.
+ * The reading taken, per 32-element block of a row (symmetric absmax, the
+ * block's largest-magnitude element landing exactly on code 0):
+ *         m    = the element of largest |w| (the first one in k on ties)
+ *         s    = fp16(m / -8), nearest-even, |s| clamped to 65504
+ *         c_k  = clamp(rint(w_k / s) + 8, 0, 15)      (s != 0; else c_k = 8)
+ * The quotient and its rounding decide an integer, so they are taken in the
+ * kernel's precision: an IEEE fp32 division and round-half-even in fp32.
+ *
  * 4-bit float blocks.  The specialised-runtime spec names a 4-bit float block
  * format as the performance path after groupwise-int weights (section "Target
  * package and artifact") but fixes no bits.  The reading taken is the public
@@ -440,4 +451,70 @@ void oracle_rmsnorm_matmul_sampled(const uint16_t *x, const uint16_t *gamma, dou
         rms_dot_one(xn + ms[i] * K, wq + ns[i] * (K / 2), ws + ns[i] * (K / Q4O_BLOCK), K,
                     &y[i], &t[i], &u[i]);
     free(xn);
+}
+
+/* ---- quantiser ------------------------------------------------------------- */
+
+/* Round a double to the nearest fp16 value, ties to even, written from the
+ * format: 11 significant bits in the normal range (>= 2^-14), a fixed
+ * quantum of 2^-24 below it; values past 65504 are clamped to +-65504. */
+static double fp16_round_clamped(double v) {
+    if (v == 0.0 || isnan(v))
+        return v;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);                       /* a = m * 2^e, m in [0.5, 1) */
+    double r;
+    if (e - 1 < -14)
+        r = ldexp(rint(ldexp(a, 24)), -24);
+    else
+        r = ldexp(rint(ldexp(a, 11 - e)), e - 11);
+    if (r > 65504.0)
+        r = 65504.0;
+    return v < 0 ? -r : r;
+}
+
+static uint16_t fp16_bits_of(double v) {
+    /* v is an fp16 value (finite): encode its fields */
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    if (e - 1 < -14)                    /* subnormal: f * 2^-24 */
+        return (uint16_t)(sign | (uint16_t)ldexp(a, 24));
+    int f = (int)(ldexp(a, 11 - e)) - 1024;   /* 1.f * 2^(e-1) */
+    return (uint16_t)(sign | ((e - 1 + 15) << 10) | f);
+}
+
+/* bf16 weights [N][K] -> codes [N][K/2] and fp16 scales [N][K/32]. */
+void oracle_quantize(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, uint16_t *ws) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < K / Q4O_BLOCK; ++b) {
+            const uint16_t *blk = w + n * K + b * Q4O_BLOCK;
+            double m = 0.0;
+            for (int i = 0; i < Q4O_BLOCK; ++i) {
+                double v = bf16_value(blk[i]);
+                if (fabs(v) > fabs(m))
+                    m = v;
+            }
+            double s = fp16_round_clamped(m / -8.0);
+            ws[n * (K / Q4O_BLOCK) + b] = fp16_bits_of(s);
+            for (int i = 0; i < Q4O_BLOCK; ++i) {
+                int c = 8;
+                if (s != 0.0) {
+                    float q = rintf((float)bf16_value(blk[i]) / (float)s);
+                    c = (int)fmaxf(0.0f, fminf(15.0f, q + 8.0f));
+                }
+                int64_t k = b * Q4O_BLOCK + i;
+                uint8_t *byte = &wq[n * (K / 2) + k / 2];
+                if (k % 2 == 0)
+                    *byte = (uint8_t)((*byte & 0xF0) | c);
+                else
+                    *byte = (uint8_t)((*byte & 0x0F) | (c << 4));
+            }
+        }
+    }
 }

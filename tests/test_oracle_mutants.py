@@ -77,6 +77,22 @@ RMS_MUTANTS = {
 }
 
 
+# Mutants of the quantiser, run against tests/test_oracle_quantize.py.
+QUANT_MUTANTS = {
+    "q_max_by_value": ("if (fabs(v) > fabs(m))", "if (v > m)"),
+    "q_divisor_sign": ("fp16_round_clamped(m / -8.0)", "fp16_round_clamped(m / 8.0)"),
+    "q_offset_7": ("fminf(15.0f, q + 8.0f)", "fminf(15.0f, q + 7.0f)"),
+    "q_round_down": ("rintf((float)bf16_value(blk[i]) / (float)s)",
+                     "floorf((float)bf16_value(blk[i]) / (float)s)"),
+    # m / -8 has at most 8 significant bits, so only fp16's subnormal range
+    # rounds it
+    "q_fp16_subnormal_truncates": ("r = ldexp(rint(ldexp(a, 24)), -24);",
+                                   "r = ldexp(floor(ldexp(a, 24)), -24);"),
+    "q_nibble_order": ("if (k % 2 == 0)\n                    *byte", "if (k % 2 == 1)\n                    *byte"),
+    "q_clamp_14": ("fminf(15.0f, q + 8.0f)", "fminf(14.0f, q + 8.0f)"),
+}
+
+
 def _run_suite_on_mutant(old, new, suite, tmp_path):
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not unique"
@@ -122,3 +138,9 @@ def test_pins_catch_mutant(name, tmp_path):
 def test_rms_pins_catch_mutant(name, tmp_path):
     r = _run_suite_on_mutant(*RMS_MUTANTS[name], "test_oracle_rmsnorm.py", tmp_path)
     assert r.returncode != 0, f"mutant {name} passed every RMSNorm pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTANTS))
+def test_quant_pins_catch_mutant(name, tmp_path):
+    r = _run_suite_on_mutant(*QUANT_MUTANTS[name], "test_oracle_quantize.py", tmp_path)
+    assert r.returncode != 0, f"mutant {name} passed every quantiser pin:\n{r.stdout[-2000:]}"
