@@ -207,6 +207,22 @@ Q4_API int32_t q4_dequantize(const void *w_q, const void *w_s, void *w_out,
                              int32_t out_dtype, int64_t N, int64_t K,
                              q4_stream_t stream);
 
+/* bf16 weights -> this format (ABI version 8): the convert step of "spec:
+ * specialized model runtimes" ("Target package and artifact": weights are
+ * converted into the runtime's profile, then qualified).  The pages fix no
+ * method; per 32-element block of a row, m = the element of largest |w|
+ * (first on ties), s = fp16(m / -8) (nearest-even; |m / 8| clamped to 65504),
+ * c = clamp(rint(w / s) + 8, 0, 15) with an IEEE fp32 quotient and
+ * round-half-even (s == 0: every code 8).  The block's largest-magnitude
+ * weight is reproduced exactly by dequantisation; every other one to within
+ * half a step |s| / 2 (one step for a weight of -m, clamped to code 15).
+ *   w    bf16  [N][K]     device
+ *   w_q  uint8 [N][K/2]   device, fully overwritten
+ *   w_s  fp16  [N][K/32]  device, fully overwritten
+ * K a positive multiple of 32.  Returns Q4_OK or an error code. */
+Q4_API int32_t q4_quantize(const void *w, void *w_q, void *w_s, int64_t N, int64_t K,
+                           q4_stream_t stream);
+
 /* Device workspace (bytes) q4_moe_matmul needs for these sizes; 0 if a size
  * is negative or the size overflows. */
 Q4_API size_t q4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t N);

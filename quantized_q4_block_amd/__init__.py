@@ -15,6 +15,7 @@ of the C ABI in ``include/q4.h``:
     q4_matmul_ex(x, w_q, w_s, out=None, out_dtype=torch.float32, workspace="auto",
                  stream=None) -> y
     q4_dequantize(w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> w
+    q4_quantize(w, w_q=None, w_s=None, stream=None) -> (w_q, w_s)
     q4_rmsnorm_matmul_workspace_bytes(M, N, K) -> int
     q4_rmsnorm_matmul(x, gamma, eps, w_q, w_s, out=None, out_dtype=torch.float32,
                       workspace="auto", stream=None) -> y
@@ -68,7 +69,7 @@ __all__ = [
     "Q4Error", "lib", "q4_abi_version", "q4_status_str", "q4_matmul_path", "q4_matmul_path_ex",
     "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
-    "q4_rmsnorm_matmul_workspace_bytes", "q4_rmsnorm_matmul",
+    "q4_rmsnorm_matmul_workspace_bytes", "q4_rmsnorm_matmul", "q4_quantize",
     "q4_moe_matmul", "q4_moe_matmul_noalloc", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
     "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
 ]
@@ -106,6 +107,8 @@ def _open():
     L.q4_rmsnorm_matmul.argtypes = [P, P, ctypes.c_float, P, P, P, I32, I64, I64, I64, P,
                                     ctypes.c_size_t, P]
     L.q4_rmsnorm_matmul.restype = I32
+    L.q4_quantize.argtypes = [P, P, P, I64, I64, P]
+    L.q4_quantize.restype = I32
     L.q4_dequantize.argtypes = [P, P, P, I32, I64, I64, P]
     L.q4_dequantize.restype = I32
     L.q4_moe_workspace_bytes.argtypes = [I64, I64, I64, I64]
@@ -332,6 +335,33 @@ def q4_rmsnorm_matmul(x, gamma, eps, w_q, w_s, out=None, out_dtype=None, workspa
     if st != Q4_OK:
         raise Q4Error(st, "q4_rmsnorm_matmul")
     return out
+
+
+def q4_quantize(w, w_q=None, w_s=None, stream=None):
+    """bf16 weights [N][K] -> (codes uint8 [N][K/2], fp16 scales [N][K/32]):
+    per 32-element block s = fp16(m / -8), m the largest-magnitude weight,
+    codes clamp(rint(w / s) + 8, 0, 15)."""
+    torch = _torch()
+    _check_dev(w, "w", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    N, K = w.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if w_q is None:
+        w_q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    else:
+        _check_dev(w_q, "w_q", (torch.uint8,), 2)
+        if tuple(w_q.shape) != (N, K // 2):
+            raise ValueError("w_q has the wrong shape")
+    if w_s is None:
+        w_s = torch.empty((N, K // 32), dtype=torch.float16, device=w.device)
+    else:
+        _check_dev(w_s, "w_s", (torch.float16, torch.int16, torch.uint16), 2)
+        if tuple(w_s.shape) != (N, K // 32):
+            raise ValueError("w_s has the wrong shape")
+    st = lib.q4_quantize(_ptr(w), _ptr(w_q), _ptr(w_s), N, K, _stream_handle(stream, w.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_quantize")
+    return w_q, w_s
 
 
 def q4_dequantize(w_q, w_s, out=None, out_dtype=None, stream=None):

@@ -286,6 +286,18 @@ Q4_API int32_t q4_dequantize(const void* w_q, const void* w_s, void* w_out, int3
                                      static_cast<hipStream_t>(stream)));
 }
 
+Q4_API int32_t q4_quantize(const void* w, void* w_q, void* w_s, int64_t N, int64_t K,
+                           q4_stream_t stream) {
+  if (int32_t s = check_weights(N, K)) return s;
+  if (N == 0) return Q4_OK;
+  if (!w || !w_q || !w_s) return Q4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_q) || !aligned16(w_s)) return Q4_ERR_ALIGN;
+  if (int32_t s = ready()) return s;
+  return launched(q4::launch_quantize(static_cast<const uint16_t*>(w),
+                                      static_cast<uint8_t*>(w_q), static_cast<uint16_t*>(w_s),
+                                      N, K, static_cast<hipStream_t>(stream)));
+}
+
 Q4_API size_t q4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t N) {
   int64_t P, PN;
   if (T < 0 || topk < 0 || E < 0 || N < 0) return 0;

@@ -7,6 +7,10 @@
 
 namespace q4 {
 
+// bf16 weights [N][K] -> codes [N][K/2] and fp16 scales [N][K/32].
+hipError_t launch_quantize(const uint16_t* w, uint8_t* wq, uint16_t* ws, int64_t N, int64_t K,
+                           hipStream_t stream);
+
 hipError_t launch_dequant(const uint8_t* wq, const uint16_t* ws, void* out, bool bf16,
                           int64_t N, int64_t K, hipStream_t stream);
 
