@@ -92,6 +92,8 @@ def _load():
     lib.oracle_rmsnorm_matmul_sampled.argtypes = [P, P, ctypes.c_double, P, P, I64, I64, I64,
                                                   P, P, I64, P, P, P]
     lib.oracle_quantize.argtypes = [P, I64, I64, P, P]
+    lib.oracle_sb_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_sb_matmul.argtypes = [P, P, P, P, I64, I64, I64, P, P]
     lib.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
     lib.oracle_mx_matmul.argtypes = [P, P, P, I64, I64, I64, P, P]
     _lib = lib
@@ -357,3 +359,37 @@ def quantize(w: np.ndarray):
     ws = np.zeros((N, K // BLOCK), dtype=np.uint16)
     _load().oracle_quantize(_ptr(w), N, K, _ptr(wq), _ptr(ws))
     return wq, ws
+
+
+# ---- super-block (two-level) scales -----------------------------------------
+
+def _check_sb(w_q, w_d, w_sc):
+    N, kh = w_q.shape
+    K = 2 * kh
+    if K % 256 or w_d.shape != (N, K // 256) or w_sc.shape != (N, K // BLOCK):
+        raise ValueError("inconsistent w_q / w_d / w_sc shapes (K a multiple of 256)")
+    return N, K
+
+
+def sb_dequant(w_q: np.ndarray, w_d: np.ndarray, w_sc: np.ndarray) -> np.ndarray:
+    """float64 [N][K]: (code - 8) * d[k / 256] * sc[k / 32], exact."""
+    N, K = _check_sb(w_q, w_d, w_sc)
+    out = np.empty((N, K), dtype=np.float64)
+    _load().oracle_sb_dequant(_ptr(_c(w_q, np.uint8)), _ptr(_c(w_d, np.uint16)),
+                              _ptr(_c(w_sc, np.uint8)), N, K, _ptr(out))
+    return out
+
+
+def sb_matmul(x: np.ndarray, w_q: np.ndarray, w_d: np.ndarray, w_sc: np.ndarray):
+    """(y, t): double [M][N] product with super-block-scaled weights and
+    sum_k |x*w| per output."""
+    N, K = _check_sb(w_q, w_d, w_sc)
+    x = _c(x, np.uint16)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x has the wrong K")
+    y = np.empty((M, N), dtype=np.float64)
+    t = np.empty((M, N), dtype=np.float64)
+    _load().oracle_sb_matmul(_ptr(x), _ptr(_c(w_q, np.uint8)), _ptr(_c(w_d, np.uint16)),
+                             _ptr(_c(w_sc, np.uint8)), M, N, K, _ptr(y), _ptr(t))
+    return y, t

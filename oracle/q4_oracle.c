@@ -70,6 +70,15 @@
  * The quotient and its rounding decide an integer, so they are taken in the
  * kernel's precision: an IEEE fp32 division and round-half-even in fp32.
  *
+ * Super-block (two-level) scales.  The layer-package spec names K-quant
+ * profiles (Q4_K-class, q2_K / q3_K; sections "Repository Identity" and
+ * "Policy Resolution") without defining them.  The reading taken keeps this
+ * format's codes and builds the structure the K-quants share: 256-element
+ * super-blocks of eight 32-element blocks, one fp16 scale d per super-block
+ * and an unsigned 8-bit multiplier sc per block:
+ *         w[n,k] = (c[n,k] - 8) * d[n, k/256] * sc[n, k/32]
+ * (d * sc has at most 19 significant bits, exact in float and double).
+ *
  * 4-bit float blocks.  The specialised-runtime spec names a 4-bit float block
  * format as the performance path after groupwise-int weights (section "Target
  * package and artifact") but fixes no bits.  The reading taken is the public
@@ -517,4 +526,42 @@ void oracle_quantize(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, uint1
             }
         }
     }
+}
+
+/* ---- super-block (two-level) scales ------------------------------------------ */
+
+static double sb_weight_at(const uint8_t *wq_row, const uint16_t *wd_row, const uint8_t *wsc_row,
+                           int64_t k) {
+    return (double)(code_at(wq_row, k) - 8) * fp16_value(wd_row[k / 256]) *
+           (double)wsc_row[k / Q4O_BLOCK];
+}
+
+/* Dequantised to double [N][K] (exact). */
+void oracle_sb_dequant(const uint8_t *wq, const uint16_t *wd, const uint8_t *wsc, int64_t N,
+                       int64_t K, double *out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = sb_weight_at(wq + n * (K / 2), wd + n * (K / 256),
+                                          wsc + n * (K / Q4O_BLOCK), k);
+}
+
+/* y, t: double [M][N]. */
+void oracle_sb_matmul(const uint16_t *x, const uint8_t *wq, const uint16_t *wd,
+                      const uint8_t *wsc, int64_t M, int64_t N, int64_t K, double *y,
+                      double *t) {
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            const uint8_t *qr = wq + n * (K / 2), *sr = wsc + n * (K / Q4O_BLOCK);
+            const uint16_t *dr = wd + n * (K / 256);
+            double sum = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = bf16_value(x[m * K + k]) * sb_weight_at(qr, dr, sr, k);
+                sum += p;
+                mag += fabs(p);
+            }
+            y[m * N + n] = sum;
+            t[m * N + n] = mag;
+        }
 }

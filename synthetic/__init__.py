@@ -31,6 +31,11 @@ RMSNorm prologue (``rms_case``): a dense case, then the norm's weights gamma,
 bf16 ``uint16[K]`` drawn as 1 + 0.1 N(0, 1) (learned norm weights sit around
 1); eps is 1e-6.
 
+Super-block scales (``sb_case``): codes as above; one fp16 scale d per 256
+elements of a row, |N(0, 1)| * 0.02 / 32 (so d * sc lands where the plain
+format's block scales do); one multiplier byte sc per 32 elements, uniform
+in 16..63 (the 6-bit range the K-quant profiles use for block scales).
+
 4-bit float blocks (``mx_case``): the codes are drawn as above (e2m1
 elements, the library's convention again); each block's E8M0 scale byte is
 drawn uniformly from 118..122 (scales 2^-9 .. 2^-5, the range in which
@@ -48,7 +53,7 @@ BLOCK = 32  # elements per quantisation block along K
 __all__ = [
     "BLOCK", "DenseCase", "MoECase", "CONFIGS", "dense_case", "moe_case",
     "f32_to_bf16_bits", "config_case", "MXCase", "mx_case", "MX_CONFIGS",
-    "RMSCase", "rms_case", "RMS_CONFIGS", "RMS_EPS",
+    "RMSCase", "rms_case", "RMS_CONFIGS", "RMS_EPS", "SBCase", "sb_case", "SB_CONFIGS",
 ]
 
 
@@ -230,4 +235,30 @@ def rms_case(seed: int, M: int, N: int, K: int) -> RMSCase:
 RMS_CONFIGS = {
     "rms_decode_gate_up": dict(kind="rms", M=1, K=5120, N=34816, seed=8, out="f32"),
     "rms_prefill":        dict(kind="rms", M=512, K=5120, N=34816, seed=9, out="bf16"),
+}
+
+
+@dataclass
+class SBCase:
+    x: np.ndarray     # uint16 [M][K]     bf16 bits
+    w_q: np.ndarray   # uint8  [N][K/2]   packed codes
+    w_d: np.ndarray   # uint16 [N][K/256] fp16 bits (super-block scales)
+    w_sc: np.ndarray  # uint8  [N][K/32]  block multipliers
+
+
+def sb_case(seed: int, M: int, N: int, K: int) -> SBCase:
+    if K % 256:
+        raise ValueError("K must be a multiple of 256")
+    rng = np.random.default_rng(seed)
+    w_q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    w_d = (np.abs(rng.standard_normal((N, K // 256))) * (0.02 / 32)).astype(np.float16)
+    w_sc = rng.integers(16, 64, size=(N, K // BLOCK), dtype=np.uint8)
+    x = f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return SBCase(x=x, w_q=w_q, w_d=w_d.view(np.uint16), w_sc=w_sc)
+
+
+# The decode gate+up and prefill shapes with super-block scales.
+SB_CONFIGS = {
+    "sb_decode_gate_up": dict(kind="sb", M=1, K=5120, N=34816, seed=10, out="f32"),
+    "sb_prefill":        dict(kind="sb", M=512, K=5120, N=34816, seed=11, out="bf16"),
 }

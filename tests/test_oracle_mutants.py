@@ -19,7 +19,7 @@ SRC = os.path.join(ROOT, "oracle", "q4_oracle.c")
 
 MUTANTS = {
     "nibble_order_swapped": ("(byte & 0x0F) : (byte >> 4)", "(byte >> 4) : (byte & 0x0F)"),
-    "offset_7_not_8": ("code_at(wq_row, k) - 8", "code_at(wq_row, k) - 7"),
+    "offset_7_not_8": ("code_at(wq_row, k) - 8) * fp16_value(ws_row", "code_at(wq_row, k) - 7) * fp16_value(ws_row"),
     "scale_block_64": ("ws_row[k / Q4O_BLOCK]", "ws_row[k / 64]"),
     "fp16_exponent_bias": ("e - 25);", "e - 24);"),
     "fp16_subnormal_quantum": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
@@ -93,6 +93,19 @@ QUANT_MUTANTS = {
 }
 
 
+# Mutants of the super-block scale format, run against tests/test_oracle_sb.py.
+SB_MUTANTS = {
+    "sb_super_index_128": ("fp16_value(wd_row[k / 256])", "fp16_value(wd_row[k / 128])"),
+    "sb_multiplier_dropped": ("fp16_value(wd_row[k / 256]) *\n           (double)wsc_row[k / Q4O_BLOCK];",
+                              "fp16_value(wd_row[k / 256]);"),
+    "sb_multiplier_index": ("(double)wsc_row[k / Q4O_BLOCK];", "(double)wsc_row[k / 64];"),
+    "sb_offset_7": ("return (double)(code_at(wq_row, k) - 8) * fp16_value(wd_row",
+                    "return (double)(code_at(wq_row, k) - 7) * fp16_value(wd_row"),
+    "sb_abs_dropped": ("                sum += p;\n                mag += fabs(p);",
+                       "                sum += p;\n                mag += p;"),
+}
+
+
 def _run_suite_on_mutant(old, new, suite, tmp_path):
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor not unique"
@@ -144,3 +157,9 @@ def test_rms_pins_catch_mutant(name, tmp_path):
 def test_quant_pins_catch_mutant(name, tmp_path):
     r = _run_suite_on_mutant(*QUANT_MUTANTS[name], "test_oracle_quantize.py", tmp_path)
     assert r.returncode != 0, f"mutant {name} passed every quantiser pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(SB_MUTANTS))
+def test_sb_pins_catch_mutant(name, tmp_path):
+    r = _run_suite_on_mutant(*SB_MUTANTS[name], "test_oracle_sb.py", tmp_path)
+    assert r.returncode != 0, f"mutant {name} passed every super-block pin:\n{r.stdout[-2000:]}"
