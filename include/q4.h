@@ -200,6 +200,32 @@ Q4_API int32_t q4_rmsnorm_matmul(const void *x, const void *gamma, float eps,
                                  void *workspace, size_t workspace_bytes,
                                  q4_stream_t stream);
 
+/* Device workspace (bytes) q4_sb_matmul needs (ABI version 8): the fp32
+ * block scales, N * K/32 floats rounded up to 256 bytes, followed by
+ * q4_matmul_workspace_bytes(M, N, K) bytes that let the tiled product cut K
+ * (optional: a workspace of only the first part is accepted).  0 for an
+ * invalid or empty shape.  Host-only. */
+Q4_API size_t q4_sb_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* y = x . W^T with super-block (two-level) scales (ABI version 8):
+ *     w[n][k] = (c[n][k] - 8) * d[n][k/256] * sc[n][k/32]
+ * The layer-package spec names K-quant profiles (Q4_K-class, q2_K / q3_K) in
+ * "Repository Identity" and "Policy Resolution" without defining them; this
+ * is the two-level block-scale structure they share, on this library's codes.
+ *   x, w_q, y, y_dtype, M, N   as for q4_matmul
+ *   w_d     fp16  [N][K/256] device, one scale per 256-element super-block
+ *   w_sc    uint8 [N][K/32]  device, an unsigned multiplier per block
+ *   K       a positive multiple of 256 (else Q4_ERR_SHAPE)
+ *   workspace  device scratch of at least the first part of
+ *           q4_sb_matmul_workspace_bytes (else Q4_ERR_WORKSPACE, after the
+ *           NULL and alignment checks); contents on entry do not matter.
+ * Every d * sc is exact in fp32 and every weight enters exactly.  Returns
+ * Q4_OK or an error code. */
+Q4_API int32_t q4_sb_matmul(const void *x, const void *w_q, const void *w_d,
+                            const void *w_sc, void *y, int32_t y_dtype, int64_t M,
+                            int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                            q4_stream_t stream);
+
 /* Dequantise W to fp32 ((c-8)*s, exact) or bf16 (that value rounded
  * nearest-even): w_out [N][K] device, out_dtype Q4_F32 or Q4_BF16.  Same
  * conventions as q4_matmul (N == 0 is a no-op). */

@@ -16,6 +16,9 @@ of the C ABI in ``include/q4.h``:
                  stream=None) -> y
     q4_dequantize(w_q, w_s, out=None, out_dtype=torch.float32, stream=None) -> w
     q4_quantize(w, w_q=None, w_s=None, stream=None) -> (w_q, w_s)
+    q4_sb_matmul_workspace_bytes(M, N, K) -> int
+    q4_sb_matmul(x, w_q, w_d, w_sc, out=None, out_dtype=torch.float32, workspace="auto",
+                 stream=None) -> y
     q4_rmsnorm_matmul_workspace_bytes(M, N, K) -> int
     q4_rmsnorm_matmul(x, gamma, eps, w_q, w_s, out=None, out_dtype=torch.float32,
                       workspace="auto", stream=None) -> y
@@ -70,6 +73,7 @@ __all__ = [
     "q4_matmul",
     "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize", "q4_moe_workspace_bytes",
     "q4_rmsnorm_matmul_workspace_bytes", "q4_rmsnorm_matmul", "q4_quantize",
+    "q4_sb_matmul_workspace_bytes", "q4_sb_matmul",
     "q4_moe_matmul", "q4_moe_matmul_noalloc", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
     "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
 ]
@@ -108,6 +112,10 @@ def _open():
                                     ctypes.c_size_t, P]
     L.q4_rmsnorm_matmul.restype = I32
     L.q4_quantize.argtypes = [P, P, P, I64, I64, P]
+    L.q4_sb_matmul_workspace_bytes.argtypes = [I64, I64, I64]
+    L.q4_sb_matmul_workspace_bytes.restype = ctypes.c_size_t
+    L.q4_sb_matmul.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, ctypes.c_size_t, P]
+    L.q4_sb_matmul.restype = I32
     L.q4_quantize.restype = I32
     L.q4_dequantize.argtypes = [P, P, P, I32, I64, I64, P]
     L.q4_dequantize.restype = I32
@@ -362,6 +370,43 @@ def q4_quantize(w, w_q=None, w_s=None, stream=None):
     if st != Q4_OK:
         raise Q4Error(st, "q4_quantize")
     return w_q, w_s
+
+
+def q4_sb_matmul_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q4_sb_matmul_workspace_bytes(int(M), int(N), int(K)))
+
+
+def q4_sb_matmul(x, w_q, w_d, w_sc, out=None, out_dtype=None, workspace="auto", stream=None):
+    """y = x . W^T with super-block scales: w = (code - 8) * d[k/256] * sc[k/32];
+    w_d fp16 [N][K/256], w_sc uint8 [N][K/32].  workspace: "auto" allocates
+    one (a torch tensor on the call's stream), or a uint8 device tensor."""
+    torch = _torch()
+    _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _check_dev(w_q, "w_q", (torch.uint8,), 2)
+    _check_dev(w_d, "w_d", (torch.float16, torch.int16, torch.uint16), 2)
+    _check_dev(w_sc, "w_sc", (torch.uint8,), 2)
+    M, K = x.shape
+    N = w_q.shape[0]
+    if (w_q.shape[1] * 2 != K or K % 256 or tuple(w_d.shape) != (N, K // 256)
+            or tuple(w_sc.shape) != (N, K // 32)):
+        raise ValueError("shape mismatch (K a multiple of 256)")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=x.device)
+    else:
+        _check_dev(out, "out", (torch.float32, torch.bfloat16), 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto" or a device tensor')
+        need = q4_sb_matmul_workspace_bytes(M, N, K)
+        workspace = _scratch(torch, max(need, 1), x.device, stream)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.q4_sb_matmul(_ptr(x), _ptr(w_q), _ptr(w_d), _ptr(w_sc), _ptr(out), _out_code(out.dtype),
+                          M, N, K, _ptr(workspace), nbytes, _stream_handle(stream, x.device))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_sb_matmul")
+    return out
 
 
 def q4_dequantize(w_q, w_s, out=None, out_dtype=None, stream=None):

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq4.so")
 SOURCES = ["q4_api.hip", "q4_dequant.hip", "q4_gemv.hip", "q4_gemm.hip", "q4_moe.hip", "q4_mx.hip",
-           "q4_norm.hip", "q4_quant.hip", "q4_small.hip"]
+           "q4_norm.hip", "q4_quant.hip", "q4_sb.hip",
+           "q4_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are kept out of the code objects on purpose.

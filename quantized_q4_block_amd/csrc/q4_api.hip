@@ -220,6 +220,36 @@ Q4_API int32_t q4_rmsnorm_matmul(const void* x, const void* gamma, float eps, co
       M, N, K, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
+Q4_API size_t q4_sb_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 256 != 0) return 0;
+  int64_t nk;
+  if (!mul_ok(N, K, &nk) || nk > (int64_t(1) << 44)) return 0;
+  if (M == 0 || N == 0) return 0;
+  return q4::sb_scale_bytes(N, K) + q4_matmul_workspace_bytes(M, N, K);
+}
+
+Q4_API int32_t q4_sb_matmul(const void* x, const void* w_q, const void* w_d, const void* w_sc,
+                            void* y, int32_t y_dtype, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  if (y_dtype != Q4_F32 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+  if (M < 0 || K % 256 != 0) return Q4_ERR_SHAPE;
+  if (int32_t s = check_weights(N, K)) return s;
+  int64_t mk, mn, nk;
+  if (!mul_ok(M, K, &mk) || !mul_ok(M, N, &mn) || !mul_ok(N, K, &nk) || nk > (int64_t(1) << 44))
+    return Q4_ERR_SHAPE;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!x || !w_q || !w_d || !w_sc || !y) return Q4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_d) || !aligned16(w_sc) || !aligned16(y))
+    return Q4_ERR_ALIGN;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < q4::sb_scale_bytes(N, K))
+    return Q4_ERR_WORKSPACE;
+  if (int32_t s = ready()) return s;
+  return launched(q4::launch_sb_matmul(
+      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w_q),
+      static_cast<const uint16_t*>(w_d), static_cast<const uint8_t*>(w_sc), y,
+      y_dtype == Q4_BF16, M, N, K, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
 // Tiled-path K slices of q4_mx_matmul_ex (0: the call never cuts K).
 static int64_t mx_split_slices(int64_t M, int64_t N, int64_t K) {
   if (M <= kGemvMaxRows || K % 64 != 0 || q4_matmul_path_ex(M, N, K, 1) != Q4_PATH_MFMA) return 0;

@@ -137,9 +137,13 @@ __device__ __forceinline__ void store_tile(const f32x16v (&acc)[2][2], void* y, 
 // one barrier per K step: the tiles of step t + 1 are written while step t's
 // MFMAs read the other buffers.  kt_slice K steps per slice; partial != NULL
 // writes the slice's fp32 sums to partial[slice][M][N].
+//
+// SP: the block scales' storage -- uint16_t (fp16, the format's own) or float
+// (exact fp32 scales, e.g. expanded from super-block scales).
+template <typename SP>
 __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __restrict__ x,
                                                           const uint8_t* __restrict__ wq,
-                                                          const uint16_t* __restrict__ ws,
+                                                          const SP* __restrict__ ws,
                                                           void* __restrict__ y, int y_bf16,
                                                           int64_t M, int64_t N, int64_t K,
                                                           int tiles_m, int tiles_n, int kt_slice,
@@ -165,10 +169,10 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
   const int64_t bn = n0 + srow;
   const bool b_ok = bn < N;
   const uint8_t* b_src = wq + (b_ok ? bn : 0) * (K / 2);
-  const uint16_t* s_src = ws + (b_ok ? bn : 0) * bpr;
+  const SP* s_src = ws + (b_ok ? bn : 0) * bpr;
   const ExactBf16Unpacker unpack;
   uint4 b_codes;
-  uint16_t b_scale;
+  SP b_scale;
   // Unconditional loads (rows past N read row 0, the missing block of a half
   // step reads the row's last block): a load under a branch makes the
   // compiler wait for it inside the branch.
@@ -187,7 +191,10 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_kernel(const uint16_t* __res
       const u32x4 v = {o[0], o[1], o[2], o[3]};
       *reinterpret_cast<u32x4*>(&Bs[buf][swz(srow, shalf * 4 + i) * 8]) = v;
     }
-    Ss[buf][srow * 2 + shalf] = b_ok ? fp16_to_f32(b_scale) : 0.0f;   // rows past N add zero
+    float sv;
+    if constexpr (std::is_same<SP, float>::value) sv = b_scale;
+    else sv = fp16_to_f32(b_scale);
+    Ss[buf][srow * 2 + shalf] = b_ok ? sv : 0.0f;   // rows past N add zero
   };
 
   f32x16v acc[2][2];
@@ -525,7 +532,13 @@ hipError_t launch_tiled(Kernel kernel, const uint16_t* x, const uint8_t* wq, con
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                        bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                        hipStream_t stream) {
-  return launch_tiled(gemm_q4_kernel, x, wq, ws, y, y_bf16, M, N, K, partial, stream);
+  return launch_tiled(gemm_q4_kernel<uint16_t>, x, wq, ws, y, y_bf16, M, N, K, partial, stream);
+}
+
+hipError_t launch_gemm_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                            bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                            hipStream_t stream) {
+  return launch_tiled(gemm_q4_kernel<float>, x, wq, ws, y, y_bf16, M, N, K, partial, stream);
 }
 
 hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,

@@ -137,9 +137,9 @@ __device__ __forceinline__ void block_rows_bf16(const CodeUnpacker& unpack, cons
 }
 
 // The same with fp32 activations xv[m][k], k = 0..31 within the block.
-template <int M, int RR>
+template <int M, int RR, typename SC>
 __device__ __forceinline__ void block_rows_f32(const CodeUnpacker& unpack, const uint4 (&c)[RR],
-                                               const _Float16 (&s)[RR], const float (&xv)[M][32],
+                                               const SC (&s)[RR], const float (&xv)[M][32],
                                                float (&acc)[RR][M]) {
 #pragma unroll
   for (int r = 0; r < RR; ++r) {
@@ -399,7 +399,8 @@ struct XStagerF32 {
 // bounds); the caller discards their results.
 enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2 };
 
-// SC: how a block scale is held -- _Float16 (the int4 codes' fp16 scales) or
+// SC: how a block scale is held -- _Float16 (the int4 codes' fp16 scales),
+// float (exact fp32 block scales, e.g. expanded from super-block scales) or
 // uint8_t (the E8M0 bytes of 4-bit float blocks).
 template <int R, int FULL, int TAIL, typename SC = _Float16>
 struct UpfrontLoads {
@@ -414,6 +415,7 @@ __device__ __forceinline__ void load_scale(const uint16_t* p, _Float16& s) {
   s = __builtin_bit_cast(_Float16, *p);
 }
 __device__ __forceinline__ void load_scale(const uint8_t* p, uint8_t& s) { s = *p; }
+__device__ __forceinline__ void load_scale(const float* p, float& s) { s = *p; }
 
 // cbase / sbase: codes and scales of the task's first row at the first
 // block of the row piece; row_bytes / row_sc: distance between rows (bytes,
@@ -562,9 +564,9 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] += ok ? t[r][m] : 0.0f;
     } else {
-      _Float16 sc[R];
+      SC sc[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (_Float16)0.0f;
+      for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (SC)0.0f;
       rows(FULL, lane, b.ct, sc, acc);
     }
   }

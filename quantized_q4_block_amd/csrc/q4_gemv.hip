@@ -22,6 +22,8 @@
 // Every product x * (c - 8) is exact and each 32-element block is summed on
 // its own before its scale is applied, so a row of zero weights (all codes
 // 8) gives exactly zero.
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_gemv.h"
 #include "q4_launch.h"
@@ -66,12 +68,16 @@ __device__ __forceinline__ void store_rows(void* __restrict__ y, int y_bf16, int
 // sums in the same fixed order, forms r = 1 / sqrt(sum / K + eps) and
 // multiplies its outputs by r, since y = r * sum_k (x gamma)_k w_k.  Every
 // workgroup computes the same r; the prologue adds no barrier.
-template <int M, int FULL, int TAIL, bool NORM = false>
+//
+// SP: the block scales' storage -- uint16_t (fp16, the format's own) or float
+// (exact fp32 scales, e.g. expanded from super-block scales).
+template <int M, int FULL, int TAIL, bool NORM = false, typename SP = uint16_t>
 __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
-    const uint16_t* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t N, int64_t K,
+    const SP* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t N, int64_t K,
     int rem, int64_t ld_blocks, int slice0, int slice_blocks, float* __restrict__ partial,
     const uint16_t* __restrict__ gamma = nullptr, float eps = 0.0f) {
+  using SC = typename std::conditional<std::is_same<SP, float>::value, float, _Float16>::type;
   constexpr int R = kLdsRows;
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[M * S * 8 * kWave];
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
   xst.load(x + blk0 * kBlock, K, ld_blocks * kBlock);
   XStager<1, S, kLdsWaves * 64> gst;
   if constexpr (NORM) gst.load(gamma, K, 0);
-  UpfrontLoads<R, FULL, TAIL> b;
+  UpfrontLoads<R, FULL, TAIL, SC> b;
   upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes + blk0 * 16,
                               ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
                               lane);
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
   // nothing (an early exit would let the compiler sink its loads past the
   // barrier)
   float out[R][M];
-  upfront_compute<M, R, FULL, TAIL>(b, xs, rem, lane, out);
+  upfront_compute<M, R, FULL, TAIL, SC>(b, xs, rem, lane, out);
   if constexpr (NORM) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -300,6 +306,32 @@ hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* gamma, float eps,
   if (!gemv_norm_fits(M, K)) return hipErrorInvalidValue;
   if (M == 1) return launch_norm_m<1>(x, gamma, eps, wq, ws, y, y_bf16, N, K, stream);
   return launch_norm_m<2>(x, gamma, eps, wq, ws, y, y_bf16, N, K, stream);
+}
+
+// The matrix-vector kernel with exact fp32 block scales [N][K/32] (M <= 2,
+// whole rows that fit its LDS staging: gemv_norm_fits).
+template <int M>
+static hipError_t launch_f32s_m(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                                bool y_bf16, int64_t N, int64_t K, hipStream_t stream) {
+  const int rem = row_leftover(K);
+  const int64_t bpr = K / kBlock;
+  return dispatch_row_geometry(K, [&](auto full, auto tail) {
+    constexpr int FULL = decltype(full)::value, TAIL = decltype(tail)::value;
+    const int64_t tasks = (N + kLdsRows - 1) / kLdsRows;
+    const int64_t grid = (tasks + kLdsWaves - 1) / kLdsWaves;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemv_lds_kernel<M, FULL, TAIL, false, float>
+        <<<dim3((unsigned)grid), dim3(kLdsWaves * 64), 0, stream>>>(
+            x, wq, ws, y, y_bf16 ? 1 : 0, N, K, rem, bpr, 0, 0, nullptr);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_gemv_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                            bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (!gemv_norm_fits(M, K)) return hipErrorInvalidValue;
+  if (M == 1) return launch_f32s_m<1>(x, wq, ws, y, y_bf16, N, K, stream);
+  return launch_f32s_m<2>(x, wq, ws, y, y_bf16, N, K, stream);
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,

@@ -94,6 +94,26 @@ hipError_t launch_moe_noalloc(const uint16_t* x, const uint8_t* wq, const uint16
                               const int32_t* ids, const float* gates, float* y, int64_t T,
                               int64_t topk, int64_t E, int64_t N, int64_t K, hipStream_t stream);
 
+// The int4 kernels with exact fp32 block scales [N][K/32] in place of fp16
+// ones (super-block scales expanded): matrix-vector (M <= 2, whole rows that
+// fit gemv_norm_fits), few-row and tiled forms.
+hipError_t launch_gemv_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                            bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_small_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                             bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                            bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                            hipStream_t stream);
+
+// Super-block scales: the fp32 block scales into the first sb_scale_bytes of
+// the workspace, then the product (K slices when the rest of the workspace
+// holds q4_matmul_workspace_bytes).  K a multiple of 256.
+size_t sb_scale_bytes(int64_t N, int64_t K);
+hipError_t launch_sb_matmul(const uint16_t* x, const uint8_t* wq, const uint16_t* wd,
+                            const uint8_t* wsc, void* y, bool y_bf16, int64_t M, int64_t N,
+                            int64_t K, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 // Routed expert FFN; the MoE layout for N = H followed by the SwiGLU
 // outputs act [T * topk][F] (fp32).  H and F at most 8192 (4 stages).
 struct MoeFfnLayout {

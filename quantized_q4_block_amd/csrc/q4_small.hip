@@ -102,12 +102,15 @@ __device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
 // aligned load (8 bytes of fp16, or 4 E8M0 bytes).
 // MX: 4-bit float blocks (scales are E8M0 bytes); else int4 codes with fp16
 // scales.
-template <int MG, bool SCALE4, bool MX>
+// F32S: int4 codes with exact fp32 block scales [N][K/32] (e.g. expanded from
+// super-block scales) instead of fp16 ones.
+template <int MG, bool SCALE4, bool MX, bool F32S = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 4 : 2))) void small_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsv, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
     int64_t K, int64_t groups_per_wave) {
-  using ScaleT = typename std::conditional<MX, uint8_t, uint16_t>::type;
+  using ScaleT = typename std::conditional<
+      MX, uint8_t, typename std::conditional<F32S, float, uint16_t>::type>::type;
   const ScaleT* ws = static_cast<const ScaleT*>(wsv);
   __shared__ f32x4v red[kWaves][kNg][MG][64];
   const int lane = threadIdx.x & 63;
@@ -167,6 +170,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             scale[d][ng][j] = e8m0_to_f32(srow[ng][b0 + j < bpr ? b0 + j : bpr - 1]);
+        }
+      } else if constexpr (F32S) {
+        if constexpr (SCALE4) {
+          const f32x4v s = *reinterpret_cast<const f32x4v*>(srow[ng] + b0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) scale[d][ng][j] = s[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) scale[d][ng][j] = srow[ng][b0 + j < bpr ? b0 + j : bpr - 1];
         }
       } else if constexpr (SCALE4) {
         const u32x2 s = *reinterpret_cast<const u32x2*>(srow[ng] + b0);
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
 
 namespace {
 
-template <int MG, bool MX>
+template <int MG, bool MX, bool F32S = false>
 hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const void* ws, void* y,
                      bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t bpr = K / 32, groups = (bpr + 3) / 4;
@@ -265,10 +277,10 @@ hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const void* ws, void*
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)gy);
   if (bpr % 4 == 0)
-    small_kernel<MG, true, MX><<<grid, dim3(kWaves * 64), 0, stream>>>(
+    small_kernel<MG, true, MX, F32S><<<grid, dim3(kWaves * 64), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw);
   else
-    small_kernel<MG, false, MX><<<grid, dim3(kWaves * 64), 0, stream>>>(
+    small_kernel<MG, false, MX, F32S><<<grid, dim3(kWaves * 64), 0, stream>>>(
         x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw);
   return hipGetLastError();
 }
@@ -279,6 +291,12 @@ hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws
                         bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M <= 16) return launch_mg<1, false>(x, wq, ws, y, y_bf16, M, N, K, stream);
   return launch_mg<2, false>(x, wq, ws, y, y_bf16, M, N, K, stream);
+}
+
+hipError_t launch_small_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
+                             bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M <= 16) return launch_mg<1, false, true>(x, wq, ws, y, y_bf16, M, N, K, stream);
+  return launch_mg<2, false, true>(x, wq, ws, y, y_bf16, M, N, K, stream);
 }
 
 hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,

@@ -50,6 +50,7 @@ def test_header_declares_the_abi():
                          "q4_matmul",
                          "q4_matmul_workspace_bytes", "q4_matmul_ex", "q4_dequantize",
                          "q4_rmsnorm_matmul_workspace_bytes", "q4_rmsnorm_matmul", "q4_quantize",
+                         "q4_sb_matmul_workspace_bytes", "q4_sb_matmul",
                          "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_matmul_noalloc",
                          "q4_moe_ffn_workspace_bytes",
                          "q4_moe_ffn", "q4_mx_matmul", "q4_mx_matmul_workspace_bytes",
