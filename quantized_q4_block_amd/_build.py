@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq4.so")
-SOURCES = ["q4_api.hip", "q4_dequant.hip", "q4_gemv.hip", "q4_gemm.hip", "q4_moe.hip", "q4_mx.hip",
+SOURCES = ["q4_api.hip", "q4_dequant.hip", "q4_gemv.hip", "q4_gemm.hip", "q4_moe.hip",
+           "q4_moe_mm.hip", "q4_mx.hip",
            "q4_norm.hip", "q4_quant.hip", "q4_sb.hip",
            "q4_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,7 +26,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hi
 # The tiled kernel applies each block's scale to the MFMA partial with VALU
 # fmas; with the MFMA results in VGPRs (not AGPRs) those partials need no
 # copy before the fmas read them.
-EXTRA = {"q4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"q4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "q4_moe_mm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -78,7 +78,7 @@ int64_t gemm_split_slices(int64_t M, int64_t N, int64_t K);
 
 // Expert-routed rows; workspace laid out by moe_workspace_layout.
 struct MoeLayout {
-  size_t counts, fill, offsets, order, active, num_active, partial, total;
+  size_t counts, fill, offsets, order, active, num_active, items, num_items, partial, total;
 };
 MoeLayout moe_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t N);
 
@@ -113,6 +113,41 @@ hipError_t launch_sb_matmul(const uint16_t* x, const uint8_t* wq, const uint16_t
                             const uint8_t* wsc, void* y, bool y_bf16, int64_t M, int64_t N,
                             int64_t K, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+// Grouped matrix-core product over the expert buckets, for routed rows with
+// many pairs per expert (moe_use_grouped: at least kMoeMmMinPairsPerExpert
+// pairs per touched expert on average).  The prep tables plus the slab list
+// (expert, first pair) that launch_moe_items writes.
+#ifndef Q4_MOE_MM_MIN_PAIRS
+#define Q4_MOE_MM_MIN_PAIRS 4
+#endif
+constexpr int64_t kMoeMmMinPairsPerExpert = Q4_MOE_MM_MIN_PAIRS;
+struct MoeMmTables {
+  const int32_t *counts, *offsets, *order, *items, *num_items;
+};
+bool moe_use_grouped(int64_t P, int64_t E);
+// Pairs per slab of the grouped product.
+int moe_mm_rows();
+// Slab list length bound for P pairs over A touched experts, slabs of tm.
+int64_t moe_mm_max_items(int64_t P, int64_t A, int tm);
+hipError_t launch_moe_items(const int32_t* counts, const int32_t* active,
+                            const int32_t* num_active, int32_t* items, int32_t* num_items,
+                            int tm, hipStream_t stream);
+// Plain routed rows: fp32 partial [P][N].
+hipError_t launch_moe_mm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
+                         const MoeMmTables& t, float* partial, int64_t max_items, int64_t topk,
+                         int64_t N, int64_t K, hipStream_t stream);
+// Gate/up rows of the routed FFN with the SwiGLU in the store: act as bf16
+// hi / lo [P][F] (times gates[p] when gates is not NULL).
+hipError_t launch_moe_mm_glu(const uint16_t* x, const uint8_t* w13q, const uint16_t* w13s,
+                             const MoeMmTables& t, const float* gates, uint16_t* act_hi,
+                             uint16_t* act_lo, int64_t max_items, int64_t topk, int64_t F,
+                             int64_t H, hipStream_t stream);
+// Down rows of the routed FFN over the hi / lo activations: fp32 partial [P][H].
+hipError_t launch_moe_mm_down(const uint16_t* act_hi, const uint16_t* act_lo,
+                              const uint8_t* w2q, const uint16_t* w2s, const MoeMmTables& t,
+                              float* partial, int64_t max_items, int64_t H, int64_t F,
+                              hipStream_t stream);
 
 // Routed expert FFN; the MoE layout for N = H followed by the SwiGLU
 // outputs act [T * topk][F] (fp32).  H and F at most 8192 (4 stages).

@@ -52,6 +52,10 @@ MoeLayout moe_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_t N) {
   L.order = o;      o = align_up(o + 4 * P);
   L.active = o;     o = align_up(o + 4 * A);
   L.num_active = o; o = align_up(o + 4);
+  // slab list of the grouped product (at its smallest slab)
+  const size_t U = (size_t)moe_mm_max_items((int64_t)P, (int64_t)A, moe_mm_rows());
+  L.items = o;      o = align_up(o + 8 * U);
+  L.num_items = o;  o = align_up(o + 4);
   L.partial = o;    o = align_up(o + 4 * P * (size_t)N);
   L.total = o;
   return L;
@@ -370,14 +374,24 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
 namespace {
 
 struct MoeBuffers {
-  int32_t *counts, *fill, *offsets, *order, *active, *num_active;
+  int32_t *counts, *fill, *offsets, *order, *active, *num_active, *items, *num_items;
 };
 
 MoeBuffers moe_buffers(void* workspace, const MoeLayout& L) {
   char* w = static_cast<char*>(workspace);
   return {reinterpret_cast<int32_t*>(w + L.counts), reinterpret_cast<int32_t*>(w + L.fill),
           reinterpret_cast<int32_t*>(w + L.offsets), reinterpret_cast<int32_t*>(w + L.order),
-          reinterpret_cast<int32_t*>(w + L.active), reinterpret_cast<int32_t*>(w + L.num_active)};
+          reinterpret_cast<int32_t*>(w + L.active), reinterpret_cast<int32_t*>(w + L.num_active),
+          reinterpret_cast<int32_t*>(w + L.items), reinterpret_cast<int32_t*>(w + L.num_items)};
+}
+
+// The slab list for the grouped product; its tables and list bound.
+hipError_t moe_grouped_items(const MoeBuffers& b, int tm, hipStream_t stream) {
+  return launch_moe_items(b.counts, b.active, b.num_active, b.items, b.num_items, tm, stream);
+}
+
+MoeMmTables moe_tables(const MoeBuffers& b) {
+  return {b.counts, b.offsets, b.order, b.items, b.num_items};
 }
 
 hipError_t moe_prep(const int32_t* ids, int64_t P, int64_t E, const MoeBuffers& b,
@@ -437,7 +451,14 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
   hipError_t err = moe_prep(ids, P, E, b, stream);
   if (err != hipSuccess) return err;
   if (max_active > 65535) return hipErrorInvalidValue;
-  if (max_active > 0) {
+  if (max_active > 0 && moe_use_grouped(P, E)) {
+    const int tm = moe_mm_rows();
+    err = moe_grouped_items(b, tm, stream);
+    if (err != hipSuccess) return err;
+    err = launch_moe_mm(x, wq, ws, moe_tables(b), partial, moe_mm_max_items(P, max_active, tm),
+                        topk, N, K, stream);
+    if (err != hipSuccess) return err;
+  } else if (max_active > 0) {
     if (x_stages(K) <= kLdsMaxStages) {
       err = moe_stage_lds<kRowsPlain>(x, wq, ws, b, partial, topk, N, K, max_active, stream);
     } else {
@@ -521,7 +542,21 @@ hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t
   hipError_t err = moe_prep(ids, P, E, b, stream);
   if (err != hipSuccess) return err;
   if (max_active > 65535) return hipErrorInvalidValue;
-  if (max_active > 0) {
+  if (max_active > 0 && moe_use_grouped(P, E)) {
+    // act as bf16 hi [P][F] then lo [P][F]: the same bytes as fp32 [P][F]
+    uint16_t* act_hi = reinterpret_cast<uint16_t*>(act);
+    uint16_t* act_lo = act_hi + P * F;
+    const int tm = moe_mm_rows();
+    const int64_t max_items = moe_mm_max_items(P, max_active, tm);
+    err = moe_grouped_items(b, tm, stream);
+    if (err != hipSuccess) return err;
+    err = launch_moe_mm_glu(x, w13q, w13s, moe_tables(b), nullptr, act_hi, act_lo, max_items,
+                            topk, F, H, stream);
+    if (err != hipSuccess) return err;
+    err = launch_moe_mm_down(act_hi, act_lo, w2q, w2s, moe_tables(b), partial, max_items, H, F,
+                             stream);
+    if (err != hipSuccess) return err;
+  } else if (max_active > 0) {
     err = moe_stage_lds<kRowsGlu>(x, w13q, w13s, b, act, topk, 2 * F, H, max_active, stream);
     if (err != hipSuccess) return err;
     err = moe_stage_lds<kRowsDown>(act, w2q, w2s, b, partial, 1, H, F, max_active, stream);
