@@ -72,7 +72,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 8
+#define Q4_ABI_VERSION 9
 
 /* Status codes. */
 #define Q4_OK            0
@@ -87,6 +87,7 @@ extern "C" {
                                in place, nothing launched (ABI version 8) */
 #define Q4_ERR_SCRATCH   9  /* needs more than Q4_MOE_NOALLOC_MAX_BYTES of the
                                built-in scratch (q4_moe_matmul_noalloc) */
+#define Q4_ERR_FLAGS    10  /* unknown bits in a flags argument */
 
 /* Output dtypes. */
 #define Q4_F32  0
@@ -327,6 +328,25 @@ Q4_API int32_t q4_moe_ffn(const void *x, const void *w13_q, const void *w13_s,
                           const int32_t *topk_ids, const float *topk_w, float *y,
                           int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
                           void *workspace, size_t workspace_bytes, q4_stream_t stream);
+
+/* q4_moe_ffn with flags (ABI version 9):
+ *   Q4_MOE_WEIGHTED_DOWN  the route weights multiply the SwiGLU outputs before
+ *                         the down product (g * a_f in fp32), so the down
+ *                         products come out weighted and the final sum over a
+ *                         token's slots adds them as they are: the
+ *                         weighted-down graph shape that "Execution Policy"
+ *                         ("Layer Package Repository Spec") lists as an
+ *                         evidence-gated experiment.  Same result up to
+ *                         rounding (within the same bar).
+ * flags == 0 is q4_moe_ffn.  Unknown bits return Q4_ERR_FLAGS (checked
+ * first). */
+#define Q4_MOE_WEIGHTED_DOWN 1u
+Q4_API int32_t q4_moe_ffn_ex(const void *x, const void *w13_q, const void *w13_s,
+                             const void *w2_q, const void *w2_s,
+                             const int32_t *topk_ids, const float *topk_w, float *y,
+                             int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
+                             uint32_t flags, void *workspace, size_t workspace_bytes,
+                             q4_stream_t stream);
 
 /* y = x . dequant(W)^T with 4-bit float block weights (ABI version 5): the
  * 4-bit float block format that "spec: specialized model runtimes" (section

@@ -50,7 +50,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 8
+Q4_ABI_VERSION = 9
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -61,6 +61,8 @@ Q4_ERR_DEVICE = 6
 Q4_ERR_LAUNCH = 7
 Q4_ERR_PENDING = 8
 Q4_ERR_SCRATCH = 9
+Q4_ERR_FLAGS = 10
+Q4_MOE_WEIGHTED_DOWN = 1
 Q4_MOE_NOALLOC_MAX_BYTES = 8 << 20
 Q4_F32 = 0
 Q4_BF16 = 1
@@ -130,6 +132,9 @@ def _open():
     L.q4_moe_ffn.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_size_t,
                              P]
     L.q4_moe_ffn.restype = I32
+    L.q4_moe_ffn_ex.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64,
+                                ctypes.c_uint32, P, ctypes.c_size_t, P]
+    L.q4_moe_ffn_ex.restype = I32
     L.q4_mx_matmul.argtypes = [P, P, P, P, I32, I64, I64, I64, P]
     L.q4_mx_matmul.restype = I32
     L.q4_mx_matmul_workspace_bytes.argtypes = [I64, I64, I64]
@@ -491,10 +496,12 @@ def q4_moe_ffn_workspace_bytes(T: int, topk: int, E: int, H: int, F: int) -> int
 
 
 def q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None, workspace=None,
-               stream=None):
+               stream=None, weighted_down=False):
     """Routed expert FFN: y[T][H] = sum_j topk_w[t][j] *
     (silu(x W_gate^T) * (x W_up^T)) W_down^T of expert topk_ids[t][j]; gate and
-    up rows interleaved in w13 (row 2f gate, 2f+1 up), down weights w2 (fp32 y)."""
+    up rows interleaved in w13 (row 2f gate, 2f+1 up), down weights w2 (fp32 y).
+    weighted_down: apply the route weights before the down product
+    (Q4_MOE_WEIGHTED_DOWN)."""
     torch = _torch()
     _check_dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
     _check_dev(w13_q, "w13_q", (torch.uint8,), 3)
@@ -521,10 +528,11 @@ def q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None, workspac
     need = q4_moe_ffn_workspace_bytes(T, topk, E, H, F)
     if workspace is None:
         workspace = _scratch(torch, max(need, 1), x.device, stream)
-    st = lib.q4_moe_ffn(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
-                        _ptr(topk_ids), _ptr(topk_w), _ptr(out), T, topk, E, H, F,
-                        _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        _stream_handle(stream, x.device))
+    flags = Q4_MOE_WEIGHTED_DOWN if weighted_down else 0
+    st = lib.q4_moe_ffn_ex(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
+                           _ptr(topk_ids), _ptr(topk_w), _ptr(out), T, topk, E, H, F, flags,
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream, x.device))
     if st != Q4_OK:
         raise Q4Error(st, "q4_moe_ffn")
     return out

@@ -103,6 +103,7 @@ Q4_API const char* q4_status_str(int32_t status) {
     case Q4_ERR_LAUNCH: return "HIP runtime error at enqueue";
     case Q4_ERR_PENDING: return "a HIP error from before the call is pending (left in place; nothing launched)";
     case Q4_ERR_SCRATCH: return "the call needs more than the library's built-in scratch (no-allocation entry point)";
+    case Q4_ERR_FLAGS: return "unknown bits in a flags argument";
     default: return "unknown status";
   }
 }
@@ -400,10 +401,12 @@ Q4_API size_t q4_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t E, int
   return q4::moe_ffn_workspace_layout(T, topk, E, H, F).total;
 }
 
-Q4_API int32_t q4_moe_ffn(const void* x, const void* w13_q, const void* w13_s, const void* w2_q,
-                          const void* w2_s, const int32_t* topk_ids, const float* topk_w,
-                          float* y, int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
-                          void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+Q4_API int32_t q4_moe_ffn_ex(const void* x, const void* w13_q, const void* w13_s,
+                             const void* w2_q, const void* w2_s, const int32_t* topk_ids,
+                             const float* topk_w, float* y, int64_t T, int64_t topk, int64_t E,
+                             int64_t H, int64_t F, uint32_t flags, void* workspace,
+                             size_t workspace_bytes, q4_stream_t stream) {
+  if ((flags & ~Q4_MOE_WEIGHTED_DOWN) != 0) return Q4_ERR_FLAGS;
   if (T < 0 || topk < 0 || E < 0) return Q4_ERR_SHAPE;
   if (H <= 0 || F <= 0 || H % 32 != 0 || F % 32 != 0) return Q4_ERR_SHAPE;
   if (H > q4::kMoeFfnMaxWidth || F > q4::kMoeFfnMaxWidth) return Q4_ERR_SHAPE;
@@ -426,8 +429,16 @@ Q4_API int32_t q4_moe_ffn(const void* x, const void* w13_q, const void* w13_s, c
   return launched(q4::launch_moe_ffn(
       static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w13_q),
       static_cast<const uint16_t*>(w13_s), static_cast<const uint8_t*>(w2_q),
-      static_cast<const uint16_t*>(w2_s), topk_ids, topk_w, y, T, topk, E, H, F, workspace,
-      static_cast<hipStream_t>(stream)));
+      static_cast<const uint16_t*>(w2_s), topk_ids, topk_w, y, T, topk, E, H, F,
+      (flags & Q4_MOE_WEIGHTED_DOWN) != 0, workspace, static_cast<hipStream_t>(stream)));
+}
+
+Q4_API int32_t q4_moe_ffn(const void* x, const void* w13_q, const void* w13_s, const void* w2_q,
+                          const void* w2_s, const int32_t* topk_ids, const float* topk_w,
+                          float* y, int64_t T, int64_t topk, int64_t E, int64_t H, int64_t F,
+                          void* workspace, size_t workspace_bytes, q4_stream_t stream) {
+  return q4_moe_ffn_ex(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, y, T, topk, E, H, F, 0,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

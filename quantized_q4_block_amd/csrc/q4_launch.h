@@ -162,6 +162,7 @@ constexpr int64_t kMoeFfnMaxWidth = 8192;
 hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t* w13s,
                           const uint8_t* w2q, const uint16_t* w2s, const int32_t* ids,
                           const float* gates, float* y, int64_t T, int64_t topk, int64_t E,
-                          int64_t H, int64_t F, void* workspace, hipStream_t stream);
+                          int64_t H, int64_t F, bool weighted_down, void* workspace,
+                          hipStream_t stream);
 
 }  // namespace q4

@@ -254,7 +254,8 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
 //              fp32 partial row of pair p;
 //  kRowsGlu    the same rows against a gate/up matrix whose rows 2f, 2f+1 are
 //              the gate and up rows of unit f (a wavefront's 2 rows are one
-//              such pair); writes act[p][f] = silu(gate) * up (fp32);
+//              such pair); writes act[p][f] = silu(gate) * up (fp32), times
+//              gates[p] when gates is not NULL;
 //  kRowsDown   x: fp32 rows, one per pair (the SwiGLU output); writes the
 //              fp32 partial row of pair p.
 enum MoeRows { kRowsPlain = 0, kRowsGlu = 1, kRowsDown = 2 };
@@ -271,7 +272,8 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
     const uint16_t* __restrict__ ws, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ order,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
-    float* __restrict__ partial, int64_t topk, int64_t N, int64_t K, int rem) {
+    const float* __restrict__ gates, float* __restrict__ partial, int64_t topk, int64_t N,
+    int64_t K, int rem) {
   constexpr int R = RT;
   static_assert(MODE != kRowsGlu || R == 2, "a gate/up pair is one wavefront task");
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
@@ -329,7 +331,9 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
       if (lane == 0) {
         if constexpr (MODE == kRowsGlu) {
           const float g = out[0][0], u = out[1][0];
-          partial[(int64_t)p * (N / 2) + n0 / 2] = g / (1.0f + expf(-g)) * u;
+          float a = g / (1.0f + expf(-g)) * u;
+          if (gates != nullptr) a *= gates[p];   // route weight before the down product
+          partial[(int64_t)p * (N / 2) + n0 / 2] = a;
         } else {
 #pragma unroll
           for (int r = 0; r < R; ++r)
@@ -343,6 +347,8 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
 // y[t][n] = sum_j g[t][j] * partial[t * topk + j][n], j ascending; slots
 // with an id outside [0, E) add nothing.  The ids, gates and partials of
 // eight slots are loaded before any is used.
+// With gates NULL the partials already carry their route weights and are
+// added as they are.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restrict__ ids,
                                                           const float* __restrict__ gates,
                                                           const float* __restrict__ partial,
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
         const int64_t j = j0 + jj < topk ? j0 + jj : topk - 1;   // in bounds
         const int64_t p = t * topk + j;
         e[jj] = ids[p];
-        g[jj] = gates[p];
+        g[jj] = gates != nullptr ? gates[p] : 1.0f;
         v[jj] = partial[p * N + n];
       }
 #pragma unroll
@@ -410,7 +416,8 @@ hipError_t moe_prep(const int32_t* ids, int64_t P, int64_t E, const MoeBuffers& 
 template <int MODE>
 hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
                          const MoeBuffers& b, float* out, int64_t topk, int64_t N, int64_t K,
-                         int64_t max_active, hipStream_t stream) {
+                         int64_t max_active, hipStream_t stream,
+                         const float* gates = nullptr) {
   const int rem = row_leftover(K);
   return dispatch_row_geometry(K, [&](auto full, auto tail) {
     constexpr int FULL = decltype(full)::value;
@@ -423,7 +430,8 @@ hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
     const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
     moe_lds_kernel<FULL, decltype(tail)::value, MODE, RT>
         <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, b.counts, b.offsets, b.order,
-                                                    b.active, b.num_active, out, topk, N, K, rem);
+                                                    b.active, b.num_active, gates, out, topk, N,
+                                                    K, rem);
     return hipGetLastError();
   });
 }
@@ -531,7 +539,12 @@ MoeFfnLayout moe_ffn_workspace_layout(int64_t T, int64_t topk, int64_t E, int64_
 hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t* w13s,
                           const uint8_t* w2q, const uint16_t* w2s, const int32_t* ids,
                           const float* gates, float* y, int64_t T, int64_t topk, int64_t E,
-                          int64_t H, int64_t F, void* workspace, hipStream_t stream) {
+                          int64_t H, int64_t F, bool weighted_down, void* workspace,
+                          hipStream_t stream) {
+  // weighted_down: the route weights multiply the SwiGLU outputs, so the
+  // down products come out weighted and the final sum adds them unweighted
+  const float* act_gates = weighted_down ? gates : nullptr;
+  const float* sum_gates = weighted_down ? nullptr : gates;
   const MoeFfnLayout L = moe_ffn_workspace_layout(T, topk, E, H, F);
   const MoeBuffers b = moe_buffers(workspace, L.base);
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.base.partial);
@@ -550,19 +563,20 @@ hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t
     const int64_t max_items = moe_mm_max_items(P, max_active, tm);
     err = moe_grouped_items(b, tm, stream);
     if (err != hipSuccess) return err;
-    err = launch_moe_mm_glu(x, w13q, w13s, moe_tables(b), nullptr, act_hi, act_lo, max_items,
+    err = launch_moe_mm_glu(x, w13q, w13s, moe_tables(b), act_gates, act_hi, act_lo, max_items,
                             topk, F, H, stream);
     if (err != hipSuccess) return err;
     err = launch_moe_mm_down(act_hi, act_lo, w2q, w2s, moe_tables(b), partial, max_items, H, F,
                              stream);
     if (err != hipSuccess) return err;
   } else if (max_active > 0) {
-    err = moe_stage_lds<kRowsGlu>(x, w13q, w13s, b, act, topk, 2 * F, H, max_active, stream);
+    err = moe_stage_lds<kRowsGlu>(x, w13q, w13s, b, act, topk, 2 * F, H, max_active, stream,
+                                  act_gates);
     if (err != hipSuccess) return err;
     err = moe_stage_lds<kRowsDown>(act, w2q, w2s, b, partial, 1, H, F, max_active, stream);
     if (err != hipSuccess) return err;
   }
-  return moe_combine(ids, gates, partial, y, T, topk, E, H, stream);
+  return moe_combine(ids, sum_gates, partial, y, T, topk, E, H, stream);
 }
 
 }  // namespace q4

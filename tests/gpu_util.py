@@ -47,9 +47,9 @@ def moe(x, w_q, w_s, ids, gates):
     return host(y)
 
 
-def moe_ffn(c, ids=None, gates=None, workspace=None):
+def moe_ffn(c, ids=None, gates=None, workspace=None, weighted_down=False):
     y = q4.q4_moe_ffn(dev(c.x), dev(c.w13_q), dev(c.w13_s), dev(c.w2_q), dev(c.w2_s),
                       dev(c.ids if ids is None else ids), dev(c.gates if gates is None else gates),
-                      workspace=workspace)
+                      workspace=workspace, weighted_down=weighted_down)
     torch.cuda.synchronize()
     return host(y)

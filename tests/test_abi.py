@@ -53,7 +53,8 @@ def test_header_declares_the_abi():
                          "q4_sb_matmul_workspace_bytes", "q4_sb_matmul",
                          "q4_moe_workspace_bytes", "q4_moe_matmul", "q4_moe_matmul_noalloc",
                          "q4_moe_ffn_workspace_bytes",
-                         "q4_moe_ffn", "q4_mx_matmul", "q4_mx_matmul_workspace_bytes",
+                         "q4_moe_ffn", "q4_moe_ffn_ex", "q4_mx_matmul",
+                         "q4_mx_matmul_workspace_bytes",
                          "q4_mx_matmul_ex"}
 
 
@@ -74,7 +75,7 @@ def test_constants_match_header():
     d = _defines()
     for name in ("Q4_ABI_VERSION", "Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN",
                  "Q4_ERR_DTYPE", "Q4_ERR_WORKSPACE", "Q4_ERR_DEVICE", "Q4_ERR_LAUNCH",
-                 "Q4_ERR_PENDING", "Q4_ERR_SCRATCH",
+                 "Q4_ERR_PENDING", "Q4_ERR_SCRATCH", "Q4_ERR_FLAGS", "Q4_MOE_WEIGHTED_DOWN",
                  "Q4_F32", "Q4_BF16", "Q4_PATH_GEMV", "Q4_PATH_MFMA", "Q4_PATH_SMALL"):
         assert getattr(q4, name) == d[name], name
     assert L.q4_abi_version() == d["Q4_ABI_VERSION"]
@@ -83,11 +84,11 @@ def test_constants_match_header():
 def test_status_strings():
     q4, L = _lib()
     seen = set()
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = q4.q4_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 10
+    assert len(seen) == 11
     assert q4.q4_status_str(99) == "unknown status"
     assert q4.q4_status_str(-1) == "unknown status"
 
@@ -377,6 +378,27 @@ def test_moe_ffn_argument_errors():
     assert ffn(wb=need - 1) == q4.Q4_ERR_WORKSPACE
     if not _gpu_present():
         assert ffn() == q4.Q4_ERR_DEVICE
+
+    def ffn_ex(flags, **kw):
+        a = dict(x=A, w13q=A, w13s=A, w2q=A, w2s=A, ids=A, g=A, y=A, T=T, topk=topk, E=E, H=H,
+                 F=F, w=A, wb=need)
+        a.update(kw)
+        return L.q4_moe_ffn_ex(P(a["x"]), P(a["w13q"]), P(a["w13s"]), P(a["w2q"]), P(a["w2s"]),
+                               P(a["ids"]), P(a["g"]), P(a["y"]), a["T"], a["topk"], a["E"],
+                               a["H"], a["F"], flags, P(a["w"]), a["wb"], None)
+
+    # unknown flag bits first, then the same checks as q4_moe_ffn
+    for flags in (2, 4, 0x80000000, 0xFFFFFFFF):
+        assert ffn_ex(flags) == q4.Q4_ERR_FLAGS, flags
+        assert ffn_ex(flags, H=100) == q4.Q4_ERR_FLAGS, flags
+    for flags in (0, q4.Q4_MOE_WEIGHTED_DOWN):
+        assert ffn_ex(flags, H=100) == q4.Q4_ERR_SHAPE
+        assert ffn_ex(flags, x=0) == q4.Q4_ERR_NULL
+        assert ffn_ex(flags, y=MIS) == q4.Q4_ERR_ALIGN
+        assert ffn_ex(flags, wb=need - 1) == q4.Q4_ERR_WORKSPACE
+        assert ffn_ex(flags, T=0, x=0, y=0, w=0) == q4.Q4_OK
+        if not _gpu_present():
+            assert ffn_ex(flags) == q4.Q4_ERR_DEVICE
 
 
 def test_binding_rejects_host_tensors():

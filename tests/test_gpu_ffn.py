@@ -68,3 +68,21 @@ def test_moe_ffn_deterministic_and_workspace_reuse():
     y3 = moe_ffn(d, workspace=work)
     y_ref, b = oracle.moe_ffn(d.x, d.w13_q, d.w13_s, d.w2_q, d.w2_s, d.ids, d.gates)
     _check(y3, y_ref, b, "reused workspace")
+
+
+# Route weights before the down product (Q4_MOE_WEIGHTED_DOWN): the same
+# oracle result within the same bar, on the per-token path (few pairs per
+# expert) and on the grouped path (many), with repeated and invalid ids.
+@pytest.mark.parametrize("T,topk,E,H,F", [(5, 3, 4, 96, 64), (8, 8, 16, 256, 160),
+                                          (40, 2, 3, 256, 160), (33, 8, 16, 1024 + 32, 512 + 96)])
+def test_moe_ffn_weighted_down(T, topk, E, H, F):
+    c = synthetic.moe_ffn_case(8300 + T + H + F, T, topk, E, H, F)
+    ids = c.ids.copy()
+    ids[0, -1] = E          # ignored
+    if topk > 1:
+        ids[1, 1] = ids[1, 0]   # summed
+    y = moe_ffn(c, ids=ids, weighted_down=True)
+    y_ref, b = oracle.moe_ffn(c.x, c.w13_q, c.w13_s, c.w2_q, c.w2_s, ids, c.gates)
+    _check(y, y_ref, b, f"weighted down T={T} topk={topk} E={E} H={H} F={F}")
+    y2 = moe_ffn(c, ids=ids, weighted_down=True)
+    assert np.array_equal(y, y2)
