@@ -140,10 +140,12 @@ Q4_API int32_t q4_matmul_path_ex(int64_t M, int64_t N, int64_t K, int32_t with_w
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 0;
   const int32_t path = q4_matmul_path_ex(M, N, K, 1);
-  if (path == Q4_PATH_SMALL) return 0;
   int64_t slices;   // 0: the call never cuts its rows
   if (path == Q4_PATH_GEMV) {
     slices = q4::gemv_split_slices(M, K);
+  } else if (path == Q4_PATH_SMALL) {
+    slices = q4::small_split_slices(M, N, K);
+    if (slices == 1) slices = 0;
   } else {
     slices = q4::gemm_split_slices(M, N, K);
     if (slices == 1) slices = 0;
@@ -178,7 +180,8 @@ Q4_API int32_t q4_matmul_ex(const void* x, const void* w_q, const void* w_s, voi
   const auto* sp = static_cast<const uint16_t*>(w_s);
   switch (q4_matmul_path_ex(M, N, K, partial != nullptr)) {
     case Q4_PATH_GEMV: return launched(q4::launch_gemv(xp, wp, sp, y, bf16, M, N, K, partial, st));
-    case Q4_PATH_SMALL: return launched(q4::launch_small(xp, wp, sp, y, bf16, M, N, K, st));
+    case Q4_PATH_SMALL:
+      return launched(q4::launch_small(xp, wp, sp, y, bf16, M, N, K, partial, st));
     default: return launched(q4::launch_gemm(xp, wp, sp, y, bf16, M, N, K, partial, st));
   }
 }

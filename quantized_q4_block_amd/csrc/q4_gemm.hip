@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void gemm_combine_kernel(const float* __restri
 
 // The fp32 slice sums of a cut call into y, enqueued after the product on
 // the same stream.
-static hipError_t launch_combine(const float* partial, void* y, bool y_bf16, int64_t MN,
+hipError_t launch_slice_combine(const float* partial, void* y, bool y_bf16, int64_t MN,
                                  int64_t slices, hipStream_t stream) {
   const int64_t grid = (MN + 1023) / 1024;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -523,7 +523,7 @@ hipError_t launch_tiled(Kernel kernel, const uint16_t* x, const uint8_t* wq, con
   if (slices > 1) {
     const hipError_t e = hipPeekAtLastError();
     if (e != hipSuccess) return e;
-    return launch_combine(partial, y, y_bf16, M * N, slices, stream);
+    return launch_slice_combine(partial, y, y_bf16, M * N, slices, stream);
   }
   return hipPeekAtLastError();
 }

@@ -45,8 +45,18 @@ hipError_t launch_rmsnorm_matmul(const uint16_t* x, const uint16_t* gamma, float
 
 // Few rows (3 <= M, at most 65535 slabs of 32): exact (c - 8) on the bf16
 // matrix cores, block scales applied in fp32; exact weights.
+// partial: NULL, or fp32 scratch of small_split_slices(M, N, K) * M * N
+// floats that lets a grid of few workgroups be cut along K.
 hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                        bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                        hipStream_t stream);
+
+// K slices of the few-row kernel when scratch is given (1: never cut).
+int64_t small_split_slices(int64_t M, int64_t N, int64_t K);
+
+// y = sum over s < slices, in order, of partial[s][MN] (fp32 or bf16 y).
+hipError_t launch_slice_combine(const float* partial, void* y, bool y_bf16, int64_t MN,
+                                int64_t slices, hipStream_t stream);
 
 // 4-bit float block weights (e2m1 elements, E8M0 scales), M <= 2: fused
 // dequant + matrix-vector product, exact weights.
@@ -100,7 +110,8 @@ hipError_t launch_moe_noalloc(const uint16_t* x, const uint8_t* wq, const uint16
 hipError_t launch_gemv_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
                             bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_small_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
-                             bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                             bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                             hipStream_t stream);
 hipError_t launch_gemm_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
                             bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                             hipStream_t stream);

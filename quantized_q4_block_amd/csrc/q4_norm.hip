@@ -96,7 +96,7 @@ hipError_t launch_rmsnorm_matmul(const uint16_t* x, const uint16_t* gamma, float
                        : nullptr;
   switch (q4_matmul_path_ex(M, N, K, partial != nullptr)) {
     case Q4_PATH_GEMV: return launch_gemv(xn, wq, ws, y, y_bf16, M, N, K, partial, stream);
-    case Q4_PATH_SMALL: return launch_small(xn, wq, ws, y, y_bf16, M, N, K, stream);
+    case Q4_PATH_SMALL: return launch_small(xn, wq, ws, y, y_bf16, M, N, K, partial, stream);
     default: return launch_gemm(xn, wq, ws, y, y_bf16, M, N, K, partial, stream);
   }
 }

@@ -62,10 +62,13 @@ hipError_t launch_sb_matmul(const uint16_t* x, const uint8_t* wq, const uint16_t
   float* partial = need > 0 && workspace_bytes >= sb + need
                        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + sb)
                        : nullptr;
-  if (q4_matmul_path_ex(M, N, K, partial != nullptr) == Q4_PATH_MFMA)
+  const int32_t path = q4_matmul_path_ex(M, N, K, partial != nullptr);
+  if (path == Q4_PATH_MFMA)
     return launch_gemm_f32s(x, wq, s, y, y_bf16, M, N, K, partial, stream);
-  // matrix-vector shapes past the LDS kernel's rows, and the few-row ones
-  return launch_small_f32s(x, wq, s, y, y_bf16, M, N, K, stream);
+  // matrix-vector shapes past the LDS kernel's rows (no K slices: the
+  // workspace was sized for the matrix-vector path's), and the few-row ones
+  return launch_small_f32s(x, wq, s, y, y_bf16, M, N, K,
+                           path == Q4_PATH_SMALL ? partial : nullptr, stream);
 }
 
 }  // namespace q4

@@ -58,15 +58,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bf16 (c - 8) of the 8 codes of d, in k order (exact: small integers).
-__device__ __forceinline__ bf16x8v codes_to_bf16(uint32_t d, const CodeUnpacker& unpack) {
-  half2v p[4];
-  unpack(d, p);
-  u32x4 o;
-  o[0] = pack_bf16x2((float)p[0][0], (float)p[1][0]);
-  o[1] = pack_bf16x2((float)p[2][0], (float)p[3][0]);
-  o[2] = pack_bf16x2((float)p[0][1], (float)p[1][1]);
-  o[3] = pack_bf16x2((float)p[2][1], (float)p[3][1]);
-  return __builtin_bit_cast(bf16x8v, o);
+__device__ __forceinline__ bf16x8v codes_to_bf16(uint32_t d, const ExactBf16Unpacker& unpack) {
+  uint32_t o[4];
+  unpack(d, o);
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8v, v);
 }
 
 // bf16 elements of the 8 e2m1 values of d, in k order (exact).
@@ -99,18 +95,26 @@ __device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
 }  // namespace
 
 // SCALE4: K/32 is a multiple of 4, so a row's 4 scales of a group are one
-// aligned load (8 bytes of fp16, or 4 E8M0 bytes).
+// aligned load (8 bytes of fp16, 4 E8M0 bytes or 16 bytes of fp32).
 // MX: 4-bit float blocks (scales are E8M0 bytes); else int4 codes with fp16
 // scales.
 // F32S: int4 codes with exact fp32 block scales [N][K/32] (e.g. expanded from
 // super-block scales) instead of fp16 ones.
-template <int MG, bool SCALE4, bool MX, bool F32S = false>
+// BUF: buffer-resource loads.  Every operand is addressed from a base of the
+// workgroup by a 32-bit offset made of a per-lane part fixed for the whole
+// call and a wave-uniform scalar part per group, so the loads take no vector
+// ALU work; rows of K < 2^26 (offsets below 2^31).  Otherwise 64-bit
+// per-lane pointers.
+template <int MG, bool SCALE4, bool MX, bool F32S, bool BUF>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 4 : 2))) void small_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsv, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
-    int64_t K, int64_t groups_per_wave) {
+    int64_t K, int64_t groups_per_wave, int64_t groups_per_slice, float* __restrict__ partial) {
   using ScaleT = typename std::conditional<
       MX, uint8_t, typename std::conditional<F32S, float, uint16_t>::type>::type;
+  // scales of a group as loaded: 4 fp16 in 2 dwords, 4 E8M0 bytes in 1, or
+  // 4 fp32
+  constexpr int SW = F32S ? 4 : (MX ? 1 : 2);
   const ScaleT* ws = static_cast<const ScaleT*>(wsv);
   __shared__ f32x4v red[kWaves][kNg][MG][64];
   const int lane = threadIdx.x & 63;
@@ -119,23 +123,40 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
   const int64_t bpr = K / 32;
   const int64_t n0 = (int64_t)blockIdx.x * (16 * kNg);
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MG);
-  // Rows past N (M) read row N-1 (M-1); their outputs are not stored.
-  const uint8_t* wrow[kNg];
-  const ScaleT* srow[kNg];
+  // Rows past N (M) read the workgroup's last row; their outputs are not
+  // stored.
+  const int64_t rows_w = N - n0 < 16 * kNg ? N - n0 : 16 * kNg;
+  const int64_t rows_x = M - m0 < 16 * MG ? M - m0 : 16 * MG;
+  int wl[kNg], xl[MG];   // this lane's weight and activation rows in the workgroup
 #pragma unroll
-  for (int ng = 0; ng < kNg; ++ng) {
-    const int64_t n = n0 + ng * 16 + r;
-    const int64_t nn = n < N ? n : N - 1;
-    wrow[ng] = wq + nn * (K / 2);
-    srow[ng] = ws + nn * bpr;
-  }
-  const uint16_t* xrow[MG];
+  for (int ng = 0; ng < kNg; ++ng) wl[ng] = ng * 16 + r < rows_w ? ng * 16 + r : (int)rows_w - 1;
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg) {
-    const int64_t m = m0 + mg * 16 + r;
-    xrow[mg] = x + (m < M ? m : M - 1) * K + 8 * g;
+  for (int mg = 0; mg < MG; ++mg) xl[mg] = mg * 16 + r < rows_x ? mg * 16 + r : (int)rows_x - 1;
+  const uint8_t* wq_g = wq + n0 * (K / 2);
+  const ScaleT* ws_g = ws + n0 * bpr;
+  const uint16_t* x_g = x + m0 * K;
+  __amdgpu_buffer_rsrc_t w_rsrc, s_rsrc, x_rsrc;
+  uint32_t w_off[kNg], s_off[kNg], x_off[MG];
+  if constexpr (BUF) {
+    w_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq_g), (short)0,
+                                               (int)(rows_w * (K / 2)), 0x00020000);
+    s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<ScaleT*>(ws_g), (short)0,
+                                               (int)(rows_w * bpr * (int64_t)sizeof(ScaleT)),
+                                               0x00020000);
+    x_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x_g), (short)0,
+                                               (int)(rows_x * K * 2), 0x00020000);
+#pragma unroll
+    for (int ng = 0; ng < kNg; ++ng) {
+      w_off[ng] = (uint32_t)(wl[ng] * (K / 2));
+      s_off[ng] = (uint32_t)(wl[ng] * bpr * (int64_t)sizeof(ScaleT));
+    }
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) x_off[mg] = (uint32_t)(xl[mg] * K * 2 + 16 * g);
   }
-  const CodeUnpacker unpack;
+  // K slice blockIdx.z: 4-block groups [q_beg, q_end) of the row
+  const int64_t q_beg = (int64_t)blockIdx.z * groups_per_slice;
+  const int64_t q_end = q_beg + groups_per_slice;
+  const ExactBf16Unpacker unpack;
   const f32x4v zero = {0.f, 0.f, 0.f, 0.f};
   f32x4v acc[kNg][MG];
 #pragma unroll
@@ -147,58 +168,99 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
   // the row's end reads the row's last group again (never out of bounds) and
   // is skipped when computed.
   uint32_t codes[kDepth][kNg][4];
-  float scale[kDepth][kNg][4];
+  uint32_t sraw[kDepth][kNg][SW];
   bf16x8v xf[kDepth][4][MG];
   auto load = [&](int64_t q, auto slot) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
-    int64_t b0 = q * 4;
+    int64_t b0 = q * 4;   // wave-uniform
     if (b0 >= bpr) b0 = (bpr - 1) & ~int64_t(3);
-    const int64_t bl = b0 + g < bpr ? b0 + g : bpr - 1;
+    // lane (r, g) takes block b0 + g of its row (the row's last block past
+    // its end, which only a group that is cut short reaches)
+    const int64_t bl = SCALE4 ? b0 + g : (b0 + g < bpr ? b0 + g : bpr - 1);
 #pragma unroll
     for (int ng = 0; ng < kNg; ++ng) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(wrow[ng] + bl * 16);
+      u32x4 v;
+      if constexpr (BUF) {
+        if constexpr (SCALE4)
+          v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ng] + 16 * g, (int)(b0 * 16), 0);
+        else
+          v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ng] + (uint32_t)(bl * 16), 0, 0);
+      } else {
+        v = *reinterpret_cast<const u32x4*>(wq_g + (int64_t)wl[ng] * (K / 2) + bl * 16);
+      }
       codes[d][ng][0] = v[0];
       codes[d][ng][1] = v[1];
       codes[d][ng][2] = v[2];
       codes[d][ng][3] = v[3];
-      if constexpr (MX) {
-        if constexpr (SCALE4) {
-          const uint32_t s = *reinterpret_cast<const uint32_t*>(srow[ng] + b0);
+      if constexpr (SCALE4) {
+        // the row's 4 scales of the group, as stored
+        if constexpr (BUF) {
+          const int so = (int)(b0 * (int64_t)sizeof(ScaleT));
+          if constexpr (SW == 4) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, s_off[ng], so, 0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) scale[d][ng][j] = e8m0_to_f32((s >> (8 * j)) & 0xFFu);
+            for (int j = 0; j < 4; ++j) sraw[d][ng][j] = t[j];
+          } else if constexpr (SW == 2) {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, s_off[ng], so, 0);
+            sraw[d][ng][0] = t[0];
+            sraw[d][ng][1] = t[1];
+          } else {
+            sraw[d][ng][0] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_off[ng], so, 0);
+          }
         } else {
+          const ScaleT* sp = ws_g + (int64_t)wl[ng] * bpr + b0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            scale[d][ng][j] = e8m0_to_f32(srow[ng][b0 + j < bpr ? b0 + j : bpr - 1]);
+          for (int j = 0; j < SW; ++j) sraw[d][ng][j] = reinterpret_cast<const uint32_t*>(sp)[j];
         }
-      } else if constexpr (F32S) {
-        if constexpr (SCALE4) {
-          const f32x4v s = *reinterpret_cast<const f32x4v*>(srow[ng] + b0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) scale[d][ng][j] = s[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) scale[d][ng][j] = srow[ng][b0 + j < bpr ? b0 + j : bpr - 1];
-        }
-      } else if constexpr (SCALE4) {
-        const u32x2 s = *reinterpret_cast<const u32x2*>(srow[ng] + b0);
-        scale[d][ng][0] = fp16_to_f32((uint16_t)(s[0] & 0xFFFFu));
-        scale[d][ng][1] = fp16_to_f32((uint16_t)(s[0] >> 16));
-        scale[d][ng][2] = fp16_to_f32((uint16_t)(s[1] & 0xFFFFu));
-        scale[d][ng][3] = fp16_to_f32((uint16_t)(s[1] >> 16));
       } else {
+        // one scale at a time, clamped to the row
+        ScaleT sv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          scale[d][ng][j] = fp16_to_f32(srow[ng][b0 + j < bpr ? b0 + j : bpr - 1]);
+        for (int j = 0; j < 4; ++j) {
+          const int64_t bj = b0 + j < bpr ? b0 + j : bpr - 1;
+          if constexpr (BUF) {
+            const int so = (int)(bj * (int64_t)sizeof(ScaleT));
+            if constexpr (SW == 4)
+              sv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_off[ng], so, 0));
+            else if constexpr (SW == 2)
+              sv[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_off[ng], so, 0);
+            else
+              sv[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_off[ng], so, 0);
+          } else {
+            sv[j] = ws_g[(int64_t)wl[ng] * bpr + bj];
+          }
+        }
+        if constexpr (SW == 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sraw[d][ng][j] = __builtin_bit_cast(uint32_t, sv[j]);
+        } else if constexpr (SW == 2) {
+          sraw[d][ng][0] = (uint32_t)sv[0] | ((uint32_t)sv[1] << 16);
+          sraw[d][ng][1] = (uint32_t)sv[2] | ((uint32_t)sv[3] << 16);
+        } else {
+          sraw[d][ng][0] = (uint32_t)sv[0] | ((uint32_t)sv[1] << 8) | ((uint32_t)sv[2] << 16) |
+                           ((uint32_t)sv[3] << 24);
+        }
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t bj = b0 + j < bpr ? b0 + j : bpr - 1;
+      const int64_t bj = b0 + j < bpr ? b0 + j : bpr - 1;   // wave-uniform
 #pragma unroll
-      for (int mg = 0; mg < MG; ++mg)
-        xf[d][j][mg] = *reinterpret_cast<const bf16x8v*>(xrow[mg] + bj * 32);
+      for (int mg = 0; mg < MG; ++mg) {
+        if constexpr (BUF)
+          xf[d][j][mg] = __builtin_bit_cast(
+              bf16x8v, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, x_off[mg], (int)(bj * 64), 0));
+        else
+          xf[d][j][mg] = *reinterpret_cast<const bf16x8v*>(x_g + (int64_t)xl[mg] * K + 8 * g + bj * 32);
+      }
     }
+  };
+  // block j's scale of 16-row weight group ng, from slot d
+  auto scale_of = [&](int d, int ng, int j) __attribute__((always_inline)) -> float {
+    if constexpr (SW == 4) return __builtin_bit_cast(float, sraw[d][ng][j]);
+    else if constexpr (SW == 2)
+      return (float)__builtin_bit_cast(half2v, sraw[d][ng][j >> 1])[j & 1];
+    else return e8m0_to_f32((sraw[d][ng][0] >> (8 * j)) & 0xFFu);
   };
   auto block = [&](int j, auto slot) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
@@ -210,7 +272,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
         const f32x4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[d][j][mg], w, zero, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[ng][mg][e] = __builtin_fmaf(scale[d][ng][j], p[e], acc[ng][mg][e]);
+          acc[ng][mg][e] = __builtin_fmaf(scale_of(d, ng, j), p[e], acc[ng][mg][e]);
       }
     }
   };
@@ -218,7 +280,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
     constexpr int d = decltype(slot)::value;
 #pragma unroll
     for (int ng = 0; ng < kNg; ++ng) transpose_groups(codes[d][ng]);
-    const int64_t left = bpr - q * 4;   // blocks of this group inside the row
+    // blocks of this group inside the row (none past the slice's end)
+    const int64_t left = q < q_end ? bpr - q * 4 : 0;
     if (left >= 4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) block(j, slot);
@@ -231,7 +294,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
   static_assert(kDepth == 2, "the ring below is written for two slots");
   const std::integral_constant<int, 0> s0;
   const std::integral_constant<int, 1> s1;
-  const int64_t q0 = (int64_t)wave * groups_per_wave;
+  const int64_t q0 = q_beg + (int64_t)wave * groups_per_wave;
   load(q0, s0);
   load(q0 + 1, s1);
   for (int64_t i = 0; i < groups_per_wave; i += kDepth) {
@@ -259,7 +322,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
     for (int w = 0; w < kWaves; ++w) s += red[w][ng][mg][src][mi % 4];
     const int64_t m = m0 + ml, n = n0 + nl;
     if (m < M && n < N) {
-      if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(s);
+      if (partial) partial[(int64_t)blockIdx.z * M * N + m * N + n] = s;
+      else if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(s);
       else static_cast<float*>(y)[m * N + n] = s;
     }
   }
@@ -267,42 +331,89 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
 
 namespace {
 
+#ifndef Q4_SMALL_SPLIT_WGS
+#define Q4_SMALL_SPLIT_WGS 1024
+#endif
+// Workgroups a cut call aims for (four per CU).
+constexpr int64_t kSmallSplitWgs = Q4_SMALL_SPLIT_WGS;
+
+int64_t small_groups(int64_t M) { return M <= 16 ? 1 : 2; }
+
+// Slice plan: slices * per >= groups, per a multiple of kWaves * kDepth.
+void small_plan(int64_t M, int64_t N, int64_t K, bool cut, int64_t* slices, int64_t* per) {
+  const int64_t groups = (K / 32 + 3) / 4;
+  *slices = 1;
+  *per = groups;
+  if (!cut || M <= 0 || N <= 0 || K % 32 != 0) return;
+  const int64_t mg = small_groups(M);
+  const int64_t wgs = ((N + 16 * kNg - 1) / (16 * kNg)) * ((M + 16 * mg - 1) / (16 * mg));
+  if (wgs >= kSmallSplitWgs) return;
+  constexpr int64_t unit = kWaves * kDepth;
+  const int64_t target = (kSmallSplitWgs + wgs - 1) / wgs;
+  int64_t p = (groups + target - 1) / target;
+  p = (p + unit - 1) / unit * unit;
+  const int64_t s = (groups + p - 1) / p;
+  if (s < 2) return;
+  *slices = s;
+  *per = p;
+}
+
 template <int MG, bool MX, bool F32S = false>
 hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const void* ws, void* y,
-                     bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  const int64_t bpr = K / 32, groups = (bpr + 3) / 4;
-  int64_t gpw = (groups + kWaves - 1) / kWaves;
+                     bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                     hipStream_t stream) {
+  int64_t slices, per;
+  small_plan(M, N, K, partial != nullptr, &slices, &per);
+  int64_t gpw = (per + kWaves - 1) / kWaves;
   gpw = (gpw + kDepth - 1) / kDepth * kDepth;
   const int64_t gx = (N + 16 * kNg - 1) / (16 * kNg), gy = (M + 16 * MG - 1) / (16 * MG);
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)gx, (unsigned)gy);
-  if (bpr % 4 == 0)
-    small_kernel<MG, true, MX, F32S><<<grid, dim3(kWaves * 64), 0, stream>>>(
-        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw);
-  else
-    small_kernel<MG, false, MX, F32S><<<grid, dim3(kWaves * 64), 0, stream>>>(
-        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw);
-  return hipGetLastError();
+  if (gx > 0x7FFFFFFF || gy > 65535 || slices > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)slices);
+  float* part = slices > 1 ? partial : nullptr;
+  const bool buf = K < (int64_t(1) << 26);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, dim3(kWaves * 64), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw,
+                                                   per, part);
+  };
+  if ((K / 32) % 4 == 0) {
+    if (buf) go(small_kernel<MG, true, MX, F32S, true>);
+    else go(small_kernel<MG, true, MX, F32S, false>);
+  } else {
+    if (buf) go(small_kernel<MG, false, MX, F32S, true>);
+    else go(small_kernel<MG, false, MX, F32S, false>);
+  }
+  if (slices == 1) return hipGetLastError();
+  const hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess) return e;
+  return launch_slice_combine(partial, y, y_bf16, M * N, slices, stream);
 }
 
 }  // namespace
 
+int64_t small_split_slices(int64_t M, int64_t N, int64_t K) {
+  int64_t slices, per;
+  small_plan(M, N, K, true, &slices, &per);
+  return slices;
+}
+
 hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
-                        bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (M <= 16) return launch_mg<1, false>(x, wq, ws, y, y_bf16, M, N, K, stream);
-  return launch_mg<2, false>(x, wq, ws, y, y_bf16, M, N, K, stream);
+                        bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                        hipStream_t stream) {
+  if (M <= 16) return launch_mg<1, false>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
+  return launch_mg<2, false>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
 }
 
 hipError_t launch_small_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
-                             bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (M <= 16) return launch_mg<1, false, true>(x, wq, ws, y, y_bf16, M, N, K, stream);
-  return launch_mg<2, false, true>(x, wq, ws, y, y_bf16, M, N, K, stream);
+                             bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
+                             hipStream_t stream) {
+  if (M <= 16) return launch_mg<1, false, true>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
+  return launch_mg<2, false, true>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
 }
 
 hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
                            bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (M <= 16) return launch_mg<1, true>(x, wq, we, y, y_bf16, M, N, K, stream);
-  return launch_mg<2, true>(x, wq, we, y, y_bf16, M, N, K, stream);
+  if (M <= 16) return launch_mg<1, true>(x, wq, we, y, y_bf16, M, N, K, nullptr, stream);
+  return launch_mg<2, true>(x, wq, we, y, y_bf16, M, N, K, nullptr, stream);
 }
 
 }  // namespace q4

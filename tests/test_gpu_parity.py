@@ -117,7 +117,8 @@ def test_gemv_parity(M, N, K):
 # path): two-stage slices of 86 (K = 8224), 108/109 (17408) and 128 (16384)
 # blocks; K = 258080 (8065 blocks) takes one-stage slices; K = 5696 (178
 # blocks, 3 stages) fits one workgroup and is not cut.  At M = 3, 4 the call
-# takes the few-row matrix-core path, which needs no workspace.
+# takes the few-row matrix-core path, cut along K into slices when its grid
+# has few workgroups.
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("N,K", [(37, 8192 + 32), (300, 17408), (65, 5696), (17, 16384),
                                  (5, 258080)])
@@ -189,13 +190,39 @@ def test_small_bf16_output(M):
     _check_dense(d, BF16, what=f"small bf16 M={M}")
 
 
-def test_small_ignores_a_workspace():
-    d = synthetic.dense_case(6900, 4, 300, 17408)
-    assert q4.q4_matmul_workspace_bytes(4, 300, 17408) == 0
-    work = torch.full((4096,), 0x7F, dtype=torch.uint8, device="cuda:0")
-    y = host(q4.q4_matmul_ex(dev(d.x), dev(d.w_q), dev(d.w_s), workspace=work))
+# K slices on the few-row path (q4_matmul_ex with a workspace): slices of
+# whole and ragged 4-block groups, a last slice shorter than the others, one
+# and two 16-row activation groups, and slabs past 32 rows.
+@pytest.mark.parametrize("M,N,K", [(4, 300, 17408), (3, 65, 8224), (16, 37, 4096 + 32),
+                                   (17, 300, 2048), (32, 1, 17408), (64, 300, 2048 + 96)])
+def test_small_split_parity(M, N, K):
+    assert q4.q4_matmul_path_ex(M, N, K, True) == q4.Q4_PATH_SMALL
+    need = q4.q4_matmul_workspace_bytes(M, N, K)
+    assert need > 0
+    d = synthetic.dense_case(6900 + M + N, M, N, K)
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
-    assert_parity(y, y_ref, t, RTOL, what="small with workspace")
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"small split M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"small split bf16 M={M}")
+
+
+def test_small_split_deterministic_and_workspace_reuse():
+    M, N, K = 4, 300, 17408
+    d = synthetic.dense_case(6950, M, N, K)
+    x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
+    need = q4.q4_matmul_workspace_bytes(M, N, K)
+    work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)   # junk contents
+    y1 = q4.q4_matmul_ex(x, wq, ws, workspace=work)
+    y2 = q4.q4_matmul_ex(x, wq, ws, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    e = synthetic.dense_case(6951, 5, 64, 2048)
+    y3 = host(q4.q4_matmul_ex(dev(e.x), dev(e.w_q), dev(e.w_s), workspace=work))
+    y_ref, t = oracle.matmul(e.x, e.w_q, e.w_s)
+    assert_parity(y3, y_ref, t, RTOL, what="small split, reused workspace")
+    with pytest.raises(q4.Q4Error):
+        q4.q4_matmul_ex(x, wq, ws, workspace=work[: need - 16])
 
 
 # ---------------------------------------------------- prefill (MFMA)
@@ -425,7 +452,7 @@ def test_batched_down_full_size():
     d, y = _full_dense("batched_down", F32)
     y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
     assert_parity(y, y_ref, t, RTOL, what="batched_down")
-    y = matmul_ex(d.x, d.w_q, d.w_s, F32)           # needs no workspace at M = 4
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)           # K slices in the workspace
     assert_parity(y, y_ref, t, RTOL, what="batched_down through q4_matmul_ex")
 
 
@@ -560,9 +587,9 @@ def test_non_default_stream():
     assert_parity(host(y), y_ref, t, RTOL, what="stream")
 
 
-@pytest.mark.parametrize("M,N,K", [(2, 300, 17408), (300, 200, 64 * 40)])
+@pytest.mark.parametrize("M,N,K", [(2, 300, 17408), (4, 300, 17408), (300, 200, 64 * 40)])
 def test_split_calls_on_a_non_default_stream(M, N, K):
-    """The cut calls (matrix-vector slices, tiled K slices) put their product
+    """The cut calls (matrix-vector slices, few-row and tiled K slices) put their product
     and their combine kernel on the caller's stream; the workspace is
     allocated on that stream too."""
     d = synthetic.dense_case(7400 + M, M, N, K)
