@@ -12,10 +12,12 @@ step streams its 100.27 MB of codes and scales from HBM.
 
 Printed: one JSON line with value = weight+scale GB/s (whole job), the
 roofline of the dominant kernel (the decode GEMV) from HIP events over the
-timed region, the CPU oracle's rate on the host, and the other workloads
-(batched decode M = 4, prefill M = 512, the decode shape with 4-bit float
-block weights, MoE, and the routed expert FFN built around the MoE expert
-shape) measured the same way as extra context.
+timed region, the CPU oracle's rate on the host (and on the batched decode,
+prefill and MoE shapes), the shader clock under load, and the other
+workloads (batched decode M = 4, prefill M = 512, 4-bit float block weights,
+MoE and the routed expert FFN at 8 and 512 tokens, the RMSNorm prologue and
+super-block scales at the decode and prefill shapes, the quantiser)
+measured the same way as extra context.
 """
 from __future__ import annotations
 
@@ -54,6 +56,74 @@ def csrc_digest(names=GEMV_SOURCES):
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def all_sources_digest():
+    d = os.path.join(ROOT, "quantized_q4_block_amd", "csrc")
+    return csrc_digest(tuple(n for n in os.listdir(d) if n.endswith((".hip", ".h"))))
+
+
+def git_commit():
+    """HEAD of the repository this script sits in, or None where the tree
+    carries no git metadata."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return r.stdout.strip() or None if r.returncode == 0 else None
+
+
+def kernel_resources(mangled_prefix):
+    """Register, LDS and occupancy figures the compiler reported for the
+    kernel whose mangled name starts with mangled_prefix (written by the
+    in-tree build next to the library), or None."""
+    path = os.path.join(ROOT, "quantized_q4_block_amd", "kernel_resources.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    hits = [v for k, v in table.items() if k.startswith(mangled_prefix)]
+    return hits[0] if len(hits) == 1 else None
+
+
+def sample_sclk(torch, work, seconds=1.5):
+    """The shader clock (MHz) rocm-smi reports while `work` keeps the GPU
+    busy, or None if the tool is not there or prints no clock."""
+    import re
+    import subprocess
+    import threading
+    box = {}
+
+    def query():
+        try:
+            r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True,
+                               text=True, timeout=20)
+            box["out"] = r.stdout
+        except (OSError, subprocess.SubprocessError):
+            box["out"] = ""
+    stream = torch.cuda.current_stream()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    th = threading.Thread(target=query)
+    i, t0 = 0, time.perf_counter()
+    for _ in range(200):            # busy before the query starts
+        work.step(i, h)
+        i += 1
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < seconds + 20:
+        for _ in range(100):
+            work.step(i, h)
+            i += 1
+        torch.cuda.synchronize()
+    th.join()
+    for line in box.get("out", "").splitlines():
+        if "sclk" in line.lower():
+            m = re.search(r"\((\d+)\s*Mhz\)", line, flags=re.I)
+            if m:
+                return int(m.group(1))
+    return None
 
 
 def traffic_from_profile(kernel_tag, digest):
@@ -143,9 +213,9 @@ class MxDense:
 
 
 class MoE:
-    def __init__(self, torch, q4, copies=None):
+    def __init__(self, torch, q4, copies=None, config=None):
         import synthetic
-        c = synthetic.CONFIGS["moe"]
+        c = config or synthetic.CONFIGS["moe"]
         self.T, self.topk, self.E, self.N, self.K = c["T"], c["topk"], c["E"], c["N"], c["K"]
         m = synthetic.moe_case(c["seed"], self.T, self.topk, self.E, self.N, self.K)
         dev = "cuda:0"
@@ -184,9 +254,9 @@ class MoeFfn:
     H = 4096, F = 1536 per expert, T = 8 tokens, top-8 of E = 128): gate/up
     product with the SwiGLU in its store, down product, weighted sum."""
 
-    def __init__(self, torch, q4, copies=None):
+    def __init__(self, torch, q4, copies=None, config=None):
         import synthetic
-        c = synthetic.FFN_CONFIGS["moe_ffn"]
+        c = config or synthetic.FFN_CONFIGS["moe_ffn"]
         self.T, self.topk, self.E, self.H, self.F = c["T"], c["topk"], c["E"], c["H"], c["F"]
         m = synthetic.moe_ffn_case(c["seed"], self.T, self.topk, self.E, self.H, self.F)
         dev = "cuda:0"
@@ -220,6 +290,113 @@ class MoeFfn:
         st = self.fn(*self.args[i % self.copies], stream)
         if st:
             raise RuntimeError(f"q4_moe_ffn failed with status {st}")
+
+
+class RmsDense:
+    """q4_rmsnorm_matmul on a dense shape: RMSNorm(x) * gamma as the
+    activations of the product (fused into the matrix-vector kernel at one
+    row, a prologue kernel before the product otherwise)."""
+
+    def __init__(self, torch, q4, name, copies=None):
+        import synthetic
+        c = synthetic.RMS_CONFIGS[name]
+        self.M, self.N, self.K = c["M"], c["N"], c["K"]
+        d = synthetic.rms_case(c["seed"], self.M, self.N, self.K)
+        dev = "cuda:0"
+        wb = weight_bytes(self.N, self.K)
+        n = copies or max(2, -(-ROTATE_BYTES // wb) + 1)
+        self.copies = n
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev)
+        self.gamma = torch.from_numpy(d.gamma.view(np.int16)).to(dev)
+        wq = torch.from_numpy(d.w_q).to(dev)
+        ws = torch.from_numpy(d.w_s.view(np.int16)).to(dev)
+        self.wq = [wq] + [wq.clone() for _ in range(n - 1)]
+        self.ws = [ws] + [ws.clone() for _ in range(n - 1)]
+        bf16 = c["out"] == "bf16"
+        self.y = torch.empty((self.M, self.N), device=dev,
+                             dtype=torch.bfloat16 if bf16 else torch.float32)
+        need = q4.q4_rmsnorm_matmul_workspace_bytes(self.M, self.N, self.K)
+        self.work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_rmsnorm_matmul
+        self.args = [(P(self.x.data_ptr()), P(self.gamma.data_ptr()), ctypes.c_float(d.eps),
+                      P(self.wq[i].data_ptr()), P(self.ws[i].data_ptr()), P(self.y.data_ptr()),
+                      q4.Q4_BF16 if bf16 else q4.Q4_F32, self.M, self.N, self.K,
+                      P(self.work.data_ptr()), need) for i in range(n)]
+        self.wbytes = wb
+        self.flops = 2 * self.M * self.N * self.K
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_rmsnorm_matmul failed with status {st}")
+
+
+class SbDense:
+    """q4_sb_matmul on a dense shape: codes with two-level (super-block)
+    scales, expanded to fp32 block scales in the workspace, then the product."""
+
+    def __init__(self, torch, q4, name, copies=None):
+        import synthetic
+        c = synthetic.SB_CONFIGS[name]
+        self.M, self.N, self.K = c["M"], c["N"], c["K"]
+        d = synthetic.sb_case(c["seed"], self.M, self.N, self.K)
+        dev = "cuda:0"
+        wb = self.N * self.K // 2 + self.N * (self.K // 256) * 2 + self.N * (self.K // 32)
+        n = copies or max(2, -(-ROTATE_BYTES // wb) + 1)
+        self.copies = n
+        self.x = torch.from_numpy(d.x.view(np.int16)).to(dev)
+
+        def put(a, i16=False):
+            t = torch.from_numpy(a.view(np.int16) if i16 else a).to(dev)
+            return [t] + [t.clone() for _ in range(n - 1)]
+        self.wq, self.wd, self.wsc = put(d.w_q), put(d.w_d.view(np.uint16), True), put(d.w_sc)
+        bf16 = c["out"] == "bf16"
+        self.y = torch.empty((self.M, self.N), device=dev,
+                             dtype=torch.bfloat16 if bf16 else torch.float32)
+        need = q4.q4_sb_matmul_workspace_bytes(self.M, self.N, self.K)
+        self.work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_sb_matmul
+        self.args = [(P(self.x.data_ptr()), P(self.wq[i].data_ptr()), P(self.wd[i].data_ptr()),
+                      P(self.wsc[i].data_ptr()), P(self.y.data_ptr()),
+                      q4.Q4_BF16 if bf16 else q4.Q4_F32, self.M, self.N, self.K,
+                      P(self.work.data_ptr()), need) for i in range(n)]
+        self.wbytes = wb
+        self.flops = 2 * self.M * self.N * self.K
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_sb_matmul failed with status {st}")
+
+
+class Quantize:
+    """q4_quantize of the decode projection's weights: bf16 [N][K] in, codes
+    and fp16 block scales out."""
+
+    def __init__(self, torch, q4, N=34816, K=5120, copies=None):
+        dev = "cuda:0"
+        self.N, self.K = N, K
+        g = torch.Generator(device="cpu").manual_seed(12)
+        w = (torch.randn((N, K), generator=g) * 0.02).to(torch.bfloat16)
+        rd = N * K * 2
+        n = copies or max(2, -(-ROTATE_BYTES // rd) + 1)
+        self.copies = n
+        wdev = w.to(dev)
+        self.w = [wdev] + [wdev.clone() for _ in range(n - 1)]
+        self.wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty((N, K // 32), dtype=torch.float16, device=dev)
+        P = ctypes.c_void_p
+        self.fn = q4.lib.q4_quantize
+        self.args = [(P(self.w[i].data_ptr()), P(self.wq.data_ptr()), P(self.ws.data_ptr()),
+                      N, K) for i in range(n)]
+        self.bytes = rd + N * K // 2 + N * (K // 32) * 2   # bf16 read, codes and scales written
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_quantize failed with status {st}")
 
 
 def calibration_copy(torch, mib, reps=3):
@@ -369,6 +546,50 @@ def cpu_baseline(min_seconds=12.0, max_reps=100000):
                                         f"{el1:.1f} s"}}
 
 
+def cpu_baselines_other(runs=3):
+    """The CPU oracle on the other headline shapes, each the median of `runs`
+    timed calls, in the metric the GPU line reports for it: batched_down
+    (whole call) and moe (whole call) as weight GB/s, prefill on a sample of
+    256 weight rows (all 512 activation rows, all of K) as TFLOP/s."""
+    import oracle
+    import synthetic
+
+    def med(f):
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), ts
+    cores = oracle.max_threads()
+    out = {}
+    c = synthetic.CONFIGS["batched_down"]
+    d = synthetic.dense_case(c["seed"], c["M"], c["N"], c["K"])
+    t, ts = med(lambda: oracle.matmul(d.x, d.w_q, d.w_s))
+    out["batched_down"] = {"value": round(weight_bytes(c["N"], c["K"]) / t / 1e9, 4),
+                           "unit": "GB/s", "cores": cores, "kind": "oracle",
+                           "sample": f"whole call M={c['M']} N={c['N']} K={c['K']}, median of "
+                                     f"{runs} ({', '.join(f'{x:.2f}' for x in ts)} s)"}
+    c = synthetic.CONFIGS["prefill"]
+    rows = 256
+    d = synthetic.dense_case(c["seed"], c["M"], rows, c["K"])
+    t, ts = med(lambda: oracle.matmul(d.x, d.w_q, d.w_s))
+    out["prefill"] = {"value": round(2.0 * c["M"] * rows * c["K"] / t / 1e12, 6),
+                      "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                      "sample": f"M={c['M']}, {rows} of the {c['N']} weight rows, K={c['K']}, "
+                                f"median of {runs} ({', '.join(f'{x:.2f}' for x in ts)} s)"}
+    c = synthetic.CONFIGS["moe"]
+    m = synthetic.moe_case(c["seed"], c["T"], c["topk"], c["E"], c["N"], c["K"])
+    t, ts = med(lambda: oracle.moe(m.x, m.w_q, m.w_s, m.ids, m.gates))
+    touched = len(np.unique(m.ids))
+    out["moe"] = {"value": round(touched * weight_bytes(c["N"], c["K"]) / t / 1e9, 4),
+                  "unit": "touched weight GB/s", "cores": cores, "kind": "oracle",
+                  "sample": f"whole call T={c['T']} top-{c['topk']} of {c['E']}, "
+                            f"N={c['N']} K={c['K']}, median of {runs} "
+                            f"({', '.join(f'{x:.2f}' for x in ts)} s)"}
+    return out
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -488,6 +709,8 @@ def main():
     progress(f"decode_gate_up: timing {args.steps} steps over {head.copies} weight copies")
     ms_step, ev_ms = time_steps(torch, head, args.steps, args.warmup, CLOCK_WARM_MS)
     copies = head.copies
+    progress("decode_gate_up: sampling the shader clock under load")
+    sclk = sample_sclk(torch, head)
     value = head.wbytes / (ms_step * 1e-3) / 1e9
     achieved = head.wbytes / (ev_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -495,7 +718,8 @@ def main():
             "traffic": traffic_from_profile("gemv_decode_gate_up", digest),
             # K = 5120 is 160 blocks a row: two full 64-lane stages and a
             # leftover stage of 32 blocks split between the half-waves
-            "kernel": "q4::gemv_lds_kernel<1, 2, 1>", "avg_launch_us": round(ev_ms * 1e3, 3),
+            "kernel": "q4::gemv_lds_kernel<1, 2, 1, false, unsigned short>",
+            "avg_launch_us": round(ev_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": head.wbytes}
     del head
     torch.cuda.empty_cache()
@@ -563,10 +787,60 @@ def main():
                              "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del w
         torch.cuda.empty_cache()
+        import synthetic
+        # the same expert shapes at 512 tokens: the grouped matrix-core path
+        for name, cls in (("moe_prefill", MoE), ("moe_ffn_prefill", MoeFfn)):
+            progress(f"{name}: generating inputs")
+            w = cls(torch, q4, config=synthetic.MOE_PREFILL_CONFIGS[name])
+            progress(f"{name}: timing")
+            _, ev = time_steps(torch, w, max(20, steps // 4), 10, CLOCK_WARM_MS)
+            gbs = w.wbytes / (ev * 1e-3) / 1e9
+            tf = w.flops / (ev * 1e-3) / 1e12
+            rec = {"T": w.T, "topk": w.topk, "E": w.E}
+            rec.update({"N": w.N, "K": w.K} if cls is MoE else {"H": w.H, "F": w.F})
+            rec.update({"touched_experts": w.touched, "avg_call_us": round(ev * 1e3, 2),
+                        "touched_weight_GB/s": round(gbs, 1),
+                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "TFLOP/s": round(tf, 2), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+            others[name] = rec
+            del w
+            torch.cuda.empty_cache()
+        # RMSNorm prologue and super-block scales at the decode and prefill
+        # shapes, and the quantiser on the decode projection's weights
+        for name, cls in (("rms_decode_gate_up", RmsDense), ("rms_prefill", RmsDense),
+                          ("sb_decode_gate_up", SbDense), ("sb_prefill", SbDense)):
+            progress(f"{name}: generating inputs")
+            w = cls(torch, q4, name)
+            progress(f"{name}: timing")
+            _, ev = time_steps(torch, w, steps, max(10, args.warmup // 10), CLOCK_WARM_MS)
+            rec = {"M": w.M, "N": w.N, "K": w.K, "avg_launch_us": round(ev * 1e3, 2)}
+            if w.M == 1:
+                gbs = w.wbytes / (ev * 1e-3) / 1e9
+                rec.update({"weight_GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            else:
+                tf = w.flops / (ev * 1e-3) / 1e12
+                rec.update({"TFLOP/s": round(tf, 2), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+            others[name] = rec
+            del w
+            torch.cuda.empty_cache()
+        progress("quantize: generating inputs")
+        w = Quantize(torch, q4)
+        progress("quantize: timing")
+        _, ev = time_steps(torch, w, max(20, steps // 4), 10, CLOCK_WARM_MS)
+        gbs = w.bytes / (ev * 1e-3) / 1e9
+        others["quantize"] = {"N": w.N, "K": w.K, "avg_launch_us": round(ev * 1e3, 2),
+                              "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                              "bytes": "bf16 weights read, codes and fp16 scales written"}
+        del w
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         progress("cpu baseline: timing the oracle")
     cpu = None if args.no_cpu_baseline else cpu_baseline()
+    if not args.no_cpu_baseline and not args.headline_only:
+        progress("cpu baselines: batched_down, prefill sample, moe")
+    cpu_others = (None if args.no_cpu_baseline or args.headline_only
+                  else cpu_baselines_other())
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -581,8 +855,13 @@ def main():
                    "rotating_weight_copies": copies, "csrc_digest": digest},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_baselines_other": cpu_others,
         "env": {"device": torch.cuda.get_device_properties(0).gcnArchName,
-                "hip_runtime": torch.version.hip, "torch": torch.__version__},
+                "hip_runtime": torch.version.hip, "torch": torch.__version__,
+                "sclk_mhz_under_load": sclk, "commit": git_commit(),
+                "sources_digest": all_sources_digest(),
+                "decode_kernel_resources": kernel_resources(
+                    "_ZN2q415gemv_lds_kernelILi1ELi2ELi1ELb0EtEE")},
         "other_workloads": others,
     }
     print(json.dumps(out), flush=True)

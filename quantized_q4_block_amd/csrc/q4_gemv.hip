@@ -1,17 +1,18 @@
-// q4_gemv.hip -- decode path (M <= 8): fused dequant + matrix-vector product.
+// q4_gemv.hip -- decode path (M <= 2): fused dequant + matrix-vector product.
 //
 // The quantised GEMM of the T0 kernel tier ("spec: specialized model
 // runtimes", sections "Architecture" and "Feasibility gate") at decode
-// shapes, where every weight byte is used by at most 8 activation rows and
-// the op is bound by streaming W from HBM.  The layer-package spec's
+// shapes, where every weight byte is used by one or two activation rows and
+// the op is bound by streaming W from HBM (from 3 rows the few-row
+// matrix-core kernel is faster).  The layer-package spec's
 // expert-matmul fixtures ("Layer Package Repository Spec", MoE paragraph
 // under "Policy Resolution") measure the same lesson on another GPU: the
 // matrix-vector kernel beat the matrix-matrix one about 5x for one token,
 // and taking several rows per thread group mattered more than other knobs.
 //
 // Two kernels (see q4_gemv.h for the per-wavefront work):
-//  * gemv_lds_kernel (M <= 4, rows of at most 4 x 64 blocks, activations
-//    within 64 KB as fp32) -- one task of 2 rows per wavefront, 8
+//  * gemv_lds_kernel (rows of at most 4 x 64 blocks, activations within
+//    64 KB as fp32) -- one task of 2 rows per wavefront, 8
 //    wavefronts per workgroup, compiled per row geometry.  Each wavefront
 //    first issues every code and scale load of its task, then the
 //    workgroup converts the activations to fp32 in LDS (one conversion per
@@ -184,11 +185,10 @@ static hipError_t launch_lds(const uint16_t* x, const uint8_t* wq, const uint16_
 }
 
 // Rows longer than the LDS kernel takes in one piece are cut into slices
-// when the caller gives a workspace for the fp32 partial sums.  For M <= 2:
-// as few slices of 65 .. 128 blocks (two stages, the second partial) as
-// cover the row, when the last one also gets more than 64 blocks.
-// Otherwise (and for M = 3, 4, whose two-stage tables would halve the
-// workgroups per CU) slices of up to 64 blocks (one stage).
+// when the caller gives a workspace for the fp32 partial sums: as few
+// slices of 65 .. 128 blocks (two stages, the second partial) as cover the
+// row, when the last one also gets more than 64 blocks; otherwise slices of
+// up to 64 blocks (one stage).
 struct SplitPlan {
   int64_t slices = 0;
   int slice_blocks = 0;
@@ -197,12 +197,12 @@ struct SplitPlan {
 
 static SplitPlan split_plan(int64_t M, int64_t K) {
   SplitPlan p;
-  if (M < 1 || M > 4) return p;
+  if (M < 1 || M > 2) return p;
   if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) return p;
   const int64_t bpr = K / kBlock;
   const int64_t ns = (bpr + 2 * kWave - 1) / (2 * kWave);
   const int64_t sb = (bpr + ns - 1) / ns;
-  if (M <= 2 && sb > kWave && bpr - (ns - 1) * sb > kWave) {
+  if (sb > kWave && bpr - (ns - 1) * sb > kWave) {
     p.slices = ns;
     p.slice_blocks = (int)sb;
     p.full = 1;
@@ -239,8 +239,9 @@ template <int M, int R>
 static hipError_t launch_m(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                            bool y_bf16, int64_t N, int64_t K, float* partial,
                            hipStream_t stream) {
+  static_assert(M >= 1 && M <= 2, "the matrix-vector path takes one or two rows");
   const int yb = y_bf16 ? 1 : 0;
-  if constexpr (M <= 4) {
+  {
     const int64_t bpr = K / kBlock;
     if (x_stages(K) <= kLdsMaxStages && xlds_bytes(M, K) <= kLdsLimit) {
       const int rem = row_leftover(K);
@@ -337,15 +338,10 @@ hipError_t launch_gemv_f32s(const uint16_t* x, const uint8_t* wq, const float* w
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                        bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                        hipStream_t stream) {
+  // one or two rows; more take the few-row matrix-core kernel
   switch (M) {
     case 1: return launch_m<1, GemvRows<1>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
     case 2: return launch_m<2, GemvRows<2>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
-    case 3: return launch_m<3, GemvRows<3>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
-    case 4: return launch_m<4, GemvRows<4>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
-    case 5: return launch_m<5, GemvRows<5>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
-    case 6: return launch_m<6, GemvRows<6>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
-    case 7: return launch_m<7, GemvRows<7>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
-    case 8: return launch_m<8, GemvRows<8>::R>(x, wq, ws, y, y_bf16, N, K, partial, stream);
     default: return hipErrorInvalidValue;
   }
 }

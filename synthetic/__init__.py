@@ -54,6 +54,7 @@ __all__ = [
     "BLOCK", "DenseCase", "MoECase", "CONFIGS", "dense_case", "moe_case",
     "f32_to_bf16_bits", "config_case", "MXCase", "mx_case", "MX_CONFIGS",
     "RMSCase", "rms_case", "RMS_CONFIGS", "RMS_EPS", "SBCase", "sb_case", "SB_CONFIGS",
+    "MOE_PREFILL_CONFIGS",
 ]
 
 
@@ -175,6 +176,14 @@ CONFIGS = {
 # expert width F = 1536 (gate/up [2F][H], down [H][F]).
 FFN_CONFIGS = {
     "moe_ffn":        dict(kind="moe_ffn", T=8, topk=8, E=128, H=4096, F=1536, seed=5, out="f32"),
+}
+
+# The same expert shapes at prefill: 512 tokens, about 32 (token, slot)
+# pairs per expert.
+MOE_PREFILL_CONFIGS = {
+    "moe_prefill":     dict(kind="moe", T=512, topk=8, E=128, K=4096, N=1536, seed=4, out="f32"),
+    "moe_ffn_prefill": dict(kind="moe_ffn", T=512, topk=8, E=128, H=4096, F=1536, seed=5,
+                            out="f32"),
 }
 
 

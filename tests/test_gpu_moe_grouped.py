@@ -104,7 +104,7 @@ def _covering_tokens(ids: np.ndarray, E: int) -> np.ndarray:
     return np.array(out, dtype=np.int64)
 
 
-PREFILL_MOE = dict(T=512, topk=8, E=128, N=1536, K=4096, seed=4)
+PREFILL_MOE = synthetic.MOE_PREFILL_CONFIGS["moe_prefill"]
 
 
 def test_grouped_prefill_workload_sampled():
@@ -141,8 +141,8 @@ def test_grouped_ffn_parity_shapes(T, topk, E, H, F):
 
 
 def test_grouped_ffn_prefill_workload_sampled():
-    cfg = synthetic.FFN_CONFIGS["moe_ffn"]
-    T, topk, E, H, F = 512, cfg["topk"], cfg["E"], cfg["H"], cfg["F"]
+    cfg = synthetic.MOE_PREFILL_CONFIGS["moe_ffn_prefill"]
+    T, topk, E, H, F = cfg["T"], cfg["topk"], cfg["E"], cfg["H"], cfg["F"]
     assert grouped(T, topk, E)
     c = synthetic.moe_ffn_case(cfg["seed"], T, topk, E, H, F)
     y = moe_ffn(c)
