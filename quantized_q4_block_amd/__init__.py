@@ -92,6 +92,13 @@ def _open():
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
             "or `python quantized_q4_block_amd/_build.py`")
+    # torch (when installed) first: it carries its own HIP runtime, and the
+    # library must bind to that same runtime rather than load a second one
+    # that does not see torch's devices and streams
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.q4_abi_version.argtypes = []

@@ -411,11 +411,24 @@ struct UpfrontLoads {
   SC st[TR > 0 ? TR : 1];
 };
 
+// Weights and scales are read once per call: the loads are non-temporal, so
+// they do not displace reusable lines from the caches (a loads-only stream
+// of 100 MB from a cold 1.3 GB rotation measured 76% of HBM peak this way
+// against 69-71% with ordinary loads).
 __device__ __forceinline__ void load_scale(const uint16_t* p, _Float16& s) {
-  s = __builtin_bit_cast(_Float16, *p);
+  s = __builtin_bit_cast(_Float16, __builtin_nontemporal_load(p));
 }
-__device__ __forceinline__ void load_scale(const uint8_t* p, uint8_t& s) { s = *p; }
-__device__ __forceinline__ void load_scale(const float* p, float& s) { s = *p; }
+__device__ __forceinline__ void load_scale(const uint8_t* p, uint8_t& s) {
+  s = __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void load_scale(const float* p, float& s) {
+  s = __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ uint4 load_codes(const uint8_t* p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // cbase / sbase: codes and scales of the task's first row at the first
 // block of the row piece; row_bytes / row_sc: distance between rows (bytes,
@@ -429,7 +442,7 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL, SC>& b,
                                              int rem, int lane) {
   auto load = [&](int row, uint32_t blk, uint4& c, SC& s) {
     row = row < room ? row : room;
-    c = *reinterpret_cast<const uint4*>(cbase + (uint32_t)row * row_bytes + blk * 16);
+    c = load_codes(cbase + (uint32_t)row * row_bytes + blk * 16);
     load_scale(sbase + (uint32_t)row * row_sc + blk, s);
   };
 #pragma unroll
@@ -610,8 +623,8 @@ __device__ __forceinline__ void gemv_task(const uint16_t* const (&xrow)[M],
     for (int r = 0; r < R; ++r) {
       const int64_t row = last ? tail_row<R>(sp, r) : r;
       const int64_t n = n0 + row < n_last ? n0 + row : n_last;
-      b.c[r] = *reinterpret_cast<const uint4*>(wq + n * row_bytes + blk * 16);
-      b.s[r] = __builtin_bit_cast(_Float16, ws[n * sp.bpr + blk]);
+      b.c[r] = load_codes(wq + n * row_bytes + blk * 16);
+      load_scale(ws + n * sp.bpr + blk, b.s[r]);
     }
   };
   auto compute = [&](int64_t st, const Buf& b) {
