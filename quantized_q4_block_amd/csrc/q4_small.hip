@@ -100,12 +100,7 @@ __device__ __forceinline__ void transpose_groups(uint32_t r[4]) {
 // scales.
 // F32S: int4 codes with exact fp32 block scales [N][K/32] (e.g. expanded from
 // super-block scales) instead of fp16 ones.
-// BUF: buffer-resource loads.  Every operand is addressed from a base of the
-// workgroup by a 32-bit offset made of a per-lane part fixed for the whole
-// call and a wave-uniform scalar part per group, so the loads take no vector
-// ALU work; rows of K < 2^26 (offsets below 2^31).  Otherwise 64-bit
-// per-lane pointers.
-template <int MG, bool SCALE4, bool MX, bool F32S, bool BUF>
+template <int MG, bool SCALE4, bool MX, bool F32S>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 4 : 2))) void small_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const void* __restrict__ wsv, void* __restrict__ y, int y_bf16, int64_t M, int64_t N,
@@ -135,24 +130,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
   const uint8_t* wq_g = wq + n0 * (K / 2);
   const ScaleT* ws_g = ws + n0 * bpr;
   const uint16_t* x_g = x + m0 * K;
-  __amdgpu_buffer_rsrc_t w_rsrc, s_rsrc, x_rsrc;
-  uint32_t w_off[kNg], s_off[kNg], x_off[MG];
-  if constexpr (BUF) {
-    w_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wq_g), (short)0,
-                                               (int)(rows_w * (K / 2)), 0x00020000);
-    s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<ScaleT*>(ws_g), (short)0,
-                                               (int)(rows_w * bpr * (int64_t)sizeof(ScaleT)),
-                                               0x00020000);
-    x_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x_g), (short)0,
-                                               (int)(rows_x * K * 2), 0x00020000);
-#pragma unroll
-    for (int ng = 0; ng < kNg; ++ng) {
-      w_off[ng] = (uint32_t)(wl[ng] * (K / 2));
-      s_off[ng] = (uint32_t)(wl[ng] * bpr * (int64_t)sizeof(ScaleT));
-    }
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) x_off[mg] = (uint32_t)(xl[mg] * K * 2 + 16 * g);
-  }
   // K slice blockIdx.z: 4-block groups [q_beg, q_end) of the row
   const int64_t q_beg = (int64_t)blockIdx.z * groups_per_slice;
   const int64_t q_end = q_beg + groups_per_slice;
@@ -179,56 +156,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
     const int64_t bl = SCALE4 ? b0 + g : (b0 + g < bpr ? b0 + g : bpr - 1);
 #pragma unroll
     for (int ng = 0; ng < kNg; ++ng) {
-      u32x4 v;
-      if constexpr (BUF) {
-        if constexpr (SCALE4)
-          v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ng] + 16 * g, (int)(b0 * 16), 0);
-        else
-          v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ng] + (uint32_t)(bl * 16), 0, 0);
-      } else {
-        v = *reinterpret_cast<const u32x4*>(wq_g + (int64_t)wl[ng] * (K / 2) + bl * 16);
-      }
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wq_g + (int64_t)wl[ng] * (K / 2) + bl * 16);
       codes[d][ng][0] = v[0];
       codes[d][ng][1] = v[1];
       codes[d][ng][2] = v[2];
       codes[d][ng][3] = v[3];
       if constexpr (SCALE4) {
         // the row's 4 scales of the group, as stored
-        if constexpr (BUF) {
-          const int so = (int)(b0 * (int64_t)sizeof(ScaleT));
-          if constexpr (SW == 4) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, s_off[ng], so, 0);
+        const ScaleT* sp = ws_g + (int64_t)wl[ng] * bpr + b0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sraw[d][ng][j] = t[j];
-          } else if constexpr (SW == 2) {
-            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, s_off[ng], so, 0);
-            sraw[d][ng][0] = t[0];
-            sraw[d][ng][1] = t[1];
-          } else {
-            sraw[d][ng][0] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_off[ng], so, 0);
-          }
-        } else {
-          const ScaleT* sp = ws_g + (int64_t)wl[ng] * bpr + b0;
-#pragma unroll
-          for (int j = 0; j < SW; ++j) sraw[d][ng][j] = reinterpret_cast<const uint32_t*>(sp)[j];
-        }
+        for (int j = 0; j < SW; ++j) sraw[d][ng][j] = reinterpret_cast<const uint32_t*>(sp)[j];
       } else {
         // one scale at a time, clamped to the row
         ScaleT sv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t bj = b0 + j < bpr ? b0 + j : bpr - 1;
-          if constexpr (BUF) {
-            const int so = (int)(bj * (int64_t)sizeof(ScaleT));
-            if constexpr (SW == 4)
-              sv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_off[ng], so, 0));
-            else if constexpr (SW == 2)
-              sv[j] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, s_off[ng], so, 0);
-            else
-              sv[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_off[ng], so, 0);
-          } else {
-            sv[j] = ws_g[(int64_t)wl[ng] * bpr + bj];
-          }
+          sv[j] = ws_g[(int64_t)wl[ng] * bpr + bj];
         }
         if constexpr (SW == 4) {
 #pragma unroll
@@ -246,13 +190,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
     for (int j = 0; j < 4; ++j) {
       const int64_t bj = b0 + j < bpr ? b0 + j : bpr - 1;   // wave-uniform
 #pragma unroll
-      for (int mg = 0; mg < MG; ++mg) {
-        if constexpr (BUF)
-          xf[d][j][mg] = __builtin_bit_cast(
-              bf16x8v, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, x_off[mg], (int)(bj * 64), 0));
-        else
-          xf[d][j][mg] = *reinterpret_cast<const bf16x8v*>(x_g + (int64_t)xl[mg] * K + 8 * g + bj * 32);
-      }
+      for (int mg = 0; mg < MG; ++mg)
+        xf[d][j][mg] = *reinterpret_cast<const bf16x8v*>(x_g + (int64_t)xl[mg] * K + 8 * g + bj * 32);
     }
   };
   // block j's scale of 16-row weight group ng, from slot d
@@ -370,18 +309,12 @@ hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const void* ws, void*
   if (gx > 0x7FFFFFFF || gy > 65535 || slices > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)slices);
   float* part = slices > 1 ? partial : nullptr;
-  const bool buf = K < (int64_t(1) << 26);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, dim3(kWaves * 64), 0, stream>>>(x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw,
-                                                   per, part);
-  };
-  if ((K / 32) % 4 == 0) {
-    if (buf) go(small_kernel<MG, true, MX, F32S, true>);
-    else go(small_kernel<MG, true, MX, F32S, false>);
-  } else {
-    if (buf) go(small_kernel<MG, false, MX, F32S, true>);
-    else go(small_kernel<MG, false, MX, F32S, false>);
-  }
+  if ((K / 32) % 4 == 0)
+    small_kernel<MG, true, MX, F32S><<<grid, dim3(kWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw, per, part);
+  else
+    small_kernel<MG, false, MX, F32S><<<grid, dim3(kWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, gpw, per, part);
   if (slices == 1) return hipGetLastError();
   const hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) return e;
