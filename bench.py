@@ -63,10 +63,21 @@ def all_sources_digest():
     return csrc_digest(tuple(n for n in os.listdir(d) if n.endswith((".hip", ".h"))))
 
 
+def under_profiler():
+    """True inside a rocprofv3 run.  Its preloaded library reaches every
+    child process too and, with counters, opens the GPU there before the
+    child starts: children that are launchers (`env` in a script's #! line)
+    would then replace a process that holds the GPU, so helpers that start
+    other programs stay off."""
+    return any(k.startswith("ROCPROF_") for k in os.environ)
+
+
 def git_commit():
     """HEAD of the repository this script sits in, or None where the tree
-    carries no git metadata."""
+    carries no git metadata (or under the profiler)."""
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
                            text=True, timeout=10)
@@ -91,10 +102,13 @@ def kernel_resources(mangled_prefix):
 
 def sample_sclk(torch, work, seconds=1.5):
     """The shader clock (MHz) rocm-smi reports while `work` keeps the GPU
-    busy, or None if the tool is not there or prints no clock."""
+    busy, or None if the tool is not there, prints no clock, or the run is
+    under the profiler."""
     import re
     import subprocess
     import threading
+    if under_profiler():
+        return None
     box = {}
 
     def query():
@@ -440,7 +454,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_mib, kernel_tag, kernel_match, algo
     write = _counter_means(write_dir, "WRITE_SIZE")
 
     def pick(table, sub):
-        hits = [(k, v) for k, v in table.items() if sub in k]
+        hits = [(k, v) for k, v in table.items() if sub in k or sub in "q4::" + k]
         if len(hits) != 1:
             raise SystemExit(f"expected one kernel matching {sub!r}, found {[k for k, _ in hits]}")
         return hits[0]
@@ -464,6 +478,11 @@ def summarize_pmc(fetch_dir, write_dir, copy_mib, kernel_tag, kernel_match, algo
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
+
+
+# The decode workload's kernel: the roofline object's kernel and the one the
+# counter summary picks out of a --pmc run.
+DECODE_KERNEL = "q4::gemv_lds_kernel<1, 2, 1, false, unsigned short>"
 
 
 # After a few seconds without GPU work (input generation on the host) the
@@ -628,29 +647,79 @@ def summarize_trace(run_dir):
     return out
 
 
-def summarize_counters(run_dir):
+def summarize_counters(run_dirs):
     """Per-kernel dispatch count and mean value per dispatch of every counter
-    in the counter_collection.csv files a rocprofv3 --pmc run wrote under
-    run_dir (kernel names shortened as in summarize_trace)."""
+    in the counter_collection.csv files that rocprofv3 --pmc runs wrote under
+    run_dirs (one pass each; kernel names shortened as in summarize_trace)."""
     import csv
-    vals = {}
-    for dirpath, _, files in os.walk(run_dir):
-        for fn in files:
-            if not fn.endswith("counter_collection.csv"):
-                continue
-            with open(os.path.join(dirpath, fn), newline="") as f:
-                for row in csv.DictReader(f):
-                    name = row["Kernel_Name"].replace("void ", "")
-                    name = name.replace("(anonymous namespace)::", "").split("(")[0]
-                    per = vals.setdefault(name, {})
-                    per.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
     out = {}
-    for name, per in vals.items():
-        rec = {"dispatches": max(len(v) for v in per.values())}
-        for c, v in sorted(per.items()):
-            rec[c] = round(float(np.mean(v)), 1)
-        out[name] = rec
+    for run_dir in run_dirs:
+        vals = {}
+        for dirpath, _, files in os.walk(run_dir):
+            for fn in files:
+                if not fn.endswith("counter_collection.csv"):
+                    continue
+                with open(os.path.join(dirpath, fn), newline="") as f:
+                    for row in csv.DictReader(f):
+                        name = row["Kernel_Name"].replace("void ", "")
+                        name = name.replace("(anonymous namespace)::", "").split("(")[0]
+                        per = vals.setdefault(name, {})
+                        per.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+        for name, per in vals.items():
+            rec = out.setdefault(name, {})
+            rec.setdefault("dispatches", {})
+            for c, v in sorted(per.items()):
+                rec["dispatches"][c] = len(v)
+                rec[c] = round(float(np.mean(v)), 1)
     return out
+
+
+# MI355X: 256 compute units of 4 SIMDs in 8 XCDs; GRBM_GUI_ACTIVE counts in
+# every XCD.
+SIMDS, XCDS = 1024, 8
+
+
+def counters_table(table, copy_mib=256):
+    """Text table of the derived per-dispatch figures: waves, VALU and LDS
+    instructions per wave, MFMA instructions, MFMA busy fraction, LDS bank
+    conflict cycles, and HBM MB read and written (FETCH_SIZE / WRITE_SIZE
+    scaled by what they read for the calibration copy of copy_mib MiB, if the
+    runs hold it)."""
+    neg = [v for k, v in table.items() if "neg_kernel" in k]
+    f_read = f_write = None
+    if neg and "FETCH_SIZE" in neg[0] and "WRITE_SIZE" in neg[0]:
+        f_read = copy_mib * (1 << 20) / (neg[0]["FETCH_SIZE"] * 1024.0)
+        f_write = copy_mib * (1 << 20) / (neg[0]["WRITE_SIZE"] * 1024.0)
+    lines = []
+    if f_read:
+        lines.append(f"HBM bytes = FETCH_SIZE KiB x 1024 x {f_read:.4f} + WRITE_SIZE KiB x 1024 x "
+                     f"{f_write:.4f} (factors from the {copy_mib} MiB copy calibration)")
+    lines.append(f"{'kernel':46s} {'waves':>7s} {'VALU/wave':>9s} {'MFMA':>9s} {'MFMA busy':>9s} "
+                 f"{'LDS/wave':>8s} {'bank cf':>8s} {'read MB':>8s} {'write MB':>8s}")
+    for name, r in sorted(table.items(), key=lambda kv: kv[0]):
+        if not name.startswith("q4::"):
+            continue
+        waves = r.get("SQ_WAVES", 0.0)
+        per = (lambda c: r[c] / waves if waves and c in r else float("nan"))
+        busy = float("nan")
+        if r.get("GRBM_GUI_ACTIVE"):
+            busy = r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS * r["GRBM_GUI_ACTIVE"] / XCDS)
+        rd = r["FETCH_SIZE"] * 1024 * f_read / 1e6 if f_read and "FETCH_SIZE" in r else float("nan")
+        wr = r["WRITE_SIZE"] * 1024 * f_write / 1e6 if f_write and "WRITE_SIZE" in r else float("nan")
+        lines.append(f"{name[:46]:46s} {waves:7.0f} {per('SQ_INSTS_VALU'):9.0f} "
+                     f"{r.get('SQ_INSTS_MFMA', float('nan')):9.0f} {100 * busy:8.1f}% "
+                     f"{per('SQ_INSTS_LDS'):8.1f} {r.get('SQ_LDS_BANK_CONFLICT', float('nan')):8.0f} "
+                     f"{rd:8.1f} {wr:8.2f}")
+    return "\n".join(lines)
+
+
+def trace_table(table):
+    lines = [f"{'Kernel (us)':52s} {'calls':>6s} {'mean':>8s} {'p10':>8s} {'median':>8s} "
+             f"{'p90':>8s} {'min':>8s} {'max':>8s}"]
+    for k, v in table.items():
+        lines.append(f"{k[:52]:52s} {v['calls']:6d} {v['mean_us']:8.2f} {v['p10_us']:8.2f} "
+                     f"{v['median_us']:8.2f} {v['p90_us']:8.2f} {v['min_us']:8.2f} {v['max_us']:8.2f}")
+    return "\n".join(lines)
 
 
 def main():
@@ -667,23 +736,28 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print per-kernel duration statistics (mean, p10, median, p90) of a "
                          "rocprofv3 --kernel-trace run of this script (no GPU needed)")
-    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
-                    help="print each kernel's mean counter values per dispatch from a "
-                         "rocprofv3 --pmc run of this script (no GPU needed)")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR", nargs="+",
+                    help="print each kernel's mean counter values per dispatch from "
+                         "rocprofv3 --pmc runs of this script, one pass each (no GPU needed)")
+    ap.add_argument("--text", action="store_true",
+                    help="with --summarize-trace or --summarize-counters: a text table "
+                         "(derived figures for the counters) in place of JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script with --calibrate-copy-mib 256 into the decode kernel's "
                          "HBM traffic record under profiles/ (no GPU needed)")
     args = ap.parse_args()
     if args.summarize_trace:
-        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        t = summarize_trace(args.summarize_trace)
+        print(trace_table(t) if args.text else json.dumps(t, indent=1))
         return
     if args.summarize_counters:
-        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        t = summarize_counters(args.summarize_counters)
+        print(counters_table(t) if args.text else json.dumps(t, indent=1))
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], 256,
-                      "gemv_decode_gate_up", "gemv_lds_kernel", weight_bytes(34816, 5120),
+                      "gemv_decode_gate_up", DECODE_KERNEL + "(", weight_bytes(34816, 5120),
                       os.path.join(ROOT, "profiles", "gemv_decode_gate_up_pmc.json"))
         return
     if args.gpus != 1:
@@ -718,7 +792,7 @@ def main():
             "traffic": traffic_from_profile("gemv_decode_gate_up", digest),
             # K = 5120 is 160 blocks a row: two full 64-lane stages and a
             # leftover stage of 32 blocks split between the half-waves
-            "kernel": "q4::gemv_lds_kernel<1, 2, 1, false, unsigned short>",
+            "kernel": DECODE_KERNEL,
             "avg_launch_us": round(ev_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": head.wbytes}
     del head

@@ -114,6 +114,37 @@ def test_summarize_counters_means(tmp_path):
                         "Counter_Value": 2 * v})
         w.writerow({"Kernel_Name": "void q4::(anonymous namespace)::b<2>(float*)",
                     "Counter_Name": "SQ_WAVES", "Counter_Value": 7})
-    s = b.summarize_counters(str(tmp_path / "pmc"))
-    assert s["q4::a<1>"] == {"dispatches": 2, "FETCH_SIZE": 40.0, "SQ_WAVES": 20.0}
-    assert s["q4::b<2>"] == {"dispatches": 1, "SQ_WAVES": 7.0}
+    s = b.summarize_counters([str(tmp_path / "pmc")])
+    assert s["q4::a<1>"] == {"dispatches": {"FETCH_SIZE": 2, "SQ_WAVES": 2},
+                             "FETCH_SIZE": 40.0, "SQ_WAVES": 20.0}
+    assert s["q4::b<2>"] == {"dispatches": {"SQ_WAVES": 1}, "SQ_WAVES": 7.0}
+
+
+def test_counters_table_derived_figures(tmp_path):
+    """The text table: per-wave VALU, MFMA busy fraction and calibrated MB,
+    from passes in separate run folders."""
+    b = _bench()
+    runs = []
+    rows = {"sq": [("SQ_WAVES", 64.0), ("SQ_INSTS_VALU", 6400.0), ("SQ_INSTS_MFMA", 3.0),
+                   ("SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 50), ("GRBM_GUI_ACTIVE", 8.0 * 100)],
+            "fetch": [("FETCH_SIZE", 1000.0)], "write": [("WRITE_SIZE", 500.0)]}
+    neg = {"fetch": ("FETCH_SIZE", 256 * 1024 / 2), "write": ("WRITE_SIZE", 256 * 1024)}
+    for run, cs in rows.items():
+        d = tmp_path / run / "host"
+        d.mkdir(parents=True)
+        with open(d / "1_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for c, v in cs:
+                w.writerow({"Kernel_Name": "void q4::k(int)", "Counter_Name": c,
+                            "Counter_Value": v})
+            if run in neg:
+                w.writerow({"Kernel_Name": "void at::native::neg_kernel_x(int)",
+                            "Counter_Name": neg[run][0], "Counter_Value": neg[run][1]})
+        runs.append(str(tmp_path / run))
+    text = b.counters_table(b.summarize_counters(runs))
+    line = [l for l in text.splitlines() if l.startswith("q4::k")][0].split()
+    # waves, VALU/wave, MFMA, busy %, LDS/wave (absent), bank cf (absent), MB read, MB written
+    assert line[1:5] == ["64", "100", "3", "50.0%"]
+    assert float(line[-2]) == round(1000 * 1024 * 2 / 1e6, 1)
+    assert float(line[-1]) == round(500 * 1024 / 1e6, 2)
