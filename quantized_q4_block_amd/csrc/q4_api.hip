@@ -128,7 +128,7 @@ static bool slabs_to_tiled(int64_t M, int64_t N, int64_t K) {
   // N * K >= 2^24 without forming the product (sizes are not checked here)
   return M > kSmallMaxRows && K % 64 == 0 && N > 0 &&
          K >= (kSlabsToTiledMinWeights + N - 1) / N &&
-         q4_matmul_path(M, N, K) == Q4_PATH_SMALL && q4::gemm_split_slices(M, N, K) > 1;
+         q4_matmul_path(M, N, K) == Q4_PATH_SMALL && q4::gemm_q4_split_slices(M, N, K) > 1;
 }
 
 Q4_API int32_t q4_matmul_path_ex(int64_t M, int64_t N, int64_t K, int32_t with_workspace) {
@@ -147,8 +147,8 @@ Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     slices = q4::small_split_slices(M, N, K);
     if (slices == 1) slices = 0;
   } else {
-    slices = q4::gemm_split_slices(M, N, K);
-    if (slices == 1) slices = 0;
+    slices = q4::gemm_q4_split_slices(M, N, K);
+    if (slices == 1) return q4::gemm_q4_tail_bytes(M, N, K);
   }
   int64_t mn, total;
   if (slices == 0 || !mul_ok(M, N, &mn) || !mul_ok(mn, slices * 4, &total)) return 0;

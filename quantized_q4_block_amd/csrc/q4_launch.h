@@ -70,21 +70,28 @@ hipError_t launch_small_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* 
 
 // 4-bit float block weights, many rows, K a multiple of 64: e2m1 * 2^(E-129)
 // exact in bf16 in LDS + bf16 MFMA tiles, accumulators times 4; exact weights.
-// partial: as for launch_gemm (K slices of gemm_split_slices(M, N, K)).
+// partial: NULL, or fp32 scratch of gemm_split_slices(M, N, K) * M * N floats.
 hipError_t launch_gemm_mx(const uint16_t* x, const uint8_t* wq, const uint8_t* we, void* y,
                           bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                           hipStream_t stream);
 
 // Many rows: exact (c - 8) tiles in LDS + bf16 MFMA, fp32 block scales (exact
 // weights); any K that is a multiple of 32.
-// partial: NULL, or fp32 scratch of gemm_split_slices(M, N, K) * M * N floats
+// partial: NULL, or fp32 scratch of gemm_q4_split_slices(M, N, K) * M * N floats
 // that lets a grid of few tiles be cut along K (K a multiple of 64).
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                        bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                        hipStream_t stream);
 
-// K slices of the tiled kernel when scratch is given (1: never cut).
+// K slices of the tiled kernels when scratch is given (1: never cut): the
+// 128-row tiles (the 4-bit float product, and int4 codes up to 128 rows or K
+// not a multiple of 64) and the int4 product as launch_gemm runs it.
 int64_t gemm_split_slices(int64_t M, int64_t N, int64_t K);
+int64_t gemm_q4_split_slices(int64_t M, int64_t N, int64_t K);
+// Workspace bytes of the int4 tiled product's tail plan (the last, partly
+// filled round of wide tiles cut along K; 0: none).  launch_gemm takes the
+// larger of this and the K slices' scratch.
+size_t gemm_q4_tail_bytes(int64_t M, int64_t N, int64_t K);
 
 // Expert-routed rows; workspace laid out by moe_workspace_layout.
 struct MoeLayout {

@@ -167,12 +167,23 @@ def test_matmul_workspace_bytes():
     # rows that fit one workgroup's LDS, the matrix-core paths and bad
     # shapes need none
     assert q4.q4_matmul_workspace_bytes(1, 34816, 5120) == 0
-    assert q4.q4_matmul_workspace_bytes(512, 34816, 5120) == 0
-    # tiled path: grids of 512 tiles or more are never cut along K; fewer
-    # tiles take up to 768 / tiles slices of at least 8 K steps, none empty
-    assert q4.q4_matmul_workspace_bytes(512, 5120, 17408) == 4 * 512 * 5120 * 4
-    assert q4.q4_matmul_workspace_bytes(1024, 5120, 17408) == 2 * 1024 * 5120 * 4
-    assert q4.q4_matmul_workspace_bytes(2048, 5120, 17408) == 0
+    # wide tiles (256 x 128, 256 a round): 544 tiles leave 32 for a third
+    # round, cut into 8 K slices of 10 steps (256 x 128 fp32 blocks); whole
+    # rounds, or a last round more than half full, take no workspace
+    assert q4.q4_matmul_workspace_bytes(512, 34816, 5120) == 32 * 8 * 256 * 128 * 4
+    assert q4.q4_matmul_workspace_bytes(512, 36864, 5120) == 64 * 4 * 256 * 128 * 4
+    assert q4.q4_matmul_workspace_bytes(512, 32768, 5120) == 0
+    assert q4.q4_matmul_workspace_bytes(512, 28672, 4096) == 0      # 448 tiles
+    assert q4.q4_matmul_workspace_bytes(512, 34816, 5120 + 32) == 0  # K % 64 != 0
+    # tiled path, more than 128 rows and K a multiple of 64 (tiles of 256
+    # rows, one workgroup per CU): grids of 171 tiles or more are never cut
+    # along K; fewer tiles take up to 256 / tiles slices of at least 8 K
+    # steps, none empty
+    assert q4.q4_matmul_workspace_bytes(512, 5120, 17408) == 3 * 512 * 5120 * 4   # 80 tiles
+    assert q4.q4_matmul_workspace_bytes(1024, 5120, 17408) == 0                   # 160 tiles
+    assert q4.q4_matmul_workspace_bytes(2048, 5120, 17408) == 64 * 4 * 256 * 128 * 4  # 320: tail
+    # up to 128 rows (tiles of 128): 512 tiles or more are never cut; fewer
+    # take up to 768 / tiles slices
     assert q4.q4_matmul_workspace_bytes(64, 5120, 17408) == 19 * 64 * 5120 * 4    # 40 tiles
     # slabs of 32 rows (64 workgroups of 32 weight rows): 4 K slices of 8 groups
     assert q4.q4_matmul_workspace_bytes(64, 1024, 4096) == 4 * 64 * 1024 * 4

@@ -239,6 +239,35 @@ def test_mfma_parity(M, N, K):
     _check_dense(d, F32, what=f"mfma M={M} N={N} K={K}")
 
 
+# More than 128 rows with K a multiple of 64 take tiles of 256 x 128: one
+# tile partly filled, a tile edge at 256 rows and one past it, ragged weight
+# tiles, one K step and an odd number of them.
+@pytest.mark.parametrize("M,N,K", [(129, 128, 64), (256, 129, 128), (257, 300, 64 * 5),
+                                   (511, 1000, 1024), (513, 64, 64 * 3), (700, 257, 2048)])
+def test_mfma_wide_tile_parity(M, N, K):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    d = synthetic.dense_case(3500 + M + N, M, N, K)
+    _check_dense(d, F32, what=f"mfma wide M={M} N={N} K={K}")
+    _check_dense(d, BF16, what=f"mfma wide bf16 M={M} N={N} K={K}")
+
+
+# With a workspace, a grid of wide tiles that fills whole rounds of the chip
+# (256 tiles) and a last round at most half full cuts the last round's tiles
+# along K: 258 tiles (2 of them in the tail, 4 slices of 4 steps), 300 tiles
+# (44 in the tail, 5 slices of 4 steps, a ragged last M tile and N tile).
+@pytest.mark.parametrize("M,N,K,tail,slices", [(257, 128 * 128 + 1, 1024, 2, 4),
+                                               (300, 150 * 128 - 5, 64 * 20, 44, 5)])
+def test_mfma_wide_tail_parity(M, N, K, tail, slices):
+    assert q4.q4_matmul_path(M, N, K) == q4.Q4_PATH_MFMA
+    assert q4.q4_matmul_workspace_bytes(M, N, K) == tail * slices * 256 * 128 * 4
+    d = synthetic.dense_case(3600 + M, M, N, K)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"wide tail M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"wide tail bf16 M={M}")
+
+
 @pytest.mark.parametrize("M,N,K", [(160, 200, 512), (512, 256, 5120)])
 def test_mfma_bf16_output(M, N, K):
     d = synthetic.dense_case(4000 + M, M, N, K)
@@ -282,14 +311,14 @@ def test_slab_shapes_with_a_workspace(M, N, K):
 
 
 def test_prefill_down_split_sampled_and_deterministic():
-    """The prefill FFN's down projection (512 x 5120 x 17408: 160 tiles) with
+    """The prefill FFN's down projection (512 x 5120 x 17408: 80 tiles of 256 x 128) with
     a workspace, against sampled outputs of the oracle; junk workspace
     contents do not matter and two calls agree bit for bit."""
     M, N, K = 512, 5120, 17408
     d = synthetic.dense_case(4200, M, N, K)
     x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
     need = q4.q4_matmul_workspace_bytes(M, N, K)
-    assert need == 4 * M * N * 4
+    assert need == 3 * M * N * 4
     work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)
     y1 = q4.q4_matmul_ex(x, wq, ws, out_dtype=BF16, workspace=work)
     y2 = q4.q4_matmul_ex(x, wq, ws, out_dtype=BF16, workspace=work)
@@ -468,6 +497,22 @@ def test_prefill_full_size_stratified():
     y_ref, t = oracle.matmul_sampled(d.x, d.w_q, d.w_s, ms, ns)
     assert_parity(y[ms, ns], y_ref, t, RTOL, bf16_half_ulp(y_ref), what="prefill")
     assert np.isfinite(y).all()
+    # as the benchmark calls it: q4_matmul_ex with its workspace, where the
+    # 32 tiles of the last round (columns 32768 and up) are cut into 8 K
+    # slices each; a junk workspace does not matter and two calls agree
+    x, wq, ws = dev(d.x), dev(d.w_q), dev(d.w_s)
+    need = q4.q4_matmul_workspace_bytes(M, N, d.x.shape[1])
+    assert need == 32 * 8 * 256 * 128 * 4
+    work = torch.full((need,), 0x7F, dtype=torch.uint8, device=x.device)
+    y1 = q4.q4_matmul_ex(x, wq, ws, out_dtype=BF16, workspace=work)
+    y2 = q4.q4_matmul_ex(x, wq, ws, out_dtype=BF16, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ye = host(y1)
+    assert_parity(ye[ms, ns], y_ref, t, RTOL, bf16_half_ulp(y_ref), what="prefill with workspace")
+    assert np.isfinite(ye).all()
+    # the whole tiles are the same computation either way
+    assert np.array_equal(ye[:, :32768].view(np.uint16), y[:, :32768].view(np.uint16))
 
 
 # ------------------------------------------------------------------ MoE
