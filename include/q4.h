@@ -141,13 +141,20 @@ Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
                          void *y, int32_t y_dtype,
                          int64_t M, int64_t N, int64_t K, q4_stream_t stream);
 
-/* Device workspace (bytes) that lets q4_matmul_ex cut long rows into
- * slices: slices * M * N fp32 partial sums.  Q4_PATH_GEMV shapes are cut when
- * K is above 8192 or the activations are too large for one workgroup's LDS;
- * tiled shapes (q4_matmul_path_ex(M, N, K, 1) == Q4_PATH_MFMA) with K a
- * multiple of 64 when their grid has fewer than 512 tiles of 128 x 128
- * outputs (at most 768 / tiles and 64 slices, each of at least 8 steps of
- * 64 k).  0 when the call needs none, or for sizes q4_matmul would reject. */
+/* Device workspace (bytes) that lets q4_matmul_ex cut work along K into
+ * slices whose fp32 partial sums are added in order.  Q4_PATH_GEMV shapes:
+ * slices * M * N floats, cut when K is above 8192 or the activations are too
+ * large for one workgroup's LDS.  Q4_PATH_SMALL: slices * M * N floats for
+ * grids of fewer than 1024 workgroups.  Tiled shapes
+ * (q4_matmul_path_ex(M, N, K, 1) == Q4_PATH_MFMA) with K a multiple of 64:
+ * up to 128 rows, tiles of 128 x 128, slices * M * N floats for grids of
+ * fewer than 512 tiles (at most 768 / tiles and 64 slices, each of at least
+ * 8 steps of 64 k); more rows, tiles of 256 x 128 (one workgroup per CU,
+ * 256 a round): slices * M * N floats for grids of fewer than 171 tiles (at
+ * most 256 / tiles slices), or, for a grid of whole rounds plus a last round
+ * at most half full, the last round's tiles cut into S slices of at least 4
+ * steps (S = min(256 / tail tiles, steps / 4)): tail tiles * S * 256 * 128
+ * floats.  0 when the call needs none, or for sizes q4_matmul would reject. */
 Q4_API size_t q4_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* q4_matmul with an optional workspace.  workspace == NULL: exactly
