@@ -30,6 +30,37 @@ __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS accesses only: it waits for this
+// wavefront's LDS (and scalar) operations but, unlike __syncthreads, whose
+// fence also waits for every global load in flight, lets earlier global
+// loads stay outstanding across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), no vmcnt or expcnt wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Sum over slices s = 0 .. slices-1, in this order, of p[s * stride].  The
+// partial sums come from an earlier kernel's stores (a round trip to the
+// far caches or HBM each), so the loads of B slices at a time are issued
+// before any of them is added.  Slots past the last slice read the last
+// slice again (in bounds) and are not added.
+template <int B, typename T>
+__device__ __forceinline__ T sum_slices(const T* __restrict__ p, int64_t stride, int slices) {
+  T acc = {};
+  for (int s0 = 0; s0 < slices; s0 += B) {
+    T v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      v[j] = p[(int64_t)(s0 + j < slices ? s0 + j : slices - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (s0 + j < slices) acc = s0 + j == 0 ? v[j] : acc + v[j];
+  }
+  return acc;
+}
+
 // Unpacks codes into exact fp16 (c - 8) pairs.
 //
 // A dword's bytes b0..b3 hold elements e0..e7 (b_i low nibble = e_{2i},

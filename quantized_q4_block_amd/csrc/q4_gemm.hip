@@ -626,9 +626,8 @@ __global__ __launch_bounds__(256) void wide_tail_combine_kernel(const float* __r
   const int64_t m = m0 + e / BN, n = n0 + e % BN;
   if (m >= M) return;
   const int64_t block = (int64_t)WM * BN;
-  f32x4v acc = *reinterpret_cast<const f32x4v*>(part + ti * block + e);
-  for (int s = 1; s < slices; ++s)
-    acc += *reinterpret_cast<const f32x4v*>(part + ((int64_t)s * tail_tiles + ti) * block + e);
+  const f32x4v acc = sum_slices<16>(reinterpret_cast<const f32x4v*>(part + ti * block + e),
+                                    tail_tiles * block / 4, slices);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (n + q >= N) break;
@@ -759,37 +758,21 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint16_t* __res
   store_tile(acc, y, y_bf16, part, M, N, m0 + wm * 64, n0 + wn * 64, lane);
 }
 
-// y[i] = sum over slices s = 0 .. slices-1, in order, of partial[s][i]; four
-// consecutive outputs per thread (16-byte loads when MN is a multiple of 4).
+// y[i] = sum over slices s = 0 .. slices-1, in order, of partial[s][i].
 __global__ __launch_bounds__(256) void gemm_combine_kernel(const float* __restrict__ partial,
                                                            void* __restrict__ y, int y_bf16,
                                                            int64_t MN, int slices) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  // one output per thread, so that every slice's load is in flight at once
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= MN) return;
-  if (MN % 4 == 0) {
-    f32x4v acc = *reinterpret_cast<const f32x4v*>(partial + i);
-    for (int s = 1; s < slices; ++s) acc += *reinterpret_cast<const f32x4v*>(partial + s * MN + i);
-    if (y_bf16) {
-      uint2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + i) = o;
-    } else {
-      *reinterpret_cast<f32x4v*>(static_cast<float*>(y) + i) = acc;
-    }
-    return;
-  }
-  for (int64_t e = i; e < i + 4 && e < MN; ++e) {
-    float acc = partial[e];
-    for (int s = 1; s < slices; ++s) acc += partial[s * MN + e];
-    if (y_bf16) static_cast<uint16_t*>(y)[e] = to_bf16(acc);
-    else static_cast<float*>(y)[e] = acc;
-  }
+  const float acc = sum_slices<32>(partial + i, MN, slices);
+  if (y_bf16) static_cast<uint16_t*>(y)[i] = to_bf16(acc);
+  else static_cast<float*>(y)[i] = acc;
 }
 
-// The fp32 slice sums of a cut call into y, enqueued after the product on
-// the same stream.
 hipError_t launch_slice_combine(const float* partial, void* y, bool y_bf16, int64_t MN,
                                  int64_t slices, hipStream_t stream) {
-  const int64_t grid = (MN + 1023) / 1024;
+  const int64_t grid = (MN + 255) / 256;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partial, y,
                      y_bf16 ? 1 : 0, MN, (int)slices);

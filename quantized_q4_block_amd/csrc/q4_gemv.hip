@@ -156,8 +156,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(const float* __restri
                                                            int64_t MN, int slices) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
-    float acc = partial[i];
-    for (int s = 1; s < slices; ++s) acc += partial[(int64_t)s * MN + i];
+    const float acc = sum_slices<32>(partial + i, MN, slices);
     if (y_bf16)
       static_cast<uint16_t*>(y)[i] = to_bf16(acc);
     else

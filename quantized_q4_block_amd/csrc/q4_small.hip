@@ -268,6 +268,250 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few rows with a K-slice workspace (M <= 16): the matrix-vector kernel's
+// streaming structure on the matrix cores.  A workgroup of kBatchWaves
+// wavefronts owns 16 * kBatchWaves weight rows and one K slice of
+// kBatchBlocks blocks; each wavefront takes 16 rows of the slice and issues
+// every code and scale load of them up front (kBatchGroups 4-block groups,
+// the few-row kernel's lane layout and transpose), after the loads of the
+// slice's activations, which the workgroup then writes once to LDS as MFMA A
+// operands while the weights are in flight.  Products are the few-row
+// kernel's: one v_mfma_f32_16x16x32_bf16 per block with exact bf16 (c - 8),
+// the block's scale applied to the 16 x 16 partial in fp32.  Every
+// workgroup of the grid is resident at once for the shapes this kernel is
+// chosen for, so the whole weight stream is in flight from the start.  The
+// fp32 partial sums of the slices are added in slice order afterwards.
+constexpr int kBatchWaves = 8;
+constexpr int kBatchGroups = 8;
+constexpr int kBatchBlocks = 4 * kBatchGroups;
+constexpr int64_t kBatchMaxSlices = 64;
+
+// LDS unit (b, g, r), 16 bytes: x[r][32 b + 8 g .. + 7] of the slice's block b
+// (the A operand of lane 16 g + r), rows r >= M zero.  Consecutive lanes read
+// consecutive units (no bank conflicts).
+__device__ __forceinline__ int batch_unit(int b, int g, int r) { return (b * 4 + g) * 16 + r; }
+
+// STAGED: the workgroup's scales of the slice (128 rows x kBatchBlocks) go
+// through LDS too, one 16-byte load per thread (rows whose slice scales are
+// 16-byte aligned: K/32 a multiple of 8 for fp16, of 4 for fp32 scales);
+// otherwise each lane loads its row's scales group by group (16 rows per
+// load instruction, a few bytes each: far slower on HBM).
+template <bool SCALE4, bool STAGED, typename SP>
+__global__ __launch_bounds__(kBatchWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void batch_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const SP* __restrict__ ws,
+    void* __restrict__ y, int y_bf16, int64_t M, int64_t N, int64_t K, float* __restrict__ partial) {
+  static_assert(!STAGED || SCALE4, "staged scales come in whole groups");
+  constexpr int kThreads = kBatchWaves * 64;
+  constexpr int kUnits = kBatchBlocks * 4 * 16;
+  constexpr int kPer = kUnits / kThreads;
+  constexpr bool kF32 = std::is_same<SP, float>::value;
+  // scales of a group as loaded: 4 fp16 in 2 dwords or 4 fp32
+  constexpr int SW = kF32 ? 4 : 2;
+  // staged scales: row stride in bytes (a row's slice plus 8 or 16 bytes of
+  // padding, so that the 16 rows a load instruction reads fall in distinct
+  // banks) and 16-byte chunks per row
+  constexpr int kSRow = kF32 ? kBatchBlocks * 4 + 16 : kBatchBlocks * 2 + 8;
+  constexpr int kSChunks = kBatchBlocks * (int)sizeof(SP) / 16;
+  constexpr int kSPer = STAGED ? 16 * kBatchWaves * kSChunks / kThreads : 0;
+  __shared__ uint4 xa[kUnits];
+  __shared__ __attribute__((aligned(16))) uint8_t ss[STAGED ? 16 * kBatchWaves * kSRow : 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t bpr = K / kBlock;
+  const int64_t kb0 = (int64_t)blockIdx.y * kBatchBlocks;
+  const int nb = (int)(bpr - kb0 < kBatchBlocks ? bpr - kb0 : kBatchBlocks);   // >= 1
+  const int64_t n = (int64_t)blockIdx.x * (16 * kBatchWaves) + wave * 16 + r;
+  const int64_t nl = n < N ? n : N - 1;
+
+  // activation loads first (the memory counter waits in issue order, so
+  // they can be used while the weight loads are still in flight); units
+  // of rows past M or blocks past the slice read the slice's first unit
+  // and are masked to zero
+  uint4 xv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = i * kThreads + (int)threadIdx.x;
+    const int b = u >> 6, gg = (u >> 4) & 3, m = u & 15;
+    const bool ok = m < M && b < nb;
+    const uint16_t* src = x + (ok ? (int64_t)m * K + (kb0 + b) * kBlock + gg * 8 : kb0 * kBlock);
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
+    xv[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+  }
+  // staged scales: thread t loads chunk t % kSChunks of workgroup row
+  // t / kSChunks (clamped to the last row); chunks past the slice are not
+  // loaded (the slice's blocks come in whole chunks)
+  const int64_t wg_n0 = (int64_t)blockIdx.x * (16 * kBatchWaves);
+  uint4 sv4[kSPer > 0 ? kSPer : 1];
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int i = 0; i < kSPer; ++i) {
+      const int c = i * kThreads + (int)threadIdx.x;
+      const int row = c / kSChunks, ch = c % kSChunks;
+      const int64_t sn = wg_n0 + row < N ? wg_n0 + row : N - 1;
+      const int chunk_blocks = 16 / (int)sizeof(SP);
+      const int cb = ch * chunk_blocks < nb ? ch * chunk_blocks : 0;
+      typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
+      const u32x4nt t =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4nt*>(ws + sn * bpr + kb0 + cb));
+      sv4[i] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+  }
+  // every code load of the wavefront's 16 rows (and, not staged, every
+  // scale load): group j, lane (r, g) takes block 4 j + g of its row
+  // (clamped to the slice)
+  const uint8_t* wrow = wq + nl * (K / 2) + kb0 * 16;
+  const SP* srow = ws + nl * bpr + kb0;
+  uint32_t codes[kBatchGroups][4];
+  uint32_t sraw[STAGED ? 1 : kBatchGroups][SW];
+#pragma unroll
+  for (int j = 0; j < kBatchGroups; ++j) {
+    const int bj = 4 * j + g < nb ? 4 * j + g : nb - 1;
+    // ordinary loads: with the non-temporal hint this pattern (16 rows x 64
+    // bytes per instruction) streams about 15% slower from HBM
+    const u32x4 v = *reinterpret_cast<const u32x4*>(wrow + bj * 16);
+    codes[j][0] = v[0];
+    codes[j][1] = v[1];
+    codes[j][2] = v[2];
+    codes[j][3] = v[3];
+    if constexpr (STAGED) {
+    } else if constexpr (SCALE4) {
+      // whole groups (bpr and the slice start are multiples of 4); a group
+      // past the slice reads the slice's first group
+      const int b0 = 4 * j < nb ? 4 * j : 0;
+      if constexpr (SW == 4) {
+        typedef float f32x4nt __attribute__((ext_vector_type(4)));
+        const f32x4nt t = __builtin_nontemporal_load(reinterpret_cast<const f32x4nt*>(srow + b0));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sraw[j][q] = __builtin_bit_cast(uint32_t, t[q]);
+      } else {
+        typedef uint32_t u32x2nt __attribute__((ext_vector_type(2)));
+        const u32x2nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x2nt*>(srow + b0));
+        sraw[j][0] = t[0];
+        sraw[j][1] = t[1];
+      }
+    } else {
+      SP sv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * j + q < nb ? 4 * j + q : nb - 1;
+        sv[q] = __builtin_nontemporal_load(srow + b);
+      }
+      if constexpr (SW == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sraw[j][q] = __builtin_bit_cast(uint32_t, sv[q]);
+      } else {
+        sraw[j][0] = (uint32_t)sv[0] | ((uint32_t)sv[1] << 16);
+        sraw[j][1] = (uint32_t)sv[2] | ((uint32_t)sv[3] << 16);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load ahead of the staging
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = i * kThreads + (int)threadIdx.x;
+    if ((u >> 6) < nb) xa[u] = xv[i];
+  }
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int i = 0; i < kSPer; ++i) {
+      const int c = i * kThreads + (int)threadIdx.x;
+      const int row = c / kSChunks, ch = c % kSChunks;
+      uint8_t* dst = ss + row * kSRow + ch * 16;
+      if constexpr (kF32) {
+        *reinterpret_cast<uint4*>(dst) = sv4[i];
+      } else {   // 8-byte aligned rows: two 8-byte stores
+        reinterpret_cast<uint2*>(dst)[0] = make_uint2(sv4[i].x, sv4[i].y);
+        reinterpret_cast<uint2*>(dst)[1] = make_uint2(sv4[i].z, sv4[i].w);
+      }
+    }
+  }
+  lds_barrier();   // the code loads stay in flight
+
+  const ExactBf16Unpacker unpack;
+  const f32x4v zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4v acc = zero;
+#pragma unroll
+  for (int j = 0; j < kBatchGroups; ++j) {
+    if (4 * j >= nb) break;   // wave-uniform
+    uint32_t sg[SW];          // the group's 4 scales of this lane's row
+    if constexpr (STAGED) {
+      const uint8_t* src = ss + (wave * 16 + r) * kSRow + j * 4 * (int)sizeof(SP);
+      if constexpr (kF32) {
+        const uint4 t = *reinterpret_cast<const uint4*>(src);
+        sg[0] = t.x; sg[1] = t.y; sg[2] = t.z; sg[3] = t.w;
+      } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(src);
+        sg[0] = t.x; sg[1] = t.y;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < SW; ++q) sg[q] = sraw[j][q];
+    }
+    transpose_groups(codes[j]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = 4 * j + q;
+      if (b >= nb) break;
+      const bf16x8v w = codes_to_bf16(codes[j][q], unpack);
+      const bf16x8v a = __builtin_bit_cast(bf16x8v, xa[batch_unit(b, g, r)]);
+      const f32x4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, zero, 0, 0, 0);
+      float sc;
+      if constexpr (SW == 4) sc = __builtin_bit_cast(float, sg[q]);
+      else sc = (float)__builtin_bit_cast(half2v, sg[q >> 1])[q & 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, p[e], acc[e]);
+    }
+  }
+  // lane (r, g) holds rows 4 g .. 4 g + 3 of column n
+  if (n >= N) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t m = 4 * g + e;
+    if (m >= M) break;
+    if (gridDim.y > 1) partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[e];
+    else if (y_bf16) static_cast<uint16_t*>(y)[m * N + n] = to_bf16(acc[e]);
+    else static_cast<float*>(y)[m * N + n] = acc[e];
+  }
+}
+
+namespace {
+
+// K slices of the workspace kernel (0: not taken): one per kBatchBlocks
+// blocks, for 3 <= M <= 16 and rows of 2 .. kBatchMaxSlices slices.
+int64_t batch_slices(int64_t M, int64_t K) {
+  if (M < 3 || M > 16 || K % kBlock != 0) return 0;
+  const int64_t s = (K / kBlock + kBatchBlocks - 1) / kBatchBlocks;
+  return s >= 2 && s <= kBatchMaxSlices ? s : 0;
+}
+
+template <typename SP>
+hipError_t launch_batch(const uint16_t* x, const uint8_t* wq, const SP* ws, void* y, bool y_bf16,
+                        int64_t M, int64_t N, int64_t K, float* partial, hipStream_t stream) {
+  const int64_t slices = batch_slices(M, K);
+  const int64_t gx = (N + 16 * kBatchWaves - 1) / (16 * kBatchWaves);
+  if (slices == 0 || gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)slices);
+  const int64_t bpr = K / kBlock;
+  constexpr int64_t kStagedAlign = 16 / sizeof(SP);   // scales per 16 bytes
+  if (bpr % kStagedAlign == 0 && bpr % 4 == 0)
+    batch_kernel<true, true, SP><<<grid, dim3(kBatchWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, partial);
+  else if (bpr % 4 == 0)
+    batch_kernel<true, false, SP><<<grid, dim3(kBatchWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, partial);
+  else
+    batch_kernel<false, false, SP><<<grid, dim3(kBatchWaves * 64), 0, stream>>>(
+        x, wq, ws, y, y_bf16 ? 1 : 0, M, N, K, partial);
+  const hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess) return e;
+  return launch_slice_combine(partial, y, y_bf16, M * N, slices, stream);
+}
+
+}  // namespace
+
 namespace {
 
 #ifndef Q4_SMALL_SPLIT_WGS
@@ -324,6 +568,7 @@ hipError_t launch_mg(const uint16_t* x, const uint8_t* wq, const void* ws, void*
 }  // namespace
 
 int64_t small_split_slices(int64_t M, int64_t N, int64_t K) {
+  if (const int64_t b = batch_slices(M, K)) return b;
   int64_t slices, per;
   small_plan(M, N, K, true, &slices, &per);
   return slices;
@@ -332,6 +577,8 @@ int64_t small_split_slices(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,
                         bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                         hipStream_t stream) {
+  if (partial && batch_slices(M, K))
+    return launch_batch(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
   if (M <= 16) return launch_mg<1, false>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
   return launch_mg<2, false>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
 }
@@ -339,6 +586,8 @@ hipError_t launch_small(const uint16_t* x, const uint8_t* wq, const uint16_t* ws
 hipError_t launch_small_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
                              bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                              hipStream_t stream) {
+  if (partial && batch_slices(M, K))
+    return launch_batch(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
   if (M <= 16) return launch_mg<1, false, true>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
   return launch_mg<2, false, true>(x, wq, ws, y, y_bf16, M, N, K, partial, stream);
 }

@@ -191,15 +191,22 @@ def test_matmul_workspace_bytes():
     assert q4.q4_matmul_workspace_bytes(129, 130, 64 * 16) == 2 * 129 * 130 * 4
     assert q4.q4_matmul_workspace_bytes(200, 128, 64 * 520) == 58 * 200 * 128 * 4
     assert q4.q4_matmul_workspace_bytes(300, 77, 96) == 0                  # K % 64 != 0
-    # few rows: grids of fewer than 1024 workgroups (32 weight rows by 16 or
-    # 32 activation rows) are cut along K, aiming at 1024 workgroups, into
-    # slices of a multiple of 8 four-block groups: 160 workgroups and 136
-    # groups at 5120 x 17408 make 6 slices of 24 groups
-    for M in (3, 4, 5, 32):
-        assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == 6 * M * 5120 * 4
-    assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 5 * 4 * 100 * 4     # 40 groups
-    assert q4.q4_matmul_workspace_bytes(4, 32768, 4096) == 0                 # 1024 workgroups
+    # 3..16 rows with a workspace: one K slice per 32 blocks when that makes
+    # 2 .. 64 slices (544 blocks: 17 slices; 160 blocks: 5; 128 blocks: 4)
+    for M in (3, 4, 5, 16):
+        assert q4.q4_matmul_workspace_bytes(M, 5120, 17408) == 17 * M * 5120 * 4
+    assert q4.q4_matmul_workspace_bytes(4, 100, 5120) == 5 * 4 * 100 * 4
+    assert q4.q4_matmul_workspace_bytes(4, 32768, 4096) == 4 * 4 * 32768 * 4
+    assert q4.q4_matmul_workspace_bytes(4, 5120, 1024) == 0                  # one slice
+    # longer rows, and 17..32 rows: grids of fewer than 1024 workgroups (32
+    # weight rows by 16 or 32 activation rows) are cut along K, aiming at 1024
+    # workgroups, into slices of a multiple of 8 four-block groups: 160
+    # workgroups and 136 groups at 5120 x 17408 make 6 slices of 24 groups
+    assert q4.q4_matmul_workspace_bytes(32, 5120, 17408) == 6 * 32 * 5120 * 4
     assert q4.q4_matmul_workspace_bytes(4, 5120, 512) == 0                   # 4 groups
+    # 2080 blocks would make 65 slices of 32: the few-row kernel's plan (520
+    # four-block groups, 160 workgroups: 7 slices of 80 groups)
+    assert q4.q4_matmul_workspace_bytes(4, 5120, 66560) == 7 * 4 * 5120 * 4
     assert q4.q4_matmul_workspace_bytes(2, 5120, 48) == 0
     assert q4.q4_matmul_workspace_bytes(-1, 5120, 17408) == 0
     # long rows on the matrix-vector path: one fp32 partial sum per slice,

@@ -117,8 +117,9 @@ def test_gemv_parity(M, N, K):
 # path): two-stage slices of 86 (K = 8224), 108/109 (17408) and 128 (16384)
 # blocks; K = 258080 (8065 blocks) takes one-stage slices; K = 5696 (178
 # blocks, 3 stages) fits one workgroup and is not cut.  At M = 3, 4 the call
-# takes the few-row matrix-core path, cut along K into slices when its grid
-# has few workgroups.
+# takes the few-row matrix-core path: with a workspace, one K slice per 32
+# blocks (the 8065-block rows, too many slices, keep the few-row kernel's
+# plan).
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("N,K", [(37, 8192 + 32), (300, 17408), (65, 5696), (17, 16384),
                                  (5, 258080)])
@@ -205,6 +206,25 @@ def test_small_split_parity(M, N, K):
     assert_parity(y, y_ref, t, RTOL, what=f"small split M={M} N={N} K={K}")
     yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
     assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"small split bf16 M={M}")
+
+
+# 3..16 rows with a workspace take the sliced kernel (one slice per 32
+# blocks): scales staged through LDS (K/32 a multiple of 8), loaded per lane
+# in aligned groups (36 blocks: a multiple of 4 only) and one by one (65
+# blocks), last slices of 4 and of 1 block, ragged 128-row weight groups,
+# and both ends of its activation-row range.
+@pytest.mark.parametrize("M,N,K", [(3, 300, 1152), (7, 129, 2080), (16, 257, 4096),
+                                   (5, 1, 2048 + 32), (4, 640, 17408 + 128)])
+def test_sliced_few_row_parity(M, N, K):
+    need = q4.q4_matmul_workspace_bytes(M, N, K)
+    slices = -(-(K // 32) // 32)
+    assert need == slices * M * N * 4
+    d = synthetic.dense_case(6950 + M + N, M, N, K)
+    y_ref, t = oracle.matmul(d.x, d.w_q, d.w_s)
+    y = matmul_ex(d.x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"sliced M={M} N={N} K={K}")
+    yb = matmul_ex(d.x, d.w_q, d.w_s, BF16)
+    assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"sliced bf16 M={M}")
 
 
 def test_small_split_deterministic_and_workspace_reuse():
@@ -384,9 +404,8 @@ def test_sparse_codes_exact_per_weight(M):
 @pytest.mark.parametrize("M", [1, 2, 4])
 @pytest.mark.parametrize("kind", ["wide", "subnormal", "huge", "tiny"])
 def test_gemv_activation_ranges(M, kind):
-    """Activation rows the decode kernel cannot scale into exact fp16 (range
-    beyond 2^28, a bf16 subnormal) or that sit at the ends of bf16's range:
-    results must still be exact-weight parity."""
+    """Activation rows of extreme range: a value 2^63 times the rest, a bf16
+    subnormal, and every value scaled by 2^100 or 2^-100."""
     N, K = 200, 5120
     d = synthetic.dense_case(5300 + M, M, N, K)
     x = d.x.copy()
@@ -402,6 +421,61 @@ def test_gemv_activation_ranges(M, kind):
     y = matmul(x, d.w_q, d.w_s)
     y_ref, t = oracle.matmul(x, d.w_q, d.w_s)
     assert_parity(y, y_ref, t, RTOL, what=f"range {kind} M={M}")
+
+
+def _two_spikes(K, k0, k1, a, spread, rng):
+    """A bf16 row that is zero but for x[k0] = +-2^a (1 + f) and
+    x[k1] = +-2^(a - spread) (1 + g), f and g random 7-bit fractions."""
+    x = np.zeros(K, np.float32)
+    for k, e in ((k0, a), (k1, a - spread)):
+        frac = 1.0 + rng.integers(0, 128) / 128.0
+        x[k] = np.float32(rng.choice([-1.0, 1.0]) * frac * 2.0 ** e)
+    return synthetic.f32_to_bf16_bits(x)
+
+
+# (k0, k1): both spikes in one dword (k and k + 4; k and k + 1), in stages 0
+# and 1, and the second one in the leftover stage
+def _spikes(K):
+    return [(96, 100), (100, 101), (100, 2100), (17, K - 20)]
+
+
+@pytest.mark.parametrize("K", [5120, 2048 + 32 * 40])
+def test_gemv_two_spikes_exactly_rounded(K):
+    """With unit scales and two nonzero activations per row, the decode
+    kernel forms y[n] = (c0 - 8) x0 + (c1 - 8) x1 with a single rounding
+    (every product is exact and every other term is an exact zero), so y
+    must be the oracle's double result rounded to fp32, bit for bit, for
+    spikes up to 2^45 apart and at both ends of the exponent range."""
+    N = 130
+    d = synthetic.dense_case(5350, 1, N, K)
+    w_s = np.full_like(d.w_s, 0x3C00)                       # 1.0
+    rng = np.random.default_rng(11)
+    for k0, k1 in _spikes(K):
+        for a in (100, 40, 15, 3, 0, -14, -40, -70):
+            for spread in (0, 1, 15, 28, 29, 30, 31, 45):
+                x = _two_spikes(K, k0, k1, a, spread, rng)[None, :]
+                y = matmul(x, d.w_q, w_s)[0]
+                y_ref, _ = oracle.matmul(x, d.w_q, w_s)
+                want = y_ref[0].astype(np.float32).astype(np.float64)
+                assert np.array_equal(y, want), f"K={K} k=({k0},{k1}) a={a} spread={spread}"
+
+
+def test_gemv_two_rows_of_different_ranges():
+    """M = 2: a random row next to a row of two values 2^40 apart, next to an
+    all-zero row, and two zero rows; a zero row gives exactly zero."""
+    N, K = 200, 5120
+    d = synthetic.dense_case(5360, 2, N, K)
+    x = d.x.copy()
+    odd = _two_spikes(K, 10, 4000, 5, 40, np.random.default_rng(12))
+    zero = np.zeros(K, np.uint16)
+    for rows in (np.stack([x[0], odd]), np.stack([odd, x[1]]), np.stack([x[0], zero]),
+                 np.stack([zero, zero])):
+        y = matmul(rows, d.w_q, d.w_s)
+        y_ref, t = oracle.matmul(rows, d.w_q, d.w_s)
+        assert_parity(y, y_ref, t, RTOL, what="two rows")
+        for m in range(2):
+            if not rows[m].any():
+                assert np.all(y[m] == 0)
 
 
 @pytest.mark.parametrize("M", [1, 16])
