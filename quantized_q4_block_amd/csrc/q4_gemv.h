@@ -236,6 +236,37 @@ __device__ __forceinline__ int64_t tail_row(const StagePlan& sp, int r) {
 }
 
 // ---------------------------------------------------------------------------
+// Raw buffer loads.  A wave-uniform base becomes a buffer descriptor (scalar
+// registers) whose extent bounds the loads: an offset past it reads zero,
+// never another allocation.  Offsets are 32-bit: a per-lane vector part and
+// a scalar part, so no 64-bit address is formed per load and lane on the
+// vector unit (these kernels are bound by vector instruction issue).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  // word 3 of a gfx9 raw-buffer descriptor (untyped loads)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// aux = 2: the non-temporal hint (each weight byte is used once)
+__device__ __forceinline__ uint4 buffer_codes(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                              uint32_t soff) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v =
+      __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void buffer_scale(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                             uint32_t soff, _Float16& s) {
+  s = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 2));
+}
+__device__ __forceinline__ void buffer_scale(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                             uint32_t soff, uint8_t& s) {
+  s = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, soff, 2);
+}
+__device__ __forceinline__ void buffer_scale(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                             uint32_t soff, float& s) {
+  s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 2));
+}
+
+// ---------------------------------------------------------------------------
 // Activations in LDS as fp32 (exact from bf16), laid out [m][stage][chunk q]
 // [lane] in 16-byte units, chunk q = elements 4q .. 4q+3 of the block, so
 // that in a stage consecutive lanes read consecutive 16 bytes (no bank
@@ -260,23 +291,24 @@ struct XStager {
   uint4 d[M][kPer];
 
   // x: row 0 of the activations at the first element of the row piece; K:
-  // length of the piece; ldx: distance between rows (elements).
+  // length of the piece; ldx: distance between rows (elements).  Raw buffer
+  // loads whose extent is the row piece: a chunk past K (or a thread past
+  // the row's chunks) reads zero, with no address clamp or mask.
   __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int64_t K, int64_t ldx) {
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+    for (int m = 0; m < M; ++m) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(x + m * ldx, (uint32_t)K * 2u);
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int c = i * THREADS + (int)threadIdx.x;
         const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
-        const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 8;
-        const bool ok = (kRowChunks % THREADS == 0 || c < kRowChunks) && k < K;
-        // unconditional load from a clamped address, masked afterwards with
-        // a mask the compiler cannot trace back to `ok` (else it turns the
-        // load into a branch, and every branch waits for earlier loads)
-        const uint4 v = *reinterpret_cast<const uint4*>(x + m * ldx + (ok ? k : 0));
-        const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
-        d[m][i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+        const uint32_t k = (uint32_t)((st * kWave + l) * kBlock + q * 8);
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t v =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, k * 2u, 0, 0));
+        d[m][i] = make_uint4(v[0], v[1], v[2], v[3]);
       }
+    }
   }
   // Marks the loaded activations as used here, so that the compiler cannot
   // sink a load into the conditional store of a thread's last chunk (that
@@ -354,18 +386,21 @@ struct XStagerF32 {
   static constexpr int kPer = (kRowChunks + THREADS - 1) / THREADS;
   uint4 d[kPer][2];
 
+  // raw buffer loads over the row (chunks past K read zero)
   __device__ __forceinline__ void load(const float* __restrict__ x, int64_t K) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(x, (uint32_t)K * 4u);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = i * THREADS + (int)threadIdx.x;
       const int st = c >> 8, q = (c >> 6) & 3, l = c & 63;
-      const int64_t k = (int64_t)(st * kWave + l) * kBlock + q * 8;
-      const bool ok = (kRowChunks % THREADS == 0 || c < kRowChunks) && k < K;
-      const uint4* src = reinterpret_cast<const uint4*>(x + (ok ? k : 0));
-      const uint4 v0 = src[0], v1 = src[1];
-      const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
-      d[i][0] = make_uint4(v0.x & keep, v0.y & keep, v0.z & keep, v0.w & keep);
-      d[i][1] = make_uint4(v1.x & keep, v1.y & keep, v1.z & keep, v1.w & keep);
+      const uint32_t k = (uint32_t)((st * kWave + l) * kBlock + q * 8);
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t v0 =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, k * 4u, 0, 0));
+      const u32x4_t v1 =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, k * 4u + 16u, 0, 0));
+      d[i][0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+      d[i][1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
     }
   }
   __device__ __forceinline__ void pin() const {
@@ -433,39 +468,54 @@ __device__ __forceinline__ uint4 load_codes(const uint8_t* p) {
 // cbase / sbase: codes and scales of the task's first row at the first
 // block of the row piece; row_bytes / row_sc: distance between rows (bytes,
 // scales); room = rows that exist past the first (>= 0); rem = leftover
-// blocks of the piece.
+// blocks of the piece; bpr = blocks from the piece's first block to the end
+// of its rows (bounds the loads).
+//
+// Raw buffer loads (above): descriptors over the task's rows exactly, a
+// row's offset in the scalar part, the lane's block in the vector part.
 template <int R, int FULL, int TAIL, typename SC, typename SP>
 __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL, SC>& b,
                                              const uint8_t* __restrict__ cbase,
                                              const SP* __restrict__ sbase,
                                              uint32_t row_bytes, uint32_t row_sc, int room,
-                                             int rem, int lane) {
-  auto load = [&](int row, uint32_t blk, uint4& c, SC& s) {
+                                             int rem, int lane, uint32_t bpr) {
+  constexpr uint32_t SZ = (uint32_t)sizeof(SP);
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(cbase, (uint32_t)room * row_bytes + bpr * 16u);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sbase, ((uint32_t)room * row_sc + bpr) * SZ);
+  auto load = [&](int row, uint32_t blk, uint32_t lane_blk, uint4& c, SC& s) {
     row = row < room ? row : room;
-    c = load_codes(cbase + (uint32_t)row * row_bytes + blk * 16);
-    load_scale(sbase + (uint32_t)row * row_sc + blk, s);
+    c = buffer_codes(rc, lane_blk * 16u, (uint32_t)row * row_bytes + blk * 16u);
+    buffer_scale(rs, lane_blk * SZ, ((uint32_t)row * row_sc + blk) * SZ, s);
   };
 #pragma unroll
   for (int st = 0; st < FULL; ++st)
 #pragma unroll
-    for (int r = 0; r < R; ++r) load(r, (uint32_t)(st * kWave + lane), b.c[st][r], b.s[st][r]);
+    for (int r = 0; r < R; ++r)
+      load(r, (uint32_t)(st * kWave), (uint32_t)lane, b.c[st][r], b.s[st][r]);
   if constexpr (TAIL == kSplitTail) {
     constexpr int H = R / 2;
     const int sub = lane & 31, half = lane >> 5;
-    const uint32_t blk = (uint32_t)(FULL * kWave + (sub < rem ? sub : 0));
+    const uint32_t t = (uint32_t)(sub < rem ? sub : 0);
+    // the two half-waves read different rows: the row offset is per lane
 #pragma unroll
-    for (int j = 0; j < H; ++j) load(half * H + j, blk, b.ct[j], b.st[j]);
+    for (int j = 0; j < H; ++j) {
+      int row = half * H + j;
+      row = row < room ? row : room;
+      const uint32_t blk = (uint32_t)(FULL * kWave);
+      b.ct[j] = buffer_codes(rc, (uint32_t)row * row_bytes + t * 16u, blk * 16u);
+      buffer_scale(rs, ((uint32_t)row * row_sc + t) * SZ, blk * SZ, b.st[j]);
+    }
   } else if constexpr (TAIL == kWideTail) {
-    const uint32_t blk = (uint32_t)(FULL * kWave + (lane < rem ? lane : 0));
+    const uint32_t t = (uint32_t)(lane < rem ? lane : 0);
 #pragma unroll
-    for (int r = 0; r < R; ++r) load(r, blk, b.ct[r], b.st[r]);
+    for (int r = 0; r < R; ++r) load(r, (uint32_t)(FULL * kWave), t, b.ct[r], b.st[r]);
   }
 }
 
 // Rows per task and wavefronts per workgroup of the kernels built on the
 // up-front loads; rows of at most kLdsMaxStages stages (K <= 8192).
 constexpr int kLdsRows = 2;
-constexpr int kLdsWaves = 8;
+constexpr int kLdsWaves = 4;
 constexpr int kLdsMaxStages = 4;
 
 // Calls f(FULL, TAIL) -- both std::integral_constant -- with the row

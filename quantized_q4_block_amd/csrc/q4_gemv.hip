@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
   UpfrontLoads<R, FULL, TAIL, SC> b;
   upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes + blk0 * 16,
                               ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
-                              lane);
+                              lane, (uint32_t)(ld_blocks - blk0));
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.pin();
   __shared__ double red[NORM ? M : 1][kLdsWaves];

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   const uint32_t row_bytes = (uint32_t)(K / 2), row_sc = (uint32_t)(K / kBlock);
   UpfrontLoads<R, FULL, TAIL> b;
   upfront_load<R, FULL, TAIL>(b, wq_e + nl * (int64_t)row_bytes, ws_e + nl * (int64_t)row_sc,
-                              row_bytes, row_sc, room, rem, lane);
+                              row_bytes, row_sc, room, rem, lane, row_sc);
   __builtin_amdgcn_sched_barrier(0);
   int32_t p = order[start];   // an active expert has at least one pair
   stage(p);

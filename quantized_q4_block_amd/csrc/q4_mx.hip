@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void mx_lds_kernel(
   xst.load(x, K, K);
   UpfrontLoads<R, FULL, TAIL, uint8_t> b;
   upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes, we + nl * (int64_t)row_sc,
-                              row_bytes, row_sc, room, rem, lane);
+                              row_bytes, row_sc, room, rem, lane, row_sc);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.pin();
   xst.store_f32(xs);
