@@ -30,6 +30,16 @@ __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
   return v;
 }
 
+// Raw buffer loads: a wave-uniform base becomes a buffer descriptor (scalar
+// registers) whose extent bounds the loads -- an offset past it reads zero,
+// never another allocation.  Offsets are 32-bit, a per-lane vector part and
+// a scalar part, so no 64-bit address is formed per load and lane on the
+// vector unit (the streaming kernels are bound by vector instruction issue).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  // word 3 of a gfx9 raw-buffer descriptor (untyped loads)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // Workgroup barrier that orders LDS accesses only: it waits for this
 // wavefront's LDS (and scalar) operations but, unlike __syncthreads, whose
 // fence also waits for every global load in flight, lets earlier global

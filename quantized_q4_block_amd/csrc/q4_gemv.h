@@ -236,15 +236,7 @@ __device__ __forceinline__ int64_t tail_row(const StagePlan& sp, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// Raw buffer loads.  A wave-uniform base becomes a buffer descriptor (scalar
-// registers) whose extent bounds the loads: an offset past it reads zero,
-// never another allocation.  Offsets are 32-bit: a per-lane vector part and
-// a scalar part, so no 64-bit address is formed per load and lane on the
-// vector unit (these kernels are bound by vector instruction issue).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  // word 3 of a gfx9 raw-buffer descriptor (untyped loads)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
+// Code and scale loads through buffer descriptors (buffer_rsrc).
 // aux = 2: the non-temporal hint (each weight byte is used once)
 __device__ __forceinline__ uint4 buffer_codes(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                               uint32_t soff) {
