@@ -144,8 +144,10 @@ Q4_API int32_t q4_matmul(const void *x, const void *w_q, const void *w_s,
 /* Device workspace (bytes) that lets q4_matmul_ex cut work along K into
  * slices whose fp32 partial sums are added in order.  Q4_PATH_GEMV shapes:
  * slices * M * N floats, cut when K is above 8192 or the activations are too
- * large for one workgroup's LDS.  Q4_PATH_SMALL: slices * M * N floats for
- * grids of fewer than 1024 workgroups.  Tiled shapes
+ * large for one workgroup's LDS.  Q4_PATH_SMALL: 3..16 rows, slices * M * N
+ * floats with one slice per 32 blocks of K when that makes 2..64 slices;
+ * otherwise slices * M * N floats for grids of fewer than 1024 workgroups.
+ * Tiled shapes
  * (q4_matmul_path_ex(M, N, K, 1) == Q4_PATH_MFMA) with K a multiple of 64:
  * up to 128 rows, tiles of 128 x 128, slices * M * N floats for grids of
  * fewer than 512 tiles (at most 768 / tiles and 64 slices, each of at least
