@@ -269,6 +269,85 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MG 
 }
 
 // ---------------------------------------------------------------------------
+// fp16 operands for the few-row kernels.  A bf16 value has an 8-bit
+// significand, so it is an fp16 normal number exactly when its exponent lies
+// in -14 .. 15.  When the nonzero activations of a workgroup's slice span at
+// most 30 binary exponents (largest minus smallest <= 29), none of them
+// subnormal, infinite or NaN, one power-of-two scaling x' = x * 2^-e puts
+// all of them in that window; (c - 8) is exact in fp16 too, so
+// v_mfma_f32_16x16x32_f16 forms the same exact products as the bf16 one,
+// and the unpack of 8 codes takes 9 instructions instead of 17.  The
+// results are multiplied back by 2^e (exact).  The range of a set of bf16
+// values is kept as a "range key": the largest magnitude (bits without the
+// sign) in the low 16 bits and 0x8000 minus the smallest nonzero magnitude
+// in the high 16 bits (0 when all are zero), both maxima, so keys combine
+// with one packed 16-bit maximum.
+namespace {
+
+typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2v, a),
+                                                                __builtin_bit_cast(u16x2v, b)));
+}
+
+// range key of the 8 bf16 values of a 16-byte unit
+__device__ __forceinline__ uint32_t unit_range_key(uint4 v) {
+  const u16x2v one = {1, 1}, top = {0x7FFF, 0x7FFF};
+  u16x2v mag = {0, 0}, inv = {0, 0};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u16x2v m = __builtin_bit_cast(u16x2v, w[q] & 0x7FFF7FFFu);
+    mag = __builtin_elementwise_max(mag, m);
+    // zero wraps to 0xFFFF and saturates to 0; a magnitude v >= 1 gives 0x8000 - v
+    inv = __builtin_elementwise_max(inv, __builtin_elementwise_sub_sat(top, m - one));
+  }
+  const uint32_t lo = mag[0] > mag[1] ? mag[0] : mag[1];
+  const uint32_t hi = inv[0] > inv[1] ? inv[0] : inv[1];
+  return lo | hi << 16;
+}
+
+// wave-uniform packed maximum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_pk_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    v = pk_max_u16(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// The scaling exponent e for a range key, and whether the values fit.  Of
+// the exponents that work the one nearest 0 is taken; e lies in -112 .. 112,
+// so 2^e and 2^-e are normal fp32.
+__device__ __forceinline__ bool h16_scale(uint32_t key, int& e) {
+  const uint32_t inv = key >> 16;
+  e = 0;
+  if (inv == 0) return true;   // all zero
+  const int emax = (int)((key & 0xFFFFu) >> 7), emin = (int)((0x8000u - inv) >> 7);
+  const int lo = emax - 127 - 15, hi = emin - 127 + 14;   // need lo <= e <= hi
+  const int near0 = hi < 0 ? hi : 0;
+  e = lo > near0 ? lo : near0;
+  return emax <= 254 && emin >= 1 && emax - emin <= 29;
+}
+
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// The unit as fp16 x * sc in CodeUnpacker's element order (e0, e4, e1, e5,
+// e2, e6, e3, e7), so that it pairs with the unpacked codes of one dword.
+__device__ __forceinline__ uint4 unit_to_f16(uint4 v, float sc) {
+  auto pair = [](float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  };
+  return make_uint4(pair(bf16_lo(v.x) * sc, bf16_lo(v.z) * sc),
+                    pair(bf16_hi(v.x) * sc, bf16_hi(v.z) * sc),
+                    pair(bf16_lo(v.y) * sc, bf16_lo(v.w) * sc),
+                    pair(bf16_hi(v.y) * sc, bf16_hi(v.w) * sc));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // Few rows with a K-slice workspace (M <= 16): the matrix-vector kernel's
 // streaming structure on the matrix cores.  A workgroup of kBatchWaves
 // wavefronts owns 16 * kBatchWaves weight rows and one K slice of
@@ -326,19 +405,21 @@ __global__ __launch_bounds__(kBatchWaves * 64) __attribute__((amdgpu_waves_per_e
   const int64_t nl = n < N ? n : N - 1;
 
   // activation loads first (the memory counter waits in issue order, so
-  // they can be used while the weight loads are still in flight); units
-  // of rows past M or blocks past the slice read the slice's first unit
-  // and are masked to zero
+  // they can be used while the weight loads are still in flight).  Unit
+  // number v = 128 m + 4 b + g (row m, block b, 8-element group g) so that
+  // the real rows come first: with M <= 4 every thread holds one real unit
+  // in xv[0].  Units of rows past M or blocks past the slice read the
+  // slice's first unit and are masked to zero.
   uint4 xv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int u = i * kThreads + (int)threadIdx.x;
-    const int b = u >> 6, gg = (u >> 4) & 3, m = u & 15;
+    const int v = i * kThreads + (int)threadIdx.x;
+    const int m = v >> 7, b = (v >> 2) & 31, gg = v & 3;
     const bool ok = m < M && b < nb;
     const uint16_t* src = x + (ok ? (int64_t)m * K + (kb0 + b) * kBlock + gg * 8 : kb0 * kBlock);
-    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const uint4 xw = *reinterpret_cast<const uint4*>(src);
     const uint32_t keep = opaque_vgpr(ok ? 0xFFFFFFFFu : 0u);
-    xv[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    xv[i] = make_uint4(xw.x & keep, xw.y & keep, xw.z & keep, xw.w & keep);
   }
   // staged scales: thread t loads chunk t % kSChunks of workgroup row
   // t / kSChunks (clamped to the last row); chunks past the slice are not
@@ -409,10 +490,30 @@ __global__ __launch_bounds__(kBatchWaves * 64) __attribute__((amdgpu_waves_per_e
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // every load ahead of the staging
+  // the slice's activation range (units past the real rows hold zeros and
+  // are skipped; the condition is uniform)
+  __shared__ uint32_t rng[kBatchWaves];
+  uint32_t key = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (i * kThreads < M * 128) key = pk_max_u16(key, unit_range_key(xv[i]));
+  key = wave_pk_max(key);
+  if (lane == 0) rng[wave] = key;
+  lds_barrier();
+  uint32_t all = rng[0];
+#pragma unroll
+  for (int w = 1; w < kBatchWaves; ++w) all = pk_max_u16(all, rng[w]);
+  int e16;
+  const bool h16 = h16_scale(__builtin_amdgcn_readfirstlane((int)all), e16);
+  const float sc16 = pow2f(-e16);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int u = i * kThreads + (int)threadIdx.x;
-    if ((u >> 6) < nb) xa[u] = xv[i];
+    const int v = i * kThreads + (int)threadIdx.x;
+    const int m = v >> 7, b = (v >> 2) & 31, gg = v & 3;
+    if (b >= nb) continue;
+    uint4 u = xv[i];
+    if (h16 && i * kThreads < M * 128) u = unit_to_f16(u, sc16);   // zeros stay zero
+    xa[batch_unit(b, gg, m)] = u;
   }
   if constexpr (STAGED) {
 #pragma unroll
@@ -430,40 +531,63 @@ __global__ __launch_bounds__(kBatchWaves * 64) __attribute__((amdgpu_waves_per_e
   }
   lds_barrier();   // the code loads stay in flight
 
-  const ExactBf16Unpacker unpack;
   const f32x4v zero = {0.f, 0.f, 0.f, 0.f};
   f32x4v acc = zero;
+  // one 4-block group: the lane's row scales, the transpose, then each block
+  // inside the slice as one MFMA (fp16 or bf16 operands) and four fmas
+  auto groups = [&](auto fp16) __attribute__((always_inline)) {
+    constexpr bool kH = decltype(fp16)::value;
+    const ExactBf16Unpacker unpack;
+    const CodeUnpacker unpack16;
 #pragma unroll
-  for (int j = 0; j < kBatchGroups; ++j) {
-    if (4 * j >= nb) break;   // wave-uniform
-    uint32_t sg[SW];          // the group's 4 scales of this lane's row
-    if constexpr (STAGED) {
-      const uint8_t* src = ss + (wave * 16 + r) * kSRow + j * 4 * (int)sizeof(SP);
-      if constexpr (kF32) {
-        const uint4 t = *reinterpret_cast<const uint4*>(src);
-        sg[0] = t.x; sg[1] = t.y; sg[2] = t.z; sg[3] = t.w;
+    for (int j = 0; j < kBatchGroups; ++j) {
+      if (4 * j >= nb) break;   // wave-uniform
+      uint32_t sg[SW];          // the group's 4 scales of this lane's row
+      if constexpr (STAGED) {
+        const uint8_t* src = ss + (wave * 16 + r) * kSRow + j * 4 * (int)sizeof(SP);
+        if constexpr (kF32) {
+          const uint4 t = *reinterpret_cast<const uint4*>(src);
+          sg[0] = t.x; sg[1] = t.y; sg[2] = t.z; sg[3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(src);
+          sg[0] = t.x; sg[1] = t.y;
+        }
       } else {
-        const uint2 t = *reinterpret_cast<const uint2*>(src);
-        sg[0] = t.x; sg[1] = t.y;
+#pragma unroll
+        for (int q = 0; q < SW; ++q) sg[q] = sraw[j][q];
       }
-    } else {
+      transpose_groups(codes[j]);
 #pragma unroll
-      for (int q = 0; q < SW; ++q) sg[q] = sraw[j][q];
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * j + q;
+        if (b >= nb) break;
+        const uint4 au = xa[batch_unit(b, g, r)];
+        f32x4v p;
+        if constexpr (kH) {
+          half2v hp[4];
+          unpack16(codes[j][q], hp);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, au),
+                                                     __builtin_bit_cast(f16x8v, hp), zero, 0, 0, 0);
+        } else {
+          const bf16x8v w = codes_to_bf16(codes[j][q], unpack);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, au), w, zero, 0,
+                                                      0, 0);
+        }
+        float sc;
+        if constexpr (SW == 4) sc = __builtin_bit_cast(float, sg[q]);
+        else sc = (float)__builtin_bit_cast(half2v, sg[q >> 1])[q & 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, p[e], acc[e]);
+      }
     }
-    transpose_groups(codes[j]);
+  };
+  if (h16) {
+    groups(std::true_type{});
+    const float back = pow2f(e16);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int b = 4 * j + q;
-      if (b >= nb) break;
-      const bf16x8v w = codes_to_bf16(codes[j][q], unpack);
-      const bf16x8v a = __builtin_bit_cast(bf16x8v, xa[batch_unit(b, g, r)]);
-      const f32x4v p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, zero, 0, 0, 0);
-      float sc;
-      if constexpr (SW == 4) sc = __builtin_bit_cast(float, sg[q]);
-      else sc = (float)__builtin_bit_cast(half2v, sg[q >> 1])[q & 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, p[e], acc[e]);
-    }
+    for (int e = 0; e < 4; ++e) acc[e] *= back;
+  } else {
+    groups(std::false_type{});
   }
   // lane (r, g) holds rows 4 g .. 4 g + 3 of column n
   if (n >= N) return;

@@ -227,6 +227,62 @@ def test_sliced_few_row_parity(M, N, K):
     assert_parity(yb, y_ref, t, RTOL, bf16_half_ulp(y_ref), what=f"sliced bf16 M={M}")
 
 
+@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("kind", ["normal", "huge", "tiny", "zero_rows", "wide", "subnormal",
+                                  "rows_apart"])
+def test_sliced_few_row_activation_ranges(M, kind):
+    """The sliced kernel takes fp16 operands when a slice's nonzero
+    activations span at most 2^29 (scaled by one power of two: by about
+    2^-100 for "huge", 2^100 for "tiny", not at all for "normal" and
+    "zero_rows") and exact bf16 ones otherwise ("wide": a value 2^63 times
+    the rest; "subnormal"; "rows_apart": one row 2^40 below the others).
+    Either way the bar is exact-weight parity, and zero rows give zero."""
+    N, K = 300, 4096
+    d = synthetic.dense_case(6960 + M, M, N, K)
+    x = d.x.copy()
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    if kind == "huge":
+        x = synthetic.f32_to_bf16_bits(xf * np.float32(2.0 ** 100))
+    elif kind == "tiny":
+        x = synthetic.f32_to_bf16_bits(xf * np.float32(2.0 ** -100))
+    elif kind == "zero_rows":
+        x[1::2] = 0
+    elif kind == "wide":
+        x[:, 7] = 0x5F00            # ~9.2e18 next to O(1) values
+    elif kind == "subnormal":
+        x[:, 100] = 0x0003
+    elif kind == "rows_apart":
+        x[M - 1] = synthetic.f32_to_bf16_bits(xf[M - 1] * np.float32(2.0 ** -40))
+    assert q4.q4_matmul_workspace_bytes(M, N, K) == 4 * M * N * 4
+    y_ref, t = oracle.matmul(x, d.w_q, d.w_s)
+    y = matmul_ex(x, d.w_q, d.w_s, F32)
+    assert_parity(y, y_ref, t, RTOL, what=f"sliced {kind} M={M}")
+    for m in range(M):
+        if not x[m].any():
+            assert np.all(y[m] == 0)
+
+
+def test_sliced_few_row_two_spikes():
+    """Unit scales and two nonzero activations per row: the sliced kernel's
+    result is the oracle's double result rounded to fp32 within one fp32 ulp
+    (one MFMA sum and at most one fp32 addition per slice and in the
+    combine), on both operand paths: spreads up to 2^29 take fp16 operands,
+    2^30 and more the bf16 ones."""
+    M, N, K = 4, 130, 4096
+    d = synthetic.dense_case(6970, M, N, K)
+    w_s = np.full_like(d.w_s, 0x3C00)                       # 1.0
+    rng = np.random.default_rng(13)
+    for a in (60, 15, 0, -14, -60):
+        for spread in (0, 28, 29, 30, 45):
+            x = np.stack([_two_spikes(K, k0, k1, a, spread, rng)
+                          for k0, k1 in ((96, 100), (100, 101), (100, 2100), (17, K - 20))])
+            y = matmul_ex(x, d.w_q, w_s, F32)
+            y_ref, _ = oracle.matmul(x, d.w_q, w_s)
+            want = y_ref.astype(np.float32).astype(np.float64)
+            ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+            assert np.all(np.abs(y - want) <= ulp), f"a={a} spread={spread}"
+
+
 def test_small_split_deterministic_and_workspace_reuse():
     M, N, K = 4, 300, 17408
     d = synthetic.dense_case(6950, M, N, K)
