@@ -348,7 +348,8 @@ class RmsDense:
 
 class SbDense:
     """q4_sb_matmul on a dense shape: codes with two-level (super-block)
-    scales, expanded to fp32 block scales in the workspace, then the product."""
+    scales; the decode shape reads them as stored, the prefill shape expands
+    them to fp32 block scales in the workspace first."""
 
     def __init__(self, torch, q4, name, copies=None):
         import synthetic

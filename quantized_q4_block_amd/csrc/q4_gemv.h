@@ -429,6 +429,17 @@ enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2 };
 // SC: how a block scale is held -- _Float16 (the int4 codes' fp16 scales),
 // float (exact fp32 block scales, e.g. expanded from super-block scales) or
 // uint8_t (the E8M0 bytes of 4-bit float blocks).
+// Super-block scales held as loaded: the fp16 scale d of the block's
+// 256-element super-block and the block's 8-bit multiplier; the block scale
+// d * m has at most 19 significant bits and is formed exactly in fp32.
+struct SbScale {
+  _Float16 d;
+  uint8_t m;
+  __device__ __forceinline__ SbScale() : d((_Float16)0.0f), m(0) {}
+  __device__ __forceinline__ explicit SbScale(float) : d((_Float16)0.0f), m(0) {}
+  __device__ __forceinline__ operator float() const { return (float)d * (float)m; }
+};
+
 template <int R, int FULL, int TAIL, typename SC = _Float16>
 struct UpfrontLoads {
   static constexpr int TR = TAIL == kSplitTail ? R / 2 : (TAIL == kWideTail ? R : 0);
@@ -501,6 +512,57 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL, SC>& b,
     const uint32_t t = (uint32_t)(lane < rem ? lane : 0);
 #pragma unroll
     for (int r = 0; r < R; ++r) load(r, (uint32_t)(FULL * kWave), t, b.ct[r], b.st[r]);
+  }
+}
+
+// The same for super-block scales, whole rows only (the piece starts at
+// block 0, so lane l's block st * 64 + l lies in super-block st * 8 + l / 8):
+// dbase and mbase are the task's first row's super-block scales and block
+// multipliers; row_d = K/256 scales per row.
+template <int R, int FULL, int TAIL>
+__device__ __forceinline__ void upfront_load_sb(UpfrontLoads<R, FULL, TAIL, SbScale>& b,
+                                                const uint8_t* __restrict__ cbase,
+                                                const uint16_t* __restrict__ dbase,
+                                                const uint8_t* __restrict__ mbase,
+                                                uint32_t row_bytes, uint32_t row_sc, int room,
+                                                int rem, int lane) {
+  const uint32_t row_d = row_sc / 8;
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(cbase, ((uint32_t)room + 1) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(mbase, ((uint32_t)room + 1) * row_sc);
+  const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dbase, ((uint32_t)room + 1) * row_d * 2u);
+  auto load = [&](uint32_t row, uint32_t blk, uint32_t lane_blk, uint4& c, SbScale& s) {
+    c = buffer_codes(rc, lane_blk * 16u, row * row_bytes + blk * 16u);
+    s.m = __builtin_amdgcn_raw_buffer_load_b8(rm, lane_blk, row * row_sc + blk, 2);
+    s.d = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+                                           rd, (lane_blk >> 3) * 2u, (row * row_d + blk / 8) * 2u, 2));
+  };
+#pragma unroll
+  for (int st = 0; st < FULL; ++st)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      load((uint32_t)(r < room ? r : room), (uint32_t)(st * kWave), (uint32_t)lane, b.c[st][r],
+           b.s[st][r]);
+  if constexpr (TAIL == kSplitTail) {
+    constexpr int H = R / 2;
+    const int sub = lane & 31, half = lane >> 5;
+    const uint32_t t = (uint32_t)(sub < rem ? sub : 0);
+    const uint32_t blk = (uint32_t)(FULL * kWave);
+    // the two half-waves read different rows: the row offset is per lane
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      int row = half * H + j;
+      row = row < room ? row : room;
+      b.ct[j] = buffer_codes(rc, (uint32_t)row * row_bytes + t * 16u, blk * 16u);
+      b.st[j].m = __builtin_amdgcn_raw_buffer_load_b8(rm, (uint32_t)row * row_sc + t, blk, 2);
+      b.st[j].d = __builtin_bit_cast(
+          _Float16, __builtin_amdgcn_raw_buffer_load_b16(
+                        rd, ((uint32_t)row * row_d + (t >> 3)) * 2u, (blk / 8) * 2u, 2));
+    }
+  } else if constexpr (TAIL == kWideTail) {
+    const uint32_t t = (uint32_t)(lane < rem ? lane : 0);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      load((uint32_t)(r < room ? r : room), (uint32_t)(FULL * kWave), t, b.ct[r], b.st[r]);
   }
 }
 

@@ -77,8 +77,14 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
     const SP* __restrict__ ws, void* __restrict__ y, int y_bf16, int64_t N, int64_t K,
     int rem, int64_t ld_blocks, int slice0, int slice_blocks, float* __restrict__ partial,
-    const uint16_t* __restrict__ gamma = nullptr, float eps = 0.0f) {
-  using SC = typename std::conditional<std::is_same<SP, float>::value, float, _Float16>::type;
+    const uint16_t* __restrict__ gamma = nullptr, float eps = 0.0f,
+    const uint16_t* __restrict__ sb_d = nullptr) {
+  // SP: the block scales' storage -- uint16_t (fp16), float (exact fp32) or
+  // uint8_t (super-block multipliers, with the fp16 super-block scales in
+  // sb_d; whole rows only)
+  using SC = typename std::conditional<
+      std::is_same<SP, float>::value, float,
+      typename std::conditional<std::is_same<SP, uint8_t>::value, SbScale, _Float16>::type>::type;
   constexpr int R = kLdsRows;
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[M * S * 8 * kWave];
@@ -104,9 +110,14 @@ __global__ __launch_bounds__(kLdsWaves * 64) void gemv_lds_kernel(
   XStager<1, S, kLdsWaves * 64> gst;
   if constexpr (NORM) gst.load(gamma, K, 0);
   UpfrontLoads<R, FULL, TAIL, SC> b;
-  upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes + blk0 * 16,
-                              ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
-                              lane, (uint32_t)(ld_blocks - blk0));
+  if constexpr (std::is_same<SC, SbScale>::value)
+    upfront_load_sb<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes,
+                                   sb_d + nl * (int64_t)(row_sc / 8), ws + nl * (int64_t)row_sc,
+                                   row_bytes, row_sc, room, rem, lane);
+  else
+    upfront_load<R, FULL, TAIL>(b, wq + nl * (int64_t)row_bytes + blk0 * 16,
+                                ws + nl * (int64_t)row_sc + blk0, row_bytes, row_sc, room, rem,
+                                lane, (uint32_t)(ld_blocks - blk0));
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.pin();
   __shared__ double red[NORM ? M : 1][kLdsWaves];
@@ -308,11 +319,13 @@ hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* gamma, float eps,
   return launch_norm_m<2>(x, gamma, eps, wq, ws, y, y_bf16, N, K, stream);
 }
 
-// The matrix-vector kernel with exact fp32 block scales [N][K/32] (M <= 2,
-// whole rows that fit its LDS staging: gemv_norm_fits).
+// The matrix-vector kernel with super-block scales read as stored (fp16 d
+// per 256 k, 8-bit multipliers per 32 k; M <= 2, whole rows that fit its LDS
+// staging: gemv_norm_fits, K a multiple of 256).
 template <int M>
-static hipError_t launch_f32s_m(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
-                                bool y_bf16, int64_t N, int64_t K, hipStream_t stream) {
+static hipError_t launch_sb_m(const uint16_t* x, const uint8_t* wq, const uint16_t* wd,
+                              const uint8_t* wsc, void* y, bool y_bf16, int64_t N, int64_t K,
+                              hipStream_t stream) {
   const int rem = row_leftover(K);
   const int64_t bpr = K / kBlock;
   return dispatch_row_geometry(K, [&](auto full, auto tail) {
@@ -320,18 +333,19 @@ static hipError_t launch_f32s_m(const uint16_t* x, const uint8_t* wq, const floa
     const int64_t tasks = (N + kLdsRows - 1) / kLdsRows;
     const int64_t grid = (tasks + kLdsWaves - 1) / kLdsWaves;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemv_lds_kernel<M, FULL, TAIL, false, float>
+    gemv_lds_kernel<M, FULL, TAIL, false, uint8_t>
         <<<dim3((unsigned)grid), dim3(kLdsWaves * 64), 0, stream>>>(
-            x, wq, ws, y, y_bf16 ? 1 : 0, N, K, rem, bpr, 0, 0, nullptr);
+            x, wq, wsc, y, y_bf16 ? 1 : 0, N, K, rem, bpr, 0, 0, nullptr, nullptr, 0.0f, wd);
     return hipGetLastError();
   });
 }
 
-hipError_t launch_gemv_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
-                            bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (!gemv_norm_fits(M, K)) return hipErrorInvalidValue;
-  if (M == 1) return launch_f32s_m<1>(x, wq, ws, y, y_bf16, N, K, stream);
-  return launch_f32s_m<2>(x, wq, ws, y, y_bf16, N, K, stream);
+hipError_t launch_gemv_sb(const uint16_t* x, const uint8_t* wq, const uint16_t* wd,
+                          const uint8_t* wsc, void* y, bool y_bf16, int64_t M, int64_t N,
+                          int64_t K, hipStream_t stream) {
+  if (!gemv_norm_fits(M, K) || K % 256 != 0) return hipErrorInvalidValue;
+  if (M == 1) return launch_sb_m<1>(x, wq, wd, wsc, y, y_bf16, N, K, stream);
+  return launch_sb_m<2>(x, wq, wd, wsc, y, y_bf16, N, K, stream);
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* wq, const uint16_t* ws, void* y,

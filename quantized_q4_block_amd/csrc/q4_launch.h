@@ -111,11 +111,14 @@ hipError_t launch_moe_noalloc(const uint16_t* x, const uint8_t* wq, const uint16
                               const int32_t* ids, const float* gates, float* y, int64_t T,
                               int64_t topk, int64_t E, int64_t N, int64_t K, hipStream_t stream);
 
+// Super-block scales read as stored (fp16 d [N][K/256], 8-bit multipliers
+// [N][K/32]), M <= 2, whole rows that gemv_norm_fits, K a multiple of 256.
+hipError_t launch_gemv_sb(const uint16_t* x, const uint8_t* wq, const uint16_t* wd,
+                          const uint8_t* wsc, void* y, bool y_bf16, int64_t M, int64_t N,
+                          int64_t K, hipStream_t stream);
+
 // The int4 kernels with exact fp32 block scales [N][K/32] in place of fp16
-// ones (super-block scales expanded): matrix-vector (M <= 2, whole rows that
-// fit gemv_norm_fits), few-row and tiled forms.
-hipError_t launch_gemv_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
-                            bool y_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+// ones (super-block scales expanded): few-row and tiled forms.
 hipError_t launch_small_f32s(const uint16_t* x, const uint8_t* wq, const float* ws, void* y,
                              bool y_bf16, int64_t M, int64_t N, int64_t K, float* partial,
                              hipStream_t stream);

@@ -6,12 +6,13 @@
 // Identity", "Policy Resolution"), on this library's 4-bit codes.
 //
 // d * sc has at most 19 significant bits, so every block scale is exact in
-// fp32.  A small kernel writes those scales into the caller's workspace
-// (N * K/32 floats: 4 bytes per 32 weights, read back once by the product),
-// then the int4 kernels run with fp32 block scales in place of fp16 ones:
-// the matrix-vector kernel for M <= 2 (whole rows up to K = 8192), the
-// few-row matrix-core kernel, or the tiled kernel -- weights exact on every
-// path, as for the base format.
+// fp32.  The matrix-vector kernel (M <= 2, whole rows up to K = 8192) reads
+// d and sc as stored and forms each block scale in fp32 as it uses it.  For
+// the other shapes a small kernel writes the fp32 scales into the caller's
+// workspace (N * K/32 floats, read back once by the product), then the
+// few-row matrix-core kernel or the tiled kernel runs with fp32 block scales
+// in place of fp16 ones -- weights exact on every path, as for the base
+// format.
 #include "../../include/q4.h"
 #include "q4_device.h"
 #include "q4_launch.h"
@@ -44,6 +45,9 @@ hipError_t launch_sb_matmul(const uint16_t* x, const uint8_t* wq, const uint16_t
                             const uint8_t* wsc, void* y, bool y_bf16, int64_t M, int64_t N,
                             int64_t K, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
+  // matrix-vector shapes whose rows fit the decode kernel read the scales as
+  // stored (1.25 instead of 4 bytes per 32 weights, and no expansion)
+  if (gemv_norm_fits(M, K)) return launch_gemv_sb(x, wq, wd, wsc, y, y_bf16, M, N, K, stream);
   float* s = static_cast<float*>(workspace);
   // the super-blocks of all rows are consecutive: d [N][K/256] and sc
   // [N][K/32] share the index n * K/256 + j (eight multipliers per j)
@@ -55,7 +59,6 @@ hipError_t launch_sb_matmul(const uint16_t* x, const uint8_t* wq, const uint16_t
       wd, reinterpret_cast<const uint2*>(wsc), reinterpret_cast<float4*>(s), (uint32_t)n_super);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (gemv_norm_fits(M, K)) return launch_gemv_f32s(x, wq, s, y, y_bf16, M, N, K, stream);
   // the rest of the workspace, if large enough, lets the tiled product cut K
   const size_t sb = sb_scale_bytes(N, K);
   const size_t need = q4_matmul_workspace_bytes(M, N, K);
