@@ -11,7 +11,9 @@
 //     exclusive-scan the counts, list the experts that got any pair, and
 //     bucket the pair indices by expert (counting in LDS when the experts
 //     fit, else in the workspace).  Everything it writes is rebuilt from
-//     scratch on every call (the workspace needs no clearing).
+//     scratch on every call (the workspace needs no clearing).  With at
+//     most 64 pairs over at most 256 experts the plain routed product skips
+//     it: each of its wavefronts finds its expert's pairs from the ids.
 //  2. gathered matrix-vector product: one workgroup per (touched expert,
 //     16 weight rows).  Each wavefront issues every code and scale load of
 //     its 2 rows once, then runs the expert's tokens one after another
@@ -37,6 +39,12 @@ constexpr int kRowsPerWg = 64;     // weight rows per workgroup (16 per wavefron
 constexpr int kRowsPerWave = 16;
 constexpr int kMaxTok = 8;         // tokens per gathered pass
 constexpr int kPrepLdsExperts = 4096;   // experts counted in LDS by the prep kernel
+// At most this many routed pairs (one per lane of a wavefront) over at most
+// this many experts take the plain routed product without the prep kernel.
+// (The routed FFN keeps the prep: its two products would each pay the
+// direct form's longer prologue, which costs more than the launch saved.)
+constexpr int kMoeDirectPairs = 64;
+constexpr int kMoeDirectExperts = 256;   // 1 KB owner table per wavefront
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 }  // namespace
@@ -266,28 +274,74 @@ enum MoeRows { kRowsPlain = 0, kRowsGlu = 1, kRowsDown = 2 };
 // Rows per wavefront task when a row is at most one stage (K <= 2048).
 constexpr int kMoeShortRows = Q4_MOE_SHORT_ROWS;
 
-template <int FULL, int TAIL, int MODE, int RT>
+//
+// DIRECT (at most 64 routed pairs, E <= kMoeDirectExperts): no routing
+// tables.  Every wavefront loads the pairs' expert ids, one per lane (ids
+// outside [0, E) take no part, as the prep would drop them), and in an LDS
+// table of its own takes the atomic min of the lane index at each id: the
+// lowest lane holding each touched expert becomes its representative (the
+// same in every wavefront and workgroup).  grid.y picks the slot-th
+// representative (a workgroup past the last returns before loading anything
+// else), and a ballot of id == e gives the expert's pairs in ascending
+// order.  Which slot serves an expert decides no result.  Otherwise grid.y
+// is a slot of the active-expert list the prep kernel built.
+template <int FULL, int TAIL, int MODE, int RT, bool DIRECT = false>
 __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
     const void* __restrict__ xv, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ ws, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ order,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
     const float* __restrict__ gates, float* __restrict__ partial, int64_t topk, int64_t N,
-    int64_t K, int rem) {
+    int64_t K, int rem, const int32_t* __restrict__ ids = nullptr, int P = 0, int E = 0) {
   constexpr int R = RT;
   static_assert(MODE != kRowsGlu || R == 2, "a gate/up pair is one wavefront task");
   constexpr int S = FULL + (TAIL != kNoTail ? 1 : 0);
   __shared__ float4 xs[S * 8 * kWave];
-  const int slot = blockIdx.y;
-  // the active count and this slot's expert in one round trip (grid.y is the
-  // length of the active list, so the read is in bounds)
-  const int na = *num_active;
-  const int32_t e = active[slot];
-  asm volatile("" :: "s"(e), "s"(na));
-  if (slot >= na) return;                          // whole workgroup
-  const int32_t start = offsets[e];
-  const int32_t cnt = counts[e];
+  __shared__ uint32_t owner[DIRECT ? kLdsWaves : 1][DIRECT ? kMoeDirectExperts : 1];
   const int lane = threadIdx.x & 63;
+  int32_t e, start = 0, cnt;
+  uint64_t pairs = 0;   // DIRECT: the expert's pairs not yet taken (wave-uniform)
+  if constexpr (DIRECT) {
+    const int32_t id = lane < P ? ids[lane] : -1;
+    const bool valid = id >= 0 && id < E;
+    // the wavefront's own table: each step completes (lgkmcnt 0) before the
+    // next is issued, so no workgroup barrier is needed
+    uint32_t* own = owner[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+    if (valid) own[id] = 0xFFFFFFFFu;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (valid) atomicMin(&own[id], (uint32_t)lane);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const bool rep = valid && own[id] == (uint32_t)lane;
+    const uint64_t reps = __ballot(rep);
+    const int slot = blockIdx.y;
+    if (slot >= __builtin_popcountll(reps)) return;   // whole workgroup
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+        (uint32_t)(reps >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)reps, 0u));
+    const int src = __builtin_ctzll(__ballot(rep && below == (uint32_t)slot));
+    e = __builtin_amdgcn_readlane(id, src);
+    pairs = __ballot(id == e);
+    cnt = __builtin_popcountll(pairs);
+  } else {
+    const int slot = blockIdx.y;
+    // the active count and this slot's expert in one round trip (grid.y is
+    // the length of the active list, so the read is in bounds)
+    const int na = *num_active;
+    e = active[slot];
+    asm volatile("" :: "s"(e), "s"(na));
+    if (slot >= na) return;                        // whole workgroup
+    start = offsets[e];
+    cnt = counts[e];
+  }
+  // next pair of the expert, in order
+  auto next_pair = [&](int32_t i) __attribute__((always_inline)) -> int32_t {
+    if constexpr (DIRECT) {
+      const int32_t q = (int32_t)__builtin_ctzll(pairs);
+      pairs &= pairs - 1;
+      return q;
+    } else {
+      return order[start + i];
+    }
+  };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n0 = ((int64_t)blockIdx.x * kLdsWaves + wave) * R;
   const bool live = n0 < N;
@@ -311,13 +365,13 @@ __global__ __launch_bounds__(kLdsWaves * 64) void moe_lds_kernel(
   upfront_load<R, FULL, TAIL>(b, wq_e + nl * (int64_t)row_bytes, ws_e + nl * (int64_t)row_sc,
                               row_bytes, row_sc, room, rem, lane, row_sc);
   __builtin_amdgcn_sched_barrier(0);
-  int32_t p = order[start];   // an active expert has at least one pair
+  int32_t p = next_pair(0);   // an active expert has at least one pair
   stage(p);
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the staging
   xst.pin();
   for (int32_t i = 0; i < cnt; ++i) {
     if (i > 0) {
-      p = order[start + i];
+      p = next_pair(i);
       stage(p);
       __syncthreads();                             // xs no longer read
     }
@@ -411,13 +465,19 @@ hipError_t moe_prep(const int32_t* ids, int64_t P, int64_t E, const MoeBuffers& 
   return hipGetLastError();
 }
 
+bool moe_direct(int64_t P, int64_t E, int64_t K) {
+  return P <= kMoeDirectPairs && E <= kMoeDirectExperts && x_stages(K) <= kLdsMaxStages;
+}
+
 // One gathered product over every touched expert (LDS kernel; rows of at
-// most kLdsMaxStages stages).
+// most kLdsMaxStages stages).  ids != NULL: the DIRECT form (grid.y = E,
+// no prep); otherwise over the prep's active list (grid.y = max_active).
 template <int MODE>
 hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
                          const MoeBuffers& b, float* out, int64_t topk, int64_t N, int64_t K,
                          int64_t max_active, hipStream_t stream,
-                         const float* gates = nullptr) {
+                         const float* gates = nullptr, const int32_t* ids = nullptr,
+                         int64_t P = 0, int64_t E = 0) {
   const int rem = row_leftover(K);
   return dispatch_row_geometry(K, [&](auto full, auto tail) {
     constexpr int FULL = decltype(full)::value;
@@ -427,6 +487,14 @@ hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
     constexpr int RT = (MODE != kRowsGlu && FULL == 0) ? kMoeShortRows : kLdsRows;
     const int64_t row_blocks = (N + kLdsWaves * RT - 1) / (kLdsWaves * RT);
     if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (ids != nullptr) {
+      const int64_t slots = P < E ? P : E;
+      moe_lds_kernel<FULL, decltype(tail)::value, MODE, RT, true>
+          <<<dim3((unsigned)row_blocks, (unsigned)slots), dim3(kLdsWaves * 64), 0, stream>>>(
+              x, wq, ws, nullptr, nullptr, nullptr, nullptr, nullptr, gates, out, topk, N, K, rem,
+              ids, (int)P, (int)E);
+      return hipGetLastError();
+    }
     const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
     moe_lds_kernel<FULL, decltype(tail)::value, MODE, RT>
         <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, b.counts, b.offsets, b.order,
@@ -456,6 +524,12 @@ hipError_t launch_moe(const uint16_t* x, const uint8_t* wq, const uint16_t* ws,
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.partial);
   const int64_t P = T * topk;
   const int64_t max_active = P < E ? P : E;
+  if (max_active > 0 && !moe_use_grouped(P, E) && moe_direct(P, E, K)) {
+    const hipError_t err = moe_stage_lds<kRowsPlain>(x, wq, ws, b, partial, topk, N, K, 0,
+                                                     stream, nullptr, ids, P, E);
+    if (err != hipSuccess) return err;
+    return moe_combine(ids, gates, partial, y, T, topk, E, N, stream);
+  }
   hipError_t err = moe_prep(ids, P, E, b, stream);
   if (err != hipSuccess) return err;
   if (max_active > 65535) return hipErrorInvalidValue;

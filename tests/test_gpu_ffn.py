@@ -27,10 +27,13 @@ def _check(y, y_ref, b, what):
 
 
 # H and F of 1 to 4 stages (64 blocks each), whole and with leftovers of
-# one block or more; experts shared by several tokens and single ones.
+# one block or more; experts shared by several tokens and single ones.  Few
+# pairs per expert: the per-token product over the prep's buckets; (8, 8,
+# 16, ...) and (9, 4, 5, ...): the grouped product.
 @pytest.mark.parametrize("T,topk,E,H,F", [(1, 1, 1, 64, 32), (5, 3, 4, 96, 64),
                                           (8, 8, 16, 256, 160), (3, 2, 6, 1024 + 32, 2048 + 32),
                                           (4, 2, 3, 8192, 64), (2, 2, 3, 64, 8192),
+                                          (40, 2, 64, 1024 + 32, 96),
                                           (9, 4, 5, 2048, 4096 + 96)])
 def test_moe_ffn_parity_shapes(T, topk, E, H, F):
     c = synthetic.moe_ffn_case(8000 + T + H + F, T, topk, E, H, F)
@@ -74,6 +77,7 @@ def test_moe_ffn_deterministic_and_workspace_reuse():
 # oracle result within the same bar, on the per-token path (few pairs per
 # expert) and on the grouped path (many), with repeated and invalid ids.
 @pytest.mark.parametrize("T,topk,E,H,F", [(5, 3, 4, 96, 64), (8, 8, 16, 256, 160),
+                                          (40, 2, 64, 256, 160),
                                           (40, 2, 3, 256, 160), (33, 8, 16, 1024 + 32, 512 + 96)])
 def test_moe_ffn_weighted_down(T, topk, E, H, F):
     c = synthetic.moe_ffn_case(8300 + T + H + F, T, topk, E, H, F)

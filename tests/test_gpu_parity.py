@@ -656,12 +656,16 @@ def test_moe_config_full():
     assert_parity(y, y_ref, t, RTOL, what="moe")
 
 
-# Up to 512 (token, slot) pairs the expert workgroups find their pairs
-# themselves; (80, 8, ...) has 640 pairs and goes through the prep kernel;
-# K = 8192 + 32 (more than 4 stages) takes the chunked global-activation
-# kernel.
+# Up to 64 (token, slot) pairs with few pairs per expert over at most 256
+# experts, the expert workgroups find their pairs from the ids themselves (no
+# prep kernel); (40, 2, 64, ...) has 80 pairs and (4, 2, 300, ...) 300
+# experts, and both take the prep kernel's buckets; (64, 2, 4, ...) and (80,
+# 8, 16, ...) have many pairs per expert and take the grouped matrix-core
+# product; K = 8192 + 32 (more than 4 stages) takes the chunked
+# global-activation kernel.
 @pytest.mark.parametrize("T,topk,E,N,K", [(1, 1, 1, 33, 64), (5, 3, 4, 100, 256),
                                           (64, 2, 4, 96, 512), (3, 4, 50, 70, 2048 + 32),
+                                          (40, 2, 64, 96, 1024 + 32), (4, 2, 300, 40, 256),
                                           (80, 8, 16, 40, 256), (4, 2, 6, 20, 8192 + 32)])
 def test_moe_parity_shapes(T, topk, E, N, K):
     m = synthetic.moe_case(6000 + T + E, T, topk, E, N, K)
