@@ -492,11 +492,13 @@ DECODE_KERNEL = "q4::gemv_lds_kernel<1, 2, 1, false, unsigned short>"
 CLOCK_WARM_MS = 60.0
 
 
-def time_steps(torch, work, steps, warmup, warm_ms=0.0):
+def time_steps(torch, work, steps, warmup, warm_ms=0.0, blocks=0, spread=None):
     """Host-timed steps (synchronised on both sides) and HIP-event time over
     the same region on the launch stream.  `warmup` untimed steps first, and
     before them, if warm_ms > 0, untimed steps until the GPU has run this
-    work for warm_ms."""
+    work for warm_ms.  With blocks > 1, events also split the timed steps
+    into that many equal blocks, and `spread` (a list) receives each block's
+    event time per step (ms)."""
     stream = torch.cuda.current_stream()
     h = ctypes.c_void_p(stream.cuda_stream)
     done, i = 0.0, 0
@@ -516,13 +518,23 @@ def time_steps(torch, work, steps, warmup, warm_ms=0.0):
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    per = steps // blocks if blocks > 1 else 0
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(blocks - 1)] if per else []
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(steps):
+        if per and i and i % per == 0 and i // per <= len(marks):
+            marks[i // per - 1].record(stream)
         work.step(warmup + i, h)
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if per and spread is not None:
+        edges = [e0] + marks
+        for b in range(len(edges)):
+            end = edges[b + 1] if b + 1 < len(edges) else e1
+            n = per if b + 1 < len(edges) else steps - per * len(marks)
+            spread.append(edges[b].elapsed_time(end) / n)
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
@@ -782,7 +794,9 @@ def main():
     progress("decode_gate_up: generating inputs")
     head = Dense(torch, q4, "decode_gate_up")
     progress(f"decode_gate_up: timing {args.steps} steps over {head.copies} weight copies")
-    ms_step, ev_ms = time_steps(torch, head, args.steps, args.warmup, CLOCK_WARM_MS)
+    blocks_ms = []
+    ms_step, ev_ms = time_steps(torch, head, args.steps, args.warmup, CLOCK_WARM_MS,
+                                blocks=10 if args.steps >= 100 else 0, spread=blocks_ms)
     copies = head.copies
     progress("decode_gate_up: sampling the shader clock under load")
     sclk = sample_sclk(torch, head)
@@ -796,6 +810,12 @@ def main():
             "kernel": DECODE_KERNEL,
             "avg_launch_us": round(ev_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": head.wbytes}
+    if blocks_ms:
+        # the timed launches in 10 consecutive blocks: each block's mean
+        us = sorted(b * 1e3 for b in blocks_ms)
+        roof["launch_us_over_blocks"] = {"blocks": len(us), "min": round(us[0], 3),
+                                         "median": round(float(np.median(us)), 3),
+                                         "max": round(us[-1], 3)}
     del head
     torch.cuda.empty_cache()
 
