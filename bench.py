@@ -86,6 +86,16 @@ def git_commit():
     return r.stdout.strip() or None if r.returncode == 0 else None
 
 
+def library_build_info():
+    """The commit the loaded library was built from and whether its sources
+    differed from it (written by the build), or None."""
+    try:
+        with open(os.path.join(ROOT, "quantized_q4_block_amd", "build_info.json")) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
 def kernel_resources(mangled_prefix):
     """Register, LDS and occupancy figures the compiler reported for the
     kernel whose mangled name starts with mangled_prefix (written by the
@@ -954,6 +964,7 @@ def main():
         "env": {"device": torch.cuda.get_device_properties(0).gcnArchName,
                 "hip_runtime": torch.version.hip, "torch": torch.__version__,
                 "sclk_mhz_under_load": sclk, "commit": git_commit(),
+                "library_built_from": library_build_info(),
                 "sources_digest": all_sources_digest(),
                 "decode_kernel_resources": kernel_resources(
                     "_ZN2q415gemv_lds_kernelILi1ELi2ELi1ELb0EtEE")},

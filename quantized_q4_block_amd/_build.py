@@ -68,6 +68,26 @@ def _compile(src: str):
     return obj, _resources(r.stderr)
 
 
+# The commit the library is built from, and whether the kernel sources or
+# the C ABI header differed from it at build time, for run records made
+# where the tree carries no git metadata.
+BUILD_INFO = os.path.join(PKG, "build_info.json")
+
+
+def _build_info() -> dict:
+    def git(*args):
+        r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True,
+                           timeout=20)
+        return r.stdout.strip() if r.returncode == 0 else None
+    try:
+        head = git("rev-parse", "HEAD")
+        status = git("status", "--porcelain", "--", "quantized_q4_block_amd/csrc", "include")
+    except (OSError, subprocess.SubprocessError):
+        head, status = None, None
+    return {"commit": head or None,
+            "sources_modified": None if head is None or status is None else status != ""}
+
+
 def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
@@ -85,6 +105,9 @@ def build(jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(BUILD_INFO, "w") as f:
+        json.dump(_build_info(), f, indent=1, sort_keys=True)
+        f.write("\n")
     return LIB
 
 

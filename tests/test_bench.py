@@ -148,3 +148,22 @@ def test_counters_table_derived_figures(tmp_path):
     assert line[1:5] == ["64", "100", "3", "50.0%"]
     assert float(line[-2]) == round(1000 * 1024 * 2 / 1e6, 1)
     assert float(line[-1]) == round(500 * 1024 / 1e6, 2)
+
+
+def test_build_records_its_commit(tmp_path, monkeypatch):
+    spec = importlib.util.spec_from_file_location(
+        "q4_build", os.path.join(ROOT, "quantized_q4_block_amd", "_build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    info = b._build_info()
+    assert set(info) == {"commit", "sources_modified"}
+    if info["commit"] is not None:    # a git checkout
+        assert len(info["commit"]) == 40 and isinstance(info["sources_modified"], bool)
+    # bench reads the record the build wrote, and copes with its absence
+    bench = _bench()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.library_build_info() is None
+    (tmp_path / "quantized_q4_block_amd").mkdir()
+    (tmp_path / "quantized_q4_block_amd" / "build_info.json").write_text(
+        '{"commit": "abc", "sources_modified": true}')
+    assert bench.library_build_info() == {"commit": "abc", "sources_modified": True}
