@@ -418,13 +418,26 @@ struct XStagerF32 {
 // ---------------------------------------------------------------------------
 // One task of R rows with the activations in LDS and every code and scale
 // load issued up front, for rows of FULL whole stages plus a leftover stage
-// of kind TAIL (none, split between the half-waves, or one block per lane).
+// of kind TAIL (none, split between the half-waves, one block per lane, or
+// -- rows of a single leftover stage of at most 48 blocks, 4 rows a task --
+// the 4 rows' blocks laid end to end over the lanes in three passes, so no
+// lane idles when a row has 48 blocks).
 //
 // Split in two so a kernel can issue the loads before it stages the
 // activations: the LDS staging and its barrier then overlap the loads'
 // HBM latency.  Rows past the last one are read as the last row (in
 // bounds); the caller discards their results.
-enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2 };
+enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2, kFlatTail = 3 };
+constexpr int kFlatRows = 4, kFlatPasses = 3, kFlatMaxBlocks = kFlatPasses * kWave / kFlatRows;
+
+// Slot t of lane l in the flat layout: block l + 64 t of the rows laid end to
+// end, i.e. block blk of task row row (row = kFlatRows past the last slot).
+__device__ __forceinline__ void flat_slot(int lane, int t, int rem, int& row, int& blk) {
+  const int j = lane + kWave * t;
+  row = (j >= rem) + (j >= 2 * rem) + (j >= 3 * rem) + (j >= 4 * rem);
+  blk = j - (row < kFlatRows ? row : 0) * rem;
+  if (row == kFlatRows) blk = 0;
+}
 
 // SC: how a block scale is held -- _Float16 (the int4 codes' fp16 scales),
 // float (exact fp32 block scales, e.g. expanded from super-block scales) or
@@ -442,7 +455,11 @@ struct SbScale {
 
 template <int R, int FULL, int TAIL, typename SC = _Float16>
 struct UpfrontLoads {
-  static constexpr int TR = TAIL == kSplitTail ? R / 2 : (TAIL == kWideTail ? R : 0);
+  static_assert(TAIL != kFlatTail || (FULL == 0 && R == kFlatRows),
+                "the flat layout covers 4 rows of one leftover stage");
+  static constexpr int TR = TAIL == kSplitTail ? R / 2
+                            : TAIL == kWideTail ? R
+                            : TAIL == kFlatTail ? kFlatPasses : 0;
   uint4 c[FULL > 0 ? FULL : 1][R];
   SC s[FULL > 0 ? FULL : 1][R];
   uint4 ct[TR > 0 ? TR : 1];
@@ -512,6 +529,17 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL, SC>& b,
     const uint32_t t = (uint32_t)(lane < rem ? lane : 0);
 #pragma unroll
     for (int r = 0; r < R; ++r) load(r, (uint32_t)(FULL * kWave), t, b.ct[r], b.st[r]);
+  } else if constexpr (TAIL == kFlatTail) {
+    // slots past the rows read row 0's block 0 (in bounds; not added)
+#pragma unroll
+    for (int t = 0; t < kFlatPasses; ++t) {
+      int row, blk;
+      flat_slot(lane, t, rem, row, blk);
+      row = row < kFlatRows ? (row < room ? row : room) : 0;
+      const uint32_t off = (uint32_t)row * row_bytes + (uint32_t)blk * 16u;
+      b.ct[t] = buffer_codes(rc, off, 0u);
+      buffer_scale(rs, ((uint32_t)row * row_sc + (uint32_t)blk) * SZ, 0u, b.st[t]);
+    }
   }
 }
 
@@ -685,6 +713,25 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
 #pragma unroll
       for (int r = 0; r < R; ++r) sc[r] = ok ? b.st[r] : (SC)0.0f;
       rows(FULL, lane, b.ct, sc, acc);
+    }
+  } else if constexpr (TAIL == kFlatTail) {
+    static_assert(!kMx, "the flat layout is built for int4 codes");
+    // each slot's block product goes to its own row (slots past the rows to
+    // none); LDS holds the activations of block blk at position blk
+#pragma unroll
+    for (int t = 0; t < kFlatPasses; ++t) {
+      int row, blk;
+      flat_slot(lane, t, rem, row, blk);
+      float part[1][M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) part[0][m] = 0.0f;
+      const uint4 c1[1] = {b.ct[t]};
+      const SC s1[1] = {b.st[t]};
+      rows(FULL, blk, c1, s1, part);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] += row == r ? part[0][m] : 0.0f;
     }
   }
 #pragma unroll

@@ -487,20 +487,28 @@ hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
     constexpr int RT = (MODE != kRowsGlu && FULL == 0) ? kMoeShortRows : kLdsRows;
     const int64_t row_blocks = (N + kLdsWaves * RT - 1) / (kLdsWaves * RT);
     if (row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (ids != nullptr) {
-      const int64_t slots = P < E ? P : E;
-      moe_lds_kernel<FULL, decltype(tail)::value, MODE, RT, true>
-          <<<dim3((unsigned)row_blocks, (unsigned)slots), dim3(kLdsWaves * 64), 0, stream>>>(
-              x, wq, ws, nullptr, nullptr, nullptr, nullptr, nullptr, gates, out, topk, N, K, rem,
-              ids, (int)P, (int)E);
+    constexpr int TAIL = decltype(tail)::value;
+    auto launch = [&](auto tail_kind) __attribute__((always_inline)) {
+      constexpr int TK = decltype(tail_kind)::value;
+      if (ids != nullptr) {
+        const int64_t slots = P < E ? P : E;
+        moe_lds_kernel<FULL, TK, MODE, RT, true>
+            <<<dim3((unsigned)row_blocks, (unsigned)slots), dim3(kLdsWaves * 64), 0, stream>>>(
+                x, wq, ws, nullptr, nullptr, nullptr, nullptr, nullptr, gates, out, topk, N, K,
+                rem, ids, (int)P, (int)E);
+      } else {
+        moe_lds_kernel<FULL, TK, MODE, RT>
+            <<<dim3((unsigned)row_blocks, (unsigned)max_active), dim3(kLdsWaves * 64), 0,
+               stream>>>(x, wq, ws, b.counts, b.offsets, b.order, b.active, b.num_active, gates,
+                         out, topk, N, K, rem);
+      }
       return hipGetLastError();
-    }
-    const dim3 grid((unsigned)row_blocks, (unsigned)max_active);
-    moe_lds_kernel<FULL, decltype(tail)::value, MODE, RT>
-        <<<grid, dim3(kLdsWaves * 64), 0, stream>>>(x, wq, ws, b.counts, b.offsets, b.order,
-                                                    b.active, b.num_active, gates, out, topk, N,
-                                                    K, rem);
-    return hipGetLastError();
+    };
+    // 4 rows of a single leftover stage of at most 48 blocks: the flat
+    // layout (no idle lanes at 48 blocks)
+    if constexpr (FULL == 0 && TAIL == kWideTail && RT == kFlatRows)
+      if (rem <= kFlatMaxBlocks) return launch(std::integral_constant<int, kFlatTail>{});
+    return launch(std::integral_constant<int, TAIL>{});
   });
 }
 

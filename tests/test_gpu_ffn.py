@@ -34,6 +34,7 @@ def _check(y, y_ref, b, what):
                                           (8, 8, 16, 256, 160), (3, 2, 6, 1024 + 32, 2048 + 32),
                                           (4, 2, 3, 8192, 64), (2, 2, 3, 64, 8192),
                                           (40, 2, 64, 1024 + 32, 96),
+                                          (6, 2, 8, 320, 37 * 32), (5, 3, 8, 224, 48 * 32),
                                           (9, 4, 5, 2048, 4096 + 96)])
 def test_moe_ffn_parity_shapes(T, topk, E, H, F):
     c = synthetic.moe_ffn_case(8000 + T + H + F, T, topk, E, H, F)
@@ -77,7 +78,7 @@ def test_moe_ffn_deterministic_and_workspace_reuse():
 # oracle result within the same bar, on the per-token path (few pairs per
 # expert) and on the grouped path (many), with repeated and invalid ids.
 @pytest.mark.parametrize("T,topk,E,H,F", [(5, 3, 4, 96, 64), (8, 8, 16, 256, 160),
-                                          (40, 2, 64, 256, 160),
+                                          (40, 2, 64, 256, 160), (12, 2, 20, 96, 48 * 32),
                                           (40, 2, 3, 256, 160), (33, 8, 16, 1024 + 32, 512 + 96)])
 def test_moe_ffn_weighted_down(T, topk, E, H, F):
     c = synthetic.moe_ffn_case(8300 + T + H + F, T, topk, E, H, F)

@@ -662,10 +662,12 @@ def test_moe_config_full():
 # experts, and both take the prep kernel's buckets; (64, 2, 4, ...) and (80,
 # 8, 16, ...) have many pairs per expert and take the grouped matrix-core
 # product; K = 8192 + 32 (more than 4 stages) takes the chunked
-# global-activation kernel.
+# global-activation kernel.  K of 37 and 48 blocks: rows of one leftover
+# stage spread over all lanes (without and with the prep).
 @pytest.mark.parametrize("T,topk,E,N,K", [(1, 1, 1, 33, 64), (5, 3, 4, 100, 256),
                                           (64, 2, 4, 96, 512), (3, 4, 50, 70, 2048 + 32),
                                           (40, 2, 64, 96, 1024 + 32), (4, 2, 300, 40, 256),
+                                          (5, 2, 9, 70, 37 * 32), (40, 2, 64, 50, 48 * 32),
                                           (80, 8, 16, 40, 256), (4, 2, 6, 20, 8192 + 32)])
 def test_moe_parity_shapes(T, topk, E, N, K):
     m = synthetic.moe_case(6000 + T + E, T, topk, E, N, K)
