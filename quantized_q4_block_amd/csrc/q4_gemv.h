@@ -419,24 +419,33 @@ struct XStagerF32 {
 // One task of R rows with the activations in LDS and every code and scale
 // load issued up front, for rows of FULL whole stages plus a leftover stage
 // of kind TAIL (none, split between the half-waves, one block per lane, or
-// -- rows of a single leftover stage of at most 48 blocks, 4 rows a task --
-// the 4 rows' blocks laid end to end over the lanes in three passes, so no
-// lane idles when a row has 48 blocks).
+// -- rows of a single leftover stage of at most 48 blocks, a multiple of 4
+// rows a task -- the rows' blocks laid end to end over the lanes, 3 passes
+// per 4 rows, so no lane idles when a row has 48 blocks).
 //
 // Split in two so a kernel can issue the loads before it stages the
 // activations: the LDS staging and its barrier then overlap the loads'
 // HBM latency.  Rows past the last one are read as the last row (in
 // bounds); the caller discards their results.
 enum TailKind { kNoTail = 0, kSplitTail = 1, kWideTail = 2, kFlatTail = 3 };
-constexpr int kFlatRows = 4, kFlatPasses = 3, kFlatMaxBlocks = kFlatPasses * kWave / kFlatRows;
+constexpr int kFlatMaxBlocks = 48;
+template <int R>
+constexpr int flat_passes() { return R * kFlatMaxBlocks / kWave; }
 
-// Slot t of lane l in the flat layout: block l + 64 t of the rows laid end to
-// end, i.e. block blk of task row row (row = kFlatRows past the last slot).
-__device__ __forceinline__ void flat_slot(int lane, int t, int rem, int& row, int& blk) {
-  const int j = lane + kWave * t;
-  row = (j >= rem) + (j >= 2 * rem) + (j >= 3 * rem) + (j >= 4 * rem);
-  blk = j - (row < kFlatRows ? row : 0) * rem;
-  if (row == kFlatRows) blk = 0;
+// Slot t of lane l in the flat layout of R rows of rem blocks: block
+// j = l + 64 t of the rows laid end to end, i.e. block blk of task row row
+// (row = R, blk = 0 past the last slot).  recip = ceil(65536 / rem):
+// (j * recip) >> 16 is j / rem exactly for j < 2^16 / rem (here j < 8 * 48).
+template <int R>
+__device__ __forceinline__ void flat_slot(int lane, int t, int rem, uint32_t recip, int& row,
+                                          int& blk) {
+  const uint32_t j = (uint32_t)(lane + kWave * t);
+  const uint32_t q = (j * recip) >> 16;
+  row = q < (uint32_t)R ? (int)q : R;
+  blk = q < (uint32_t)R ? (int)(j - q * (uint32_t)rem) : 0;
+}
+__host__ __device__ __forceinline__ uint32_t flat_recip(int rem) {
+  return (65536u + (uint32_t)rem - 1u) / (uint32_t)rem;
 }
 
 // SC: how a block scale is held -- _Float16 (the int4 codes' fp16 scales),
@@ -455,11 +464,11 @@ struct SbScale {
 
 template <int R, int FULL, int TAIL, typename SC = _Float16>
 struct UpfrontLoads {
-  static_assert(TAIL != kFlatTail || (FULL == 0 && R == kFlatRows),
-                "the flat layout covers 4 rows of one leftover stage");
+  static_assert(TAIL != kFlatTail || (FULL == 0 && R % 4 == 0),
+                "the flat layout covers a multiple of 4 rows of one leftover stage");
   static constexpr int TR = TAIL == kSplitTail ? R / 2
                             : TAIL == kWideTail ? R
-                            : TAIL == kFlatTail ? kFlatPasses : 0;
+                            : TAIL == kFlatTail ? flat_passes<R>() : 0;
   uint4 c[FULL > 0 ? FULL : 1][R];
   SC s[FULL > 0 ? FULL : 1][R];
   uint4 ct[TR > 0 ? TR : 1];
@@ -531,11 +540,12 @@ __device__ __forceinline__ void upfront_load(UpfrontLoads<R, FULL, TAIL, SC>& b,
     for (int r = 0; r < R; ++r) load(r, (uint32_t)(FULL * kWave), t, b.ct[r], b.st[r]);
   } else if constexpr (TAIL == kFlatTail) {
     // slots past the rows read row 0's block 0 (in bounds; not added)
+    const uint32_t recip = flat_recip(rem);
 #pragma unroll
-    for (int t = 0; t < kFlatPasses; ++t) {
+    for (int t = 0; t < flat_passes<R>(); ++t) {
       int row, blk;
-      flat_slot(lane, t, rem, row, blk);
-      row = row < kFlatRows ? (row < room ? row : room) : 0;
+      flat_slot<R>(lane, t, rem, recip, row, blk);
+      row = row < R ? (row < room ? row : room) : 0;
       const uint32_t off = (uint32_t)row * row_bytes + (uint32_t)blk * 16u;
       b.ct[t] = buffer_codes(rc, off, 0u);
       buffer_scale(rs, ((uint32_t)row * row_sc + (uint32_t)blk) * SZ, 0u, b.st[t]);
@@ -718,10 +728,11 @@ __device__ __forceinline__ void upfront_compute(const UpfrontLoads<R, FULL, TAIL
     static_assert(!kMx, "the flat layout is built for int4 codes");
     // each slot's block product goes to its own row (slots past the rows to
     // none); LDS holds the activations of block blk at position blk
+    const uint32_t recip = flat_recip(rem);
 #pragma unroll
-    for (int t = 0; t < kFlatPasses; ++t) {
+    for (int t = 0; t < flat_passes<R>(); ++t) {
       int row, blk;
-      flat_slot(lane, t, rem, row, blk);
+      flat_slot<R>(lane, t, rem, recip, row, blk);
       float part[1][M];
 #pragma unroll
       for (int m = 0; m < M; ++m) part[0][m] = 0.0f;

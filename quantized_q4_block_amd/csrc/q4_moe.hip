@@ -506,7 +506,7 @@ hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
     };
     // 4 rows of a single leftover stage of at most 48 blocks: the flat
     // layout (no idle lanes at 48 blocks)
-    if constexpr (FULL == 0 && TAIL == kWideTail && RT == kFlatRows)
+    if constexpr (FULL == 0 && TAIL == kWideTail && RT % 4 == 0)
       if (rem <= kFlatMaxBlocks) return launch(std::integral_constant<int, kFlatTail>{});
     return launch(std::integral_constant<int, TAIL>{});
   });
