@@ -367,9 +367,14 @@ constexpr int kBatchBlocks = 4 * kBatchGroups;
 constexpr int64_t kBatchMaxSlices = 64;
 
 // LDS unit (b, g, r), 16 bytes: x[r][32 b + 8 g .. + 7] of the slice's block b
-// (the A operand of lane 16 g + r), rows r >= M zero.  Consecutive lanes read
-// consecutive units (no bank conflicts).
-__device__ __forceinline__ int batch_unit(int b, int g, int r) { return (b * 4 + g) * 16 + r; }
+// (the A operand of lane 16 g + r), rows r >= M zero.  The 16 units of one
+// (b, g) sit together, 17 apart from the next (b, g): the MFMA reads (16 lanes
+// on consecutive units) and the staging writes (16 lanes on consecutive
+// (b, g) of one row, 272 bytes apart) both meet 16 distinct bank groups.
+constexpr int kBatchUnitStride = 17;
+__device__ __forceinline__ int batch_unit(int b, int g, int r) {
+  return (b * 4 + g) * kBatchUnitStride + r;
+}
 
 // STAGED: the workgroup's scales of the slice (128 rows x kBatchBlocks) go
 // through LDS too, one 16-byte load per thread (rows whose slice scales are
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(kBatchWaves * 64) __attribute__((amdgpu_waves_per_e
   constexpr int kSRow = kF32 ? kBatchBlocks * 4 + 16 : kBatchBlocks * 2 + 8;
   constexpr int kSChunks = kBatchBlocks * (int)sizeof(SP) / 16;
   constexpr int kSPer = STAGED ? 16 * kBatchWaves * kSChunks / kThreads : 0;
-  __shared__ uint4 xa[kUnits];
+  __shared__ uint4 xa[kBatchBlocks * 4 * kBatchUnitStride];
   __shared__ __attribute__((aligned(16))) uint8_t ss[STAGED ? 16 * kBatchWaves * kSRow : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
