@@ -699,6 +699,19 @@ def test_moe_repeated_and_invalid_ids():
     assert_parity(y, y_ref, t, RTOL, what="moe repeated/invalid ids")
 
 
+def test_moe_prep_free_one_expert_takes_every_pair():
+    # 64 pairs over 200 experts, all but two on expert 7 (one id invalid):
+    # the prep-free path runs one expert's 62 pairs in a row
+    T, topk, E, N, K = 8, 8, 200, 72, 1024 + 32
+    m = synthetic.moe_case(6300, T, topk, E, N, K)
+    ids = np.full((T, topk), 7, dtype=np.int32)
+    ids[3, 5] = 199
+    ids[6, 0] = -1
+    y = moe(m.x, m.w_q, m.w_s, ids, m.gates)
+    y_ref, t = oracle.moe(m.x, m.w_q, m.w_s, ids, m.gates)
+    assert_parity(y, y_ref, t, RTOL, what="moe, one expert takes every pair")
+
+
 def test_moe_deterministic_and_workspace_reuse():
     c = synthetic.CONFIGS["moe"]
     m = synthetic.moe_case(c["seed"], c["T"], c["topk"], 32, 256, 1024)
