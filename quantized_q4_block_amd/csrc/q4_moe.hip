@@ -470,8 +470,9 @@ bool moe_direct(int64_t P, int64_t E, int64_t K) {
 }
 
 // One gathered product over every touched expert (LDS kernel; rows of at
-// most kLdsMaxStages stages).  ids != NULL: the DIRECT form (grid.y = E,
-// no prep); otherwise over the prep's active list (grid.y = max_active).
+// most kLdsMaxStages stages).  ids != NULL: the DIRECT form (grid.y =
+// min(P, E) slots, no prep); otherwise over the prep's active list (grid.y =
+// max_active).
 template <int MODE>
 hipError_t moe_stage_lds(const void* x, const uint8_t* wq, const uint16_t* ws,
                          const MoeBuffers& b, float* out, int64_t topk, int64_t N, int64_t K,
