@@ -201,6 +201,26 @@ class Dense:
             raise RuntimeError(f"q4_matmul_ex failed with status {st}")
 
 
+class StreamRead:
+    """The streaming ceiling beside the decode kernel: q4_stream_read over the
+    code bytes of the same rotating weight copies (16-byte non-temporal loads,
+    the decode kernel's width and hint), one copy per step."""
+
+    def __init__(self, torch, q4, dense):
+        P = ctypes.c_void_p
+        self.copies = dense.copies
+        words = int(q4.lib.q4_stream_read_sink_words())
+        self.sink = torch.empty(words, dtype=torch.int32, device="cuda:0")
+        self.bytes = dense.wq[0].numel()
+        self.fn = q4.lib.q4_stream_read
+        self.args = [(P(w.data_ptr()), self.bytes, P(self.sink.data_ptr())) for w in dense.wq]
+
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % self.copies], stream)
+        if st:
+            raise RuntimeError(f"q4_stream_read failed with status {st}")
+
+
 class MxDense:
     """A dense shape with 4-bit float block weights (e2m1 elements, one E8M0
     byte per 32 k), weights rotated over copies."""
@@ -826,7 +846,18 @@ def main():
         roof["launch_us_over_blocks"] = {"blocks": len(us), "min": round(us[0], 3),
                                          "median": round(float(np.median(us)), 3),
                                          "max": round(us[-1], 3)}
-    del head
+    progress("decode_gate_up: streaming ceiling (a read-only pass over the same copies)")
+    probe = StreamRead(torch, q4, head)
+    _, pr_ms = time_steps(torch, probe, max(50, args.steps // 4), max(10, args.warmup // 10),
+                          CLOCK_WARM_MS)
+    ceil = probe.bytes / (pr_ms * 1e-3) / 1e9
+    roof["stream_read_ceiling"] = {"kernel": "q4::stream_read_kernel",
+                                   "bytes_per_launch": probe.bytes,
+                                   "avg_launch_us": round(pr_ms * 1e3, 3),
+                                   "GB/s": round(ceil, 1),
+                                   "frac_of_peak": round(ceil / HBM_PEAK_GBS, 4)}
+    roof["frac_of_stream_ceiling"] = round(achieved / ceil, 4)
+    del probe, head
     torch.cuda.empty_cache()
 
     others = {}

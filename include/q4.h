@@ -72,7 +72,7 @@ extern "C" {
 #define Q4_API
 #endif
 
-#define Q4_ABI_VERSION 9
+#define Q4_ABI_VERSION 10
 
 /* Status codes. */
 #define Q4_OK            0
@@ -402,6 +402,21 @@ Q4_API int32_t q4_mx_matmul_ex(const void *x, const void *w_q, const void *w_e,
                                int64_t M, int64_t N, int64_t K,
                                void *workspace, size_t workspace_bytes,
                                q4_stream_t stream);
+
+/* Measurement helper, not part of the matmul path (ABI version 10): the
+ * streaming ceiling a benchmark sets beside the decode kernel's HBM rate.
+ * Reads the bytes at src once, 16 bytes per lane and load with
+ * non-temporal hints (the decode kernel's width and hint), each wavefront
+ * streaming a contiguous stretch with six 1 KB loads in flight, and writes the
+ * XOR of what each wavefront read to one word of sink, so that every load
+ * is used; the XOR of all of sink is the XOR of every 32-bit word read.
+ *   src    device, 16-byte aligned, bytes a positive multiple of 16
+ *   sink   uint32 [q4_stream_read_sink_words()] device, fully overwritten
+ * Returns Q4_OK or an error code (Q4_ERR_SHAPE for a size that is zero or
+ * not a multiple of 16). */
+Q4_API int32_t q4_stream_read_sink_words(void);
+Q4_API int32_t q4_stream_read(const void *src, size_t bytes, uint32_t *sink,
+                              q4_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -50,7 +50,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
 
-Q4_ABI_VERSION = 9
+Q4_ABI_VERSION = 10
 Q4_OK = 0
 Q4_ERR_NULL = 1
 Q4_ERR_SHAPE = 2
@@ -77,7 +77,7 @@ __all__ = [
     "q4_rmsnorm_matmul_workspace_bytes", "q4_rmsnorm_matmul", "q4_quantize",
     "q4_sb_matmul_workspace_bytes", "q4_sb_matmul",
     "q4_moe_matmul", "q4_moe_matmul_noalloc", "q4_moe_ffn_workspace_bytes", "q4_moe_ffn", "q4_mx_matmul",
-    "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex",
+    "q4_mx_matmul_workspace_bytes", "q4_mx_matmul_ex", "q4_stream_read",
 ]
 
 
@@ -148,6 +148,10 @@ def _open():
     L.q4_mx_matmul_workspace_bytes.restype = ctypes.c_size_t
     L.q4_mx_matmul_ex.argtypes = [P, P, P, P, I32, I64, I64, I64, P, ctypes.c_size_t, P]
     L.q4_mx_matmul_ex.restype = I32
+    L.q4_stream_read_sink_words.argtypes = []
+    L.q4_stream_read_sink_words.restype = I32
+    L.q4_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    L.q4_stream_read.restype = I32
     if L.q4_abi_version() != Q4_ABI_VERSION:
         raise ImportError(f"libq4 ABI version {L.q4_abi_version()} != {Q4_ABI_VERSION}")
     return L
@@ -543,3 +547,20 @@ def q4_moe_ffn(x, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_w, out=None, workspac
     if st != Q4_OK:
         raise Q4Error(st, "q4_moe_ffn")
     return out
+
+
+def q4_stream_read(src, sink=None, stream=None):
+    """Read every byte of the device tensor src once (the benchmark's
+    streaming ceiling; see include/q4.h).  Returns the uint32 sink tensor,
+    whose XOR is the XOR of src's 32-bit words."""
+    torch = _torch()
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = _scratch(torch, 4 * int(lib.q4_stream_read_sink_words()), src.device,
+                        stream).view(torch.int32)
+    st = lib.q4_stream_read(_ptr(src), nbytes, _ptr(sink), _stream_handle(stream, src.device))
+    if st != 0:
+        raise Q4Error(st, "q4_stream_read")
+    return sink

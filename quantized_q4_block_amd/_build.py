@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq4.so")
 SOURCES = ["q4_api.hip", "q4_dequant.hip", "q4_gemv.hip", "q4_gemm.hip", "q4_moe.hip",
            "q4_moe_mm.hip", "q4_mx.hip",
-           "q4_norm.hip", "q4_quant.hip", "q4_sb.hip",
+           "q4_norm.hip", "q4_probe.hip", "q4_quant.hip", "q4_sb.hip",
            "q4_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

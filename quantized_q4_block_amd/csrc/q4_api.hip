@@ -332,6 +332,17 @@ Q4_API int32_t q4_quantize(const void* w, void* w_q, void* w_s, int64_t N, int64
                                       N, K, static_cast<hipStream_t>(stream)));
 }
 
+Q4_API int32_t q4_stream_read_sink_words(void) { return q4::kStreamReadBlocks * 4; }
+
+Q4_API int32_t q4_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                              q4_stream_t stream) {
+  if (bytes == 0 || bytes % 16 != 0) return Q4_ERR_SHAPE;
+  if (!src || !sink) return Q4_ERR_NULL;
+  if (!aligned16(src) || !aligned16(sink)) return Q4_ERR_ALIGN;
+  if (int32_t s = ready()) return s;
+  return launched(q4::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 Q4_API size_t q4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t N) {
   int64_t P, PN;
   if (T < 0 || topk < 0 || E < 0 || N < 0) return 0;

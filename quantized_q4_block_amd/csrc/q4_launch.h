@@ -186,4 +186,11 @@ hipError_t launch_moe_ffn(const uint16_t* x, const uint8_t* w13q, const uint16_t
                           int64_t H, int64_t F, bool weighted_down, void* workspace,
                           hipStream_t stream);
 
+// The benchmark's streaming ceiling: reads bytes (a multiple of 16) at src
+// once with 16-byte non-temporal loads over kStreamReadBlocks workgroups of
+// 4 wavefronts, each streaming a contiguous stretch; sink receives
+// kStreamReadBlocks * 4 words (the XOR of what each wavefront read).
+constexpr int kStreamReadBlocks = 2048;
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace q4

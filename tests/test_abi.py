@@ -55,7 +55,7 @@ def test_header_declares_the_abi():
                          "q4_moe_ffn_workspace_bytes",
                          "q4_moe_ffn", "q4_moe_ffn_ex", "q4_mx_matmul",
                          "q4_mx_matmul_workspace_bytes",
-                         "q4_mx_matmul_ex"}
+                         "q4_mx_matmul_ex", "q4_stream_read_sink_words", "q4_stream_read"}
 
 
 def test_every_declared_symbol_is_exported():
