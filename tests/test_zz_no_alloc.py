@@ -57,6 +57,20 @@ def test_noalloc_matches_the_workspace_call_twice():
         assert_parity(y, y_ref, t, RTOL, what=what)
 
 
+def test_noalloc_with_the_prep_buckets_then_without():
+    # 80 pairs (more than the prep-free form takes): the prep kernel's tables
+    # live in the built-in scratch; then a smaller call that skips the prep
+    prep = synthetic.moe_case(8150, 40, 2, 64, 96, 1024)
+    small = synthetic.moe_case(8160, 5, 2, 9, 70, 512)
+    for what, m in (("prep buckets in the scratch", prep), ("smaller prep-free call", small)):
+        st, y = _noalloc(m)
+        assert st == q4.Q4_OK, q4.q4_status_str(st)
+        y_ws = _with_workspace(m)
+        assert np.array_equal(y.view(np.int64), y_ws.view(np.int64)), what
+        y_ref, t = oracle.moe(m.x, m.w_q, m.w_s, m.ids, m.gates)
+        assert_parity(y, y_ref, t, RTOL, what=what)
+
+
 def test_noalloc_binding_and_repeated_ids():
     m = synthetic.moe_case(8200, 4, 4, 6, 64, 512)
     ids = m.ids.copy()
